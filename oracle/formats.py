@@ -1,0 +1,40 @@
+"""Storage-format decoding for the oracle (test infrastructure only).
+
+bf16 is the upper half of an IEEE binary32; OCP FP8 E4M3FN has 1 sign bit, 4
+exponent bits (bias 7) and 3 mantissa bits, no infinities, and the all-ones
+exponent+mantissa pattern as NaN (largest finite value 448).  Both decoders are
+written from those definitions by bit manipulation.
+"""
+import numpy as np
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN codes (uint8) -> float64, exactly.  NaN codes decode to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int64))
+    subnormal = (m / 8.0) * np.ldexp(1.0, -6)
+    v = np.where(e == 0, subnormal, normal) * sign
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, v)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits with a single round-to-nearest-even to 8 significant bits.
+
+    Finite, normal-range inputs only (|x| in [2^-126, 2^128)) plus exact zeros,
+    which is all the oracle rounds.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0) / 256.0           # 8 significant bits, ties to even
+    y = np.ldexp(r, e).astype(np.float32)    # exact: 8 bits fit in binary32
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)

@@ -1,0 +1,96 @@
+"""Pins for the oracle's indexer scores.
+
+Each case reduces the score to something fixed independently of the oracle's code:
+a library dot product, an exact identity of ReLU, or an invariance of paging.
+"""
+import dataclasses
+
+import numpy as np
+import torch
+
+import synth
+from oracle import indexer
+
+
+def grid_workload(L=300, H=4, D=64, Sq=1, seed=0):
+    return synth.make_workload(synth.spec(1).scaled(L=L, idx_heads=H, idx_dim=D, Sq=Sq, seed=seed), with_kv=False)
+
+
+def keys_dense(wl, b):
+    return indexer.request_keys(wl, b, np.arange(wl.seq_lens[b]))
+
+
+def test_single_head_positive_is_plain_dot():
+    wl = grid_workload(H=1)
+    wl.idx_q = np.abs(wl.idx_q) + 1
+    wl.idx_k = np.abs(wl.idx_k)
+    wl.idx_w = np.ones_like(wl.idx_w)
+    got = indexer.scores(wl, 0)[0]
+    K = keys_dense(wl, 0)
+    want = np.array([np.dot(wl.idx_q[0, 0, 0].astype(np.float64), K[s]) for s in range(len(K))])
+    assert np.array_equal(got, want.astype(np.float32))
+
+
+def test_relu_gate_identity():
+    # for one head with weight 1: score(q) - score(-q) = q.k and both are >= 0
+    wl = grid_workload(H=1)
+    wl.idx_w = np.ones_like(wl.idx_w)
+    pos = indexer.scores(wl, 0)[0].astype(np.float64)
+    neg = dataclasses.replace(wl, idx_q=-wl.idx_q)
+    negs = indexer.scores(neg, 0)[0].astype(np.float64)
+    K = keys_dense(wl, 0)
+    dots = np.array([np.dot(wl.idx_q[0, 0, 0].astype(np.float64), K[s]) for s in range(len(K))])
+    assert (pos >= 0).all() and (negs >= 0).all()
+    assert np.array_equal(pos - negs, dots)
+    assert (dots < 0).any() and (dots > 0).any()
+
+
+def test_one_hot_head_weights_and_linearity():
+    wl = grid_workload(H=4)
+    K = keys_dense(wl, 0)
+    total = np.zeros(len(K))
+    for h in range(4):
+        w = np.zeros_like(wl.idx_w)
+        w[0, 0, h] = wl.idx_w[0, 0, h]
+        one = indexer.scores(dataclasses.replace(wl, idx_w=w), 0)[0].astype(np.float64)
+        d = np.array([np.dot(wl.idx_q[0, 0, h].astype(np.float64), K[s]) for s in range(len(K))])
+        assert np.array_equal(one, wl.idx_w[0, 0, h] * np.maximum(d, 0))
+        total += one
+    assert np.array_equal(indexer.scores(wl, 0)[0].astype(np.float64), total)
+
+
+def test_page_permutation_invariance():
+    wl = grid_workload(L=333)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(wl.num_pages)              # new physical page of old page i
+    k2 = np.empty_like(wl.idx_k)
+    k2[perm] = wl.idx_k
+    pt2 = wl.page_table.copy()
+    ok = pt2 >= 0
+    pt2[ok] = perm[pt2[ok]]
+    wl2 = dataclasses.replace(wl, idx_k=k2, page_table=pt2)
+    assert np.array_equal(indexer.scores(wl, 0), indexer.scores(wl2, 0))
+
+
+def test_e4m3_scale_is_per_token_and_positive_homogeneous():
+    wl = synth.make_workload(synth.spec(2).scaled(B=1, L=200, idx_heads=8), with_kv=False)
+    base = indexer.scores(dataclasses.replace(wl, idx_k_scale=np.ones_like(wl.idx_k_scale)), 0)[0]
+    got = indexer.scores(wl, 0)[0]
+    sig = wl.idx_k_scale.reshape(-1)[indexer.paged_rows(wl.page_table[0], np.arange(200), wl.page_size)]
+    # the bf16 x e4m3 products are exact, so the float64 sums differ only by the factor sigma
+    np.testing.assert_allclose(got.astype(np.float64), base.astype(np.float64) * sig, rtol=2e-7, atol=0)
+    # decoded keys equal torch's float8 decode times sigma
+    codes = wl.idx_k.reshape(-1, wl.idx_k.shape[-1])
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = ref * wl.idx_k_scale.reshape(-1)[:, None].astype(np.float64)
+    rows = indexer.paged_rows(wl.page_table[0], np.arange(200), wl.page_size)
+    assert np.array_equal(indexer.request_keys(wl, 0, np.arange(200)), ref[rows])
+
+
+def test_visibility_of_draft_queries():
+    wl = grid_workload(L=300, Sq=4)
+    sc = indexer.scores(wl, 0)
+    for t in range(4):
+        n = 300 - 4 + 1 + t                       # history 296 tokens + drafts 0..t
+        assert np.isfinite(sc[t, :n]).all()
+        assert np.isneginf(sc[t, n:]).all()
