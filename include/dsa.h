@@ -1,0 +1,246 @@
+/*
+ * libdsa — one decode step of DSA-style sparse attention on AMD MI355X (gfx950).
+ *
+ * The step (sources are web pages describing the method):
+ *   [GLM52] "Shared-Indexer KV Cache Offload for GLM-5.2 on CANN" (lmnt.cn news 268566)
+ *   [HCCP]  "HiCache across parallel modes and distributed serving" (dujian.net)
+ *   [TSA]   TokenSpeed engine code audit (devpress.csdn.net, AMD channel)
+ *   [GLM5R] Zhipu GLM-5 serving report (hkstock.com.hk news 808716)
+ *
+ *   dsa_indexer_scores     Lightning-Indexer scan over every visible cached token   [GLM52] §2.1
+ *   dsa_topk               top-k positions per query (k = 2048 in the pages)        [GLM52] §2.1
+ *   dsa_plan               shared-group pool plan, set-associative FIFO            [GLM52] §3, §4.2-4.3, §5
+ *   dsa_gather_kv          per-layer serve (pool / paged / host rows) and install  [GLM52] §4.4, §5
+ *   dsa_sparse_mla_decode  MLA latent attention over the selected rows only        [TSA] "MLA", [GLM52] §2.1
+ *   dsa_page_translate     page-sharded ownership closed form                      [HCCP] §1.1
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers owned by the caller, unless stated otherwise.  The
+ *     library never allocates memory: scratch space is a caller buffer sized by the
+ *     matching *_workspace_size() call.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; 0 = the null stream)
+ *     and returns; nothing synchronises.  There is no global mutable state.
+ *   - Argument checks that need no device access (null pointers, sizes, dtypes,
+ *     alignment) happen before anything is enqueued and return DSA_ERR_INVALID_ARG or
+ *     DSA_ERR_UNSUPPORTED; then nothing was enqueued.  A failed launch returns
+ *     DSA_ERR_HIP, with the HIP error text in dsa_last_error() (thread-local).
+ *   - Data-dependent indices (page ids, positions, slots) are checked on the device:
+ *     an out-of-range entry is treated as absent (score -inf / row skipped / entry
+ *     invalid, as each call states) and, if `err_count` is not NULL, one is added to
+ *     *err_count (a device int32 the caller zeroes).  No kernel reads or writes
+ *     outside the buffers described here.
+ *   - Integer layouts are row-major C arrays; strides are in elements.
+ */
+#ifndef LIBDSA_DSA_H
+#define LIBDSA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, dtype or alignment              */
+  DSA_ERR_UNSUPPORTED = -2,  /* valid request outside what this build implements        */
+  DSA_ERR_HIP = -3,          /* a HIP launch/runtime call failed; see dsa_last_error()   */
+  DSA_ERR_WORKSPACE = -4     /* workspace pointer NULL or smaller than *_workspace_size  */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,   /* IEEE binary32                                            */
+  DSA_BF16 = 1,  /* bfloat16 (upper half of binary32)                        */
+  DSA_E4M3 = 2   /* OCP FP8 E4M3FN (bias 7, max 448, no infinities)          */
+} dsa_dtype_t;
+
+/*
+ * A per-token row store: the paged caches (indexer keys, latent KV rows), a device
+ * pool, a dense selection buffer, or mapped pinned host memory.
+ *
+ * Paged (page_table != NULL): token `pos` of request b lives at physical row
+ *     page_table[b * pt_stride + pos / page_size] * page_size + pos % page_size
+ *   and physical page ids must lie in [0, num_rows / page_size).  Only the entries
+ *   of pages that hold positions < the request's length are read.  (Page-table
+ *   metadata kept apart from the physical rows: [TSA] "req_to_token_pool vs KV
+ *   allocator".)
+ * Dense (page_table == NULL): token `pos` of request b lives at row
+ *     b * req_stride + pos,  which must be < num_rows.
+ * Row r starts at (const char*)base + r * row_bytes.  `base` may be a device
+ * pointer or a host pointer from hipHostMalloc(..., hipHostMallocMapped) (or its
+ * device alias); it must be 16-byte aligned and row_bytes a multiple of 16.
+ */
+typedef struct {
+  const void* base;
+  int64_t num_rows;
+  int32_t row_bytes;
+  int32_t page_size;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  int32_t reserved;
+  int64_t req_stride;
+} dsa_rows_t;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int dsa_version(void);
+
+/* Text of the last DSA_ERR_HIP / DSA_ERR_INVALID_ARG on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * dsa_indexer_scores — Lightning-Indexer scan ([GLM52] §2.1: the indexer scores every
+ * history token against the current query; the score is the ReLU-gated,
+ * head-weighted dot product below).
+ *
+ *   score[b,t,s] = sum_h w[b,t,h] * max(0, sigma_s * sum_d q[b,t,h,d] * k[b,s,d])
+ *
+ * for s < vis(b,t) = seq_lens[b] - Sq + 1 + t  (query t of an MTP verify step sees the
+ * history and the draft tokens up to its own), and -inf for vis(b,t) <= s < seq_lens[b].
+ * Entries at s >= seq_lens[b] (up to score_stride) are not written.
+ *
+ *   q        [B, Sq, H, D]  dtype q_dtype (F32, BF16 or E4M3)
+ *   w        [B, Sq, H]     float32 head weights
+ *   keys     row store of keys: row_bytes = D * sizeof(k_dtype); k_dtype F32 or E4M3
+ *   k_scale  float32 per key row (same row index as `keys`, sigma_s > 0), or NULL (1.0)
+ *   seq_lens [B] int32 cache length per request (history + Sq query tokens), >= Sq
+ *   scores   [B, Sq, score_stride] float32, score_stride >= max(seq_lens)
+ *   ready    if not NULL, the stream waits on this event before the scan starts: the
+ *            load stream records it after the indexer-cache copy, so the scan can never
+ *            read keys that are not yet resident ([GLM5R] "BugFix#2": the indexer must
+ *            sync with the load stream before it launches; [HCCP] §1.3 ordering).
+ *
+ * Supported: (q F32, k F32): any H*D <= 4096; (q BF16, k E4M3) and (q E4M3, k E4M3):
+ * D = 128, H a multiple of 32, Sq*H <= 256.  Page size (paged keys) a multiple of 32.
+ * Out-of-range page ids: the affected tokens score -inf and count in err_count.
+ */
+dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
+                                const dsa_rows_t* keys, dsa_dtype_t k_dtype, const float* k_scale,
+                                const int32_t* seq_lens, int B, int Sq, int H, int D,
+                                int64_t score_stride, float* scores, int32_t* err_count,
+                                hipEvent_t ready, hipStream_t stream);
+
+/*
+ * dsa_topk — keep the k best-scoring visible positions of each query ([GLM52] §2.1:
+ * top-2048 feeds sparse attention).  Order: score descending, then position ascending
+ * (lowest position wins a tie); -0.0 and +0.0 compare equal.  Output per (b,t) is the
+ * selected positions in ascending order, padded with -1 when vis(b,t) < k.
+ *
+ *   scores   [B, Sq, score_stride] float32 (positions < vis(b,t) are read; no NaNs)
+ *   idx      [B, Sq, k] int32 output
+ *   ws       workspace of at least dsa_topk_workspace_size(B, Sq, k) bytes (may be 0)
+ * Supported: 1 <= k <= 8192, vis(b,t) < 2^31.
+ */
+size_t dsa_topk_workspace_size(int B, int Sq, int k);
+dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B,
+                      int Sq, int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_plan — shared-group pool plan ("DsaPlan", [GLM52] §4.2 and §5), run once per
+ * decode step for a group of layers that share one top-k ([GLM52] §4.1, groups of 4).
+ * The device pool of each request has n_sets sets of `ways` slots; id u belongs to
+ * set u mod n_sets and may use any way of it; each set has one FIFO pointer that moves
+ * once per install and never on a hit ([GLM52] §4.3).  Per request:
+ *   U = ascending de-duplicated union of the valid (>= 0) positions of all Sq rows;
+ *   u is a hit iff id_to_slot[u] != -1; the misses M (ascending) of set s get ways
+ *   (ptr[s] + i) mod ways, i = 0..m_s-1, slot = s*ways + way, and survive iff
+ *   i >= m_s - ways; ptr[s] advances by m_s mod ways.
+ *
+ *   topk        [B, Sq, k] int32 positions (-1 = padding), each row ascending
+ *   pool_ids    [B, n_sets*ways] int32  id held by each slot, -1 = empty
+ *   id_to_slot  [B, id_range] int32     slot of each id, -1 = not pooled
+ *   ptr         [B, n_sets] int32       FIFO pointer per set
+ *   is_hit      [B, Sq, k] uint8 out    1 = served from the pool
+ *   slot        [B, Sq, k] int32 out    hit: its slot; surviving miss: its new slot;
+ *                                       other miss and padding: -1
+ *   miss_pos    [B, Sq*k] int32 out     the misses, ascending (first miss_count[b] valid)
+ *   miss_slot   [B, Sq*k] int32 out     slot of each miss, -1 if it does not survive
+ *   miss_count  [B] int32 out
+ *   commit      1: apply the step to pool_ids / id_to_slot / ptr in the same launch (clear
+ *               each evicted occupant's id_to_slot, install survivors, advance ptr).  The
+ *               outputs above carry everything serve and install need, so committing at
+ *               plan time equals the pages' commit at the end of the group.  0: leave the
+ *               metadata untouched.
+ * Positions >= id_range, and stored slots outside [0, n_sets*ways), are treated as
+ * invalid entries (is_hit 0, slot -1, not counted as misses) and counted in err_count.
+ * Supported: Sq*k <= 8192, n_sets <= 4096, ways <= 64, n_sets*ways <= 2^24.
+ */
+dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int32_t* pool_ids,
+                      int32_t* id_to_slot, int32_t* ptr, int n_sets, int ways, int id_range,
+                      uint8_t* is_hit, int32_t* slot, int32_t* miss_pos, int32_t* miss_slot,
+                      int32_t* miss_count, int commit, int32_t* err_count, hipStream_t stream);
+
+/*
+ * dsa_gather_kv — per-layer serve and install ("DsaServe" / "DsaInstall", [GLM52] §4.4
+ * and §5; the basic offload gather of selected rows from the host cache, §2.1).
+ *
+ * mode DSA_GATHER_SERVE: for every entry (b,t,j) with p = topk[b,t,j]:
+ *     sel[b,t,j,:] = pool[b, slot[b,t,j], :]   if is_hit != NULL and is_hit[b,t,j]
+ *                  = src row (b, p)            otherwise (p >= 0)
+ *                  = zeros                     if p == -1
+ * mode DSA_GATHER_INSTALL: for every entry with is_hit == 0 and slot >= 0 (a surviving
+ *     miss; the first entry of a repeated position only):  pool[b, slot, :] = sel[b,t,j,:]
+ *     The backfill reads the already-served row from `sel` rather than from `src`, so a
+ *     miss crosses the host link once.  Run it after the layer's serve and after every
+ *     reader of the overwritten pool rows ([GLM52] §4.4: backfill is off the critical
+ *     path, on an auxiliary stream).
+ *
+ *   src    row store of the full cache for this layer (paged device cache, dense device
+ *          rows, or mapped pinned host rows); row_bytes must equal `row_bytes`
+ *   pool   [B, pool_rows, row_bytes] bytes (NULL allowed when is_hit is NULL in SERVE)
+ *   sel    [B, Sq, k, row_bytes] bytes
+ * Supported: row_bytes a multiple of 16, <= 4096.  Invalid slots / positions: zero row
+ * (SERVE) or skipped (INSTALL), counted in err_count.
+ */
+#define DSA_GATHER_SERVE 0
+#define DSA_GATHER_INSTALL 1
+dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int32_t* slot, int B,
+                           int Sq, int k, const dsa_rows_t* src, void* pool, int64_t pool_rows,
+                           int32_t row_bytes, void* sel, int mode, int32_t* err_count,
+                           hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode — MLA latent attention over the selected rows only.  One
+ * 576-wide bf16 latent row per token serves as key (all 576) and value (first 512)
+ * ([TSA] "MLA (tokenspeed-mla)"); attention reads only the top-k rows ([GLM52] §2.1).
+ * Per (b, t, h):
+ *     logit_j = scale * <q[b,t,h,:], K_j>     over valid entries j of idx[b,t,:]
+ *     lse     = ln sum_j exp(logit_j)
+ *     o       = sum_j exp(logit_j - lse) * K_j[:512]
+ * Empty selection: o = 0, lse = -inf.  The rows are split over work-groups and the
+ * partial (o, lse) are merged by LSE rescaling ([TSA] two-stage split-KV decode).
+ *
+ *   q      [B, Sq, H, 576] bf16
+ *   idx    [B, Sq, k] int32 positions into `rows` (-1 = skip)
+ *   rows   row store of latent rows, row_bytes = 1152
+ *   o      [B, Sq, H, 512], o_dtype BF16 (round-to-nearest-even) or F32
+ *   lse    [B, Sq, H] float32
+ *   ws     workspace of dsa_sparse_mla_workspace_size(B, Sq, H, k) bytes
+ * Supported: H a multiple of 16 (H % 128 == 0 runs the full-width kernel), k <= 65536.
+ */
+size_t dsa_sparse_mla_workspace_size(int B, int Sq, int H, int k);
+dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_rows_t* rows,
+                                   int B, int Sq, int H, int k, float scale, void* o,
+                                   dsa_dtype_t o_dtype, float* lse, void* ws, size_t ws_bytes,
+                                   int32_t* err_count, hipStream_t stream);
+
+/*
+ * dsa_page_translate — owner rank and owner-local row of logical cache slots under
+ * page-based KV sharding ([HCCP] §1.1): q = floor(x / page_size), rank = q mod n_ranks,
+ * local_row = floor(q / n_ranks) * page_size + (x mod page_size).  Arithmetic only,
+ * no lookup table.
+ *
+ *   x          [n] int64 logical slots (>= 0; negative slots give rank -1, row -1 and
+ *              count in err_count)
+ *   rank       [n] int32 out
+ *   local_row  [n] int64 out
+ */
+dsa_status_t dsa_page_translate(const int64_t* x, int64_t n, int page_size, int n_ranks,
+                                int32_t* rank, int64_t* local_row, int32_t* err_count,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBDSA_DSA_H */

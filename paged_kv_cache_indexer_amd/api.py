@@ -1,0 +1,139 @@
+"""Thin torch-facing binding of libdsa: argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes device tensors
+(torch is used for device memory and streams only); all computation happens in the
+HIP kernels.  A non-OK status raises DsaError with the library's error text.
+"""
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import dsa_rows_t, DSA_F32, DSA_BF16, DSA_E4M3, DSA_GATHER_SERVE, DSA_GATHER_INSTALL  # noqa: F401
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.load().dsa_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_lib.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != _lib.DSA_OK:
+        raise DsaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libdsa needs contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Rows:
+    """A dsa_rows_t over a tensor of rows (paged when a page table is given)."""
+
+    def __init__(self, base: torch.Tensor, row_bytes: int, page_table: Optional[torch.Tensor] = None,
+                 page_size: int = 0, req_stride: int = 0, num_rows: Optional[int] = None,
+                 base_ptr: Optional[int] = None):
+        self._keep = (base, page_table)
+        nbytes = base.numel() * base.element_size()
+        self.c = dsa_rows_t()
+        self.c.base = base_ptr if base_ptr is not None else base.data_ptr()
+        self.c.num_rows = num_rows if num_rows is not None else nbytes // row_bytes
+        self.c.row_bytes = row_bytes
+        self.c.page_size = page_size
+        self.c.page_table = page_table.data_ptr() if page_table is not None else None
+        self.c.pt_stride = page_table.shape[-1] if page_table is not None else 0
+        self.c.reserved = 0
+        self.c.req_stride = req_stride
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def dsa_version() -> int:
+    return _lib.load().dsa_version()
+
+
+def dsa_indexer_scores(q: torch.Tensor, w: torch.Tensor, keys: Rows, k_scale: Optional[torch.Tensor],
+                       seq_lens: torch.Tensor, scores: torch.Tensor, k_dtype: int = DSA_E4M3,
+                       err: Optional[torch.Tensor] = None, ready: Optional[torch.cuda.Event] = None, stream=None,
+                       q_dtype: Optional[int] = None):
+    B, Sq, H, D = q.shape
+    qd = _dtype_code(q) if q_dtype is None else q_dtype
+    ev = ctypes.c_void_p(ready.cuda_event) if ready is not None else None
+    _check(_lib.load().dsa_indexer_scores(_ptr(q), qd, _ptr(w), keys.ref(), k_dtype, _ptr(k_scale), _ptr(seq_lens),
+                                          B, Sq, H, D, scores.shape[-1], _ptr(scores), _ptr(err), ev,
+                                          _stream(stream)), "dsa_indexer_scores")
+
+
+def dsa_topk_workspace_size(B: int, Sq: int, k: int) -> int:
+    return _lib.load().dsa_topk_workspace_size(B, Sq, k)
+
+
+def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor, ws: Optional[torch.Tensor] = None,
+             stream=None):
+    B, Sq, k = idx.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.load().dsa_topk(_ptr(scores), scores.shape[-1], _ptr(seq_lens), B, Sq, k, _ptr(idx), _ptr(ws),
+                                ws_bytes, _stream(stream)), "dsa_topk")
+
+
+def dsa_plan(topk: torch.Tensor, pool_ids: torch.Tensor, id_to_slot: torch.Tensor, ptr: torch.Tensor, n_sets: int,
+             ways: int, is_hit: torch.Tensor, slot: torch.Tensor, miss_pos: torch.Tensor, miss_slot: torch.Tensor,
+             miss_count: torch.Tensor, commit: bool = True, err: Optional[torch.Tensor] = None, stream=None):
+    B, Sq, k = topk.shape
+    _check(_lib.load().dsa_plan(_ptr(topk), B, Sq, k, _ptr(pool_ids), _ptr(id_to_slot), _ptr(ptr), n_sets, ways,
+                                id_to_slot.shape[-1], _ptr(is_hit), _ptr(slot), _ptr(miss_pos), _ptr(miss_slot),
+                                _ptr(miss_count), int(commit), _ptr(err), _stream(stream)), "dsa_plan")
+
+
+def dsa_gather_kv(topk: torch.Tensor, is_hit: Optional[torch.Tensor], slot: Optional[torch.Tensor],
+                  src: Optional[Rows], pool: Optional[torch.Tensor], sel: torch.Tensor, mode: int = DSA_GATHER_SERVE,
+                  row_bytes: int = 1152, err: Optional[torch.Tensor] = None, stream=None):
+    B, Sq, k = topk.shape
+    pool_rows = 0 if pool is None else (pool.numel() * pool.element_size()) // (B * row_bytes)
+    _check(_lib.load().dsa_gather_kv(_ptr(topk), _ptr(is_hit), _ptr(slot), B, Sq, k,
+                                     src.ref() if src is not None else None, _ptr(pool), pool_rows, row_bytes,
+                                     _ptr(sel), mode, _ptr(err), _stream(stream)), "dsa_gather_kv")
+
+
+def dsa_sparse_mla_workspace_size(B: int, Sq: int, H: int, k: int) -> int:
+    return _lib.load().dsa_sparse_mla_workspace_size(B, Sq, H, k)
+
+
+def dsa_sparse_mla_decode(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale: float, o: torch.Tensor,
+                          lse: torch.Tensor, ws: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
+                          stream=None):
+    B, Sq, H, _ = q.shape
+    k = idx.shape[-1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.load().dsa_sparse_mla_decode(_ptr(q), _ptr(idx), rows.ref(), B, Sq, H, k, float(scale), _ptr(o),
+                                             _dtype_code(o), _ptr(lse), _ptr(ws), ws_bytes, _ptr(err),
+                                             _stream(stream)), "dsa_sparse_mla_decode")
+
+
+def dsa_page_translate(x: torch.Tensor, page_size: int, n_ranks: int, rank: torch.Tensor, local_row: torch.Tensor,
+                       err: Optional[torch.Tensor] = None, stream=None):
+    _check(_lib.load().dsa_page_translate(_ptr(x), x.numel(), page_size, n_ranks, _ptr(rank), _ptr(local_row),
+                                          _ptr(err), _stream(stream)), "dsa_page_translate")

@@ -1,0 +1,314 @@
+// Lightning-Indexer scan ("Shared-Indexer KV Cache Offload for GLM-5.2", §2.1: the
+// indexer scores every history token so that the most relevant ones can be kept).
+//
+//   score[b,t,s] = sum_h w[b,t,h] * max(0, sigma_s * <q[b,t,h,:], k[b,s,:]>)
+//
+// Three kernels on one entry point:
+//   * indexer_f32_kernel   fp32 q and keys on the VALU (one thread per token).
+//   * indexer_mfma_kernel  D = 128 e4m3 keys streamed from the paged cache, heads on the
+//     MFMA M axis and 32 tokens on N, so the ReLU-weighted head sum is an in-lane
+//     reduction plus one cross-half add.  bf16 queries use v_mfma_f32_32x32x16_bf16 with
+//     the keys widened e4m3 -> bf16 in registers (exact); e4m3 queries use the fp8
+//     v_mfma_scale_f32_32x32x64_f8f6f4 directly on the key bytes.
+//
+// Key loads: lane (n = lane%32, g = lane/32) owns token n of the tile and bytes
+// [64g, 64g+64) of its 128-byte key: four 16-byte loads, all 64 bytes consumed.  The
+// contraction order over d is the same permutation for the A (query) and B (key)
+// operands, so any d -> (lane group, register slot) assignment is valid; this one makes
+// every lane's key bytes contiguous.
+#include <type_traits>
+
+#include "common.h"
+
+namespace dsa {
+
+// ------------------------------------------------------------------------- fp32 VALU
+constexpr int kF32MaxQ = 4096;
+
+__global__ void __launch_bounds__(256) indexer_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ w, RowStore keys,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ seq_lens, int Sq, int H, int D,
+    int64_t score_stride, float* __restrict__ scores, int32_t* err) {
+  __shared__ float qs[kF32MaxQ];
+  __shared__ float ws[256];
+  const int b = blockIdx.y;
+  const int L = seq_lens[b];
+  const int n_q = Sq * H * D;
+  for (int i = threadIdx.x; i < n_q; i += blockDim.x) qs[i] = q[(int64_t)b * n_q + i];
+  for (int i = threadIdx.x; i < Sq * H; i += blockDim.x) ws[i] = w[(int64_t)b * Sq * H + i];
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= L) return;
+  const int64_t r = keys.row(b, s);
+  float* out = scores + (int64_t)b * Sq * score_stride + s;
+  if (r < 0) {
+    count_error(err);
+    for (int t = 0; t < Sq; ++t) out[(int64_t)t * score_stride] = -INFINITY;
+    return;
+  }
+  const float* k = reinterpret_cast<const float*>(keys.base + r * keys.row_bytes);
+  const float sig = k_scale ? k_scale[r] : 1.0f;
+  for (int t = 0; t < Sq; ++t) {
+    const int vis = L - Sq + 1 + t;
+    float acc = 0.0f;
+    for (int h = 0; h < H; ++h) {
+      const float* qh = qs + (t * H + h) * D;
+      float dot = 0.0f;
+      for (int d = 0; d < D; d += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(k + d);
+        dot = fmaf(qh[d], kv.x, dot);
+        dot = fmaf(qh[d + 1], kv.y, dot);
+        dot = fmaf(qh[d + 2], kv.z, dot);
+        dot = fmaf(qh[d + 3], kv.w, dot);
+      }
+      const float v = dot * sig;
+      acc = fmaf(ws[t * H + h], v > 0.0f ? v : 0.0f, acc);
+    }
+    out[(int64_t)t * score_stride] = (s < vis) ? acc : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------------- MFMA scan
+constexpr int kTile = 32;      // tokens per wave tile (MFMA N)
+constexpr int kMaxB = 1024;    // requests per launch on this path
+
+struct MfmaArgs {
+  const void* q;               // [B, Sq, H, 128] bf16 or e4m3
+  const float* w;              // [B, Sq, H]
+  RowStore keys;               // 128-byte e4m3 rows
+  const float* k_scale;        // per row, or null
+  const int32_t* seq_lens;     // [B]
+  int B, Sq, H;
+  int64_t score_stride;
+  float* scores;
+  int32_t* err;
+};
+
+// HMT: 32-row M tiles per query (H / 32); NQ: queries per wave; RG: waves that share one
+// token tile (each covers NQ of the Sq queries).  MT_W = HMT * NQ M tiles per wave.
+template <bool QFP8, int HMT, int NQ, int RG>
+__global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
+  constexpr int MT_W = HMT * NQ;
+  constexpr int TS = 4 / RG;                       // token tiles per work-group step
+  constexpr int KSTEPS = QFP8 ? 2 : 8;
+  __shared__ int64_t tile_off[kMaxB + 1];          // prefix of tiles per request
+  __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = wave % RG;
+  const int ts = wave / RG;
+  const int n = lane & 31;                         // token within tile / row within M tile
+  const int g = lane >> 5;                         // lane group
+
+  if (threadIdx.x == 0) {
+    int64_t acc = 0;
+    for (int b = 0; b < a.B; ++b) {
+      tile_off[b] = acc;
+      acc += (a.seq_lens[b] + kTile - 1) / kTile;
+    }
+    tile_off[a.B] = acc;
+  }
+  __syncthreads();
+  const int64_t total_tiles = tile_off[a.B];
+  const int64_t total_steps = (total_tiles + TS - 1) / TS;
+  const int64_t step_lo = total_steps * blockIdx.x / gridDim.x;
+  const int64_t step_hi = total_steps * (blockIdx.x + 1) / gridDim.x;
+  int64_t gt = step_lo * TS + ts;
+  const int64_t gt_end = step_hi * TS < total_tiles ? step_hi * TS : total_tiles;
+  if (gt >= gt_end) return;
+
+  typedef typename std::conditional<QFP8, i32x8, bf16x8>::type qop_t;
+  qop_t qa[MT_W][KSTEPS];
+  int cur_b = -1;
+  const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
+
+  auto tile_b = [&](int64_t t_) {
+    int lo = 0, hi = a.B - 1;                      // last b with tile_off[b] <= t_
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_off[mid] <= t_) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  u32x4 kb[4], kn[4];
+  float sig = 0.0f, sig_n = 0.0f;
+  int b = 0, b_n = 0;
+  int64_t s0 = 0, s0_n = 0;
+  bool valid = false, valid_n = false;
+
+#define DSA_FETCH(GT, KB, SIG, BB, S0, VALID)                                              \
+  do {                                                                                     \
+    BB = tile_b(GT);                                                                       \
+    S0 = ((GT) - tile_off[BB]) * kTile;                                                    \
+    const int64_t r_ = a.keys.row(BB, S0 + n);                                             \
+    VALID = r_ >= 0;                                                                       \
+    const u32x4* kp_ = reinterpret_cast<const u32x4*>(a.keys.base + (VALID ? r_ : 0) * 128 + g * 64); \
+    _Pragma("unroll") for (int c_ = 0; c_ < 4; ++c_) KB[c_] = __builtin_nontemporal_load(kp_ + c_); \
+    SIG = (a.k_scale && VALID) ? a.k_scale[r_] : 1.0f;                                     \
+  } while (0)
+
+  DSA_FETCH(gt, kb, sig, b, s0, valid);
+
+  while (true) {
+    const int64_t gt_next = gt + TS;
+    const bool has_next = gt_next < gt_end;
+    if (has_next) DSA_FETCH(gt_next, kn, sig_n, b_n, s0_n, valid_n);
+
+    if (b != cur_b) {
+      // query operand rows row0 .. row0 + 32*MT_W of request b, and their weights
+#pragma unroll
+      for (int mt = 0; mt < MT_W; ++mt) {
+        const int64_t qoff = ((int64_t)b * a.Sq * a.H + row0 + mt * 32 + n) * 128;
+        if constexpr (QFP8) {
+          const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qoff + g * 64;
+#pragma unroll
+          for (int j = 0; j < KSTEPS; ++j) {
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(qp + j * 32);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(qp + j * 32 + 16);
+            qa[mt][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          }
+        } else {
+          const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff + g * 64;
+#pragma unroll
+          for (int j = 0; j < KSTEPS; ++j) qa[mt][j] = *reinterpret_cast<const bf16x8*>(qp + j * 8);
+        }
+      }
+      for (int i = lane; i < MT_W * 32; i += 64) wsm[wave][i] = a.w[(int64_t)b * a.Sq * a.H + row0 + i];
+      cur_b = b;
+    }
+    f32x16 acc[MT_W];
+#pragma unroll
+    for (int mt = 0; mt < MT_W; ++mt) acc[mt] = f32x16{};
+    if constexpr (QFP8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 k0 = kb[2 * j], k1 = kb[2 * j + 1];
+        const i32x8 bop = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+        for (int mt = 0; mt < MT_W; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][j], bop, acc[mt], 0, 0, 0, 127, 0, 127);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 kc = kb[j >> 1];
+        const bf16x8 bop = (j & 1) ? e4m3x8_to_bf16x8(kc.z, kc.w) : e4m3x8_to_bf16x8(kc.x, kc.y);
+#pragma unroll
+        for (int mt = 0; mt < MT_W; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][j], bop, acc[mt], 0, 0, 0);
+      }
+    }
+
+    // epilogue: per query, sum over this lane's 16 rows of each M tile, plus the other half
+    const int L = a.seq_lens[b];
+    const int64_t s = s0 + n;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      float part = 0.0f;
+#pragma unroll
+      for (int hm = 0; hm < HMT; ++hm) {
+        const int mt = qq * HMT + hm;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(&wsm[wave][mt * 32 + i4 * 8 + g * 4]);
+          part = fmaf(wv.x, fmaxf(acc[mt][i4 * 4 + 0], 0.0f), part);
+          part = fmaf(wv.y, fmaxf(acc[mt][i4 * 4 + 1], 0.0f), part);
+          part = fmaf(wv.z, fmaxf(acc[mt][i4 * 4 + 2], 0.0f), part);
+          part = fmaf(wv.w, fmaxf(acc[mt][i4 * 4 + 3], 0.0f), part);
+        }
+      }
+      part += __shfl_xor(part, 32);
+      const int t = rg * NQ + qq;
+      if (g == 0 && s < L) {
+        const int vis = L - a.Sq + 1 + t;
+        float v = part * sig;
+        if (!valid || s >= vis) v = -INFINITY;
+        a.scores[((int64_t)b * a.Sq + t) * a.score_stride + s] = v;
+      }
+    }
+    if (!valid && lane == 0 && rg == 0) count_error(a.err);
+
+    if (!has_next) break;
+    gt = gt_next;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kb[c] = kn[c];
+    sig = sig_n;
+    b = b_n;
+    s0 = s0_n;
+    valid = valid_n;
+  }
+#undef DSA_FETCH
+}
+
+template <bool QFP8, int HMT, int NQ, int RG>
+static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
+  static int grid = 0;
+  if (grid == 0) {
+    int dev = 0, cus = 256, per_cu = 1;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, HMT, NQ, RG>, 256, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    grid = cus * per_cu;
+  }
+  hipLaunchKernelGGL((indexer_mfma_kernel<QFP8, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
+  return launch_status("dsa_indexer_scores");
+}
+
+}  // namespace dsa
+
+extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
+                                           const dsa_rows_t* keys, dsa_dtype_t k_dtype, const float* k_scale,
+                                           const int32_t* seq_lens, int B, int Sq, int H, int D,
+                                           int64_t score_stride, float* scores, int32_t* err_count,
+                                           hipEvent_t ready, hipStream_t stream) {
+  using namespace dsa;
+  DSA_CHECK_ARG(B >= 0 && Sq >= 1 && H >= 1 && D >= 1, "dsa_indexer_scores: bad sizes");
+  if (B == 0) return DSA_OK;
+  DSA_CHECK_ARG(q && w && keys && keys->base && seq_lens && scores, "dsa_indexer_scores: null pointer");
+  DSA_CHECK_ARG(score_stride >= 1, "dsa_indexer_scores: score_stride < 1");
+  DSA_CHECK_ARG(keys->num_rows >= 1, "dsa_indexer_scores: num_rows < 1");
+  DSA_CHECK_ARG(((uintptr_t)keys->base & 15) == 0, "dsa_indexer_scores: keys not 16-byte aligned");
+  if (keys->page_table) DSA_CHECK_ARG(keys->page_size > 0 && keys->pt_stride >= 0, "dsa_indexer_scores: bad paging");
+  if (ready) {
+    hipError_t e = hipStreamWaitEvent(stream, ready, 0);
+    if (e != hipSuccess) {
+      set_last_error("dsa_indexer_scores: hipStreamWaitEvent: %s", hipGetErrorString(e));
+      return DSA_ERR_HIP;
+    }
+  }
+  RowStore ks = RowStore::from(*keys);
+  if (q_dtype == DSA_F32 && k_dtype == DSA_F32) {
+    DSA_CHECK_SUPPORTED(Sq * H * D <= kF32MaxQ && Sq * H <= 256 && D % 4 == 0,
+                        "dsa_indexer_scores: fp32 path needs Sq*H*D <= 4096, Sq*H <= 256, D %% 4 == 0");
+    DSA_CHECK_ARG(keys->row_bytes == D * 4, "dsa_indexer_scores: row_bytes != D*4");
+    DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
+    const int64_t gx = (score_stride + 255) / 256;
+    hipLaunchKernelGGL(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
+                       static_cast<const float*>(q), w, ks, k_scale, seq_lens, Sq, H, D, score_stride, scores,
+                       err_count);
+    return launch_status("dsa_indexer_scores");
+  }
+  DSA_CHECK_SUPPORTED(k_dtype == DSA_E4M3 && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
+                      "dsa_indexer_scores: supported dtypes are (f32,f32), (bf16,e4m3), (e4m3,e4m3)");
+  DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && Sq * H <= 256 && B <= kMaxB,
+                      "dsa_indexer_scores: MFMA path needs D == 128, H %% 32 == 0, Sq*H <= 256, B <= 1024");
+  DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
+  if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "dsa_indexer_scores: page_size %% 32 != 0");
+  MfmaArgs a{q, w, ks, k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count};
+  const int HMT = H / 32;
+  const bool f8 = q_dtype == DSA_E4M3;
+  // one wave covers up to 4 M tiles; queries beyond that go to a second wave on the same tile
+#define DSA_CASE(HM, NQ_, RG_)                                                                  \
+  if (HMT == HM && Sq == NQ_ * RG_)                                                              \
+    return f8 ? launch_mfma<true, HM, NQ_, RG_>(a, stream) : launch_mfma<false, HM, NQ_, RG_>(a, stream);
+  DSA_CASE(1, 1, 1) DSA_CASE(1, 2, 1) DSA_CASE(1, 4, 1) DSA_CASE(1, 4, 2)
+  DSA_CASE(2, 1, 1) DSA_CASE(2, 2, 1) DSA_CASE(2, 2, 2)
+  DSA_CASE(4, 1, 1) DSA_CASE(4, 1, 2)
+#undef DSA_CASE
+  set_last_error("dsa_indexer_scores: unsupported (Sq, H) combination for the MFMA path");
+  return DSA_ERR_UNSUPPORTED;
+}

@@ -1,0 +1,56 @@
+"""The C-ABI library loads and exports every entry point include/dsa.h declares; argument
+checks that need no device reject bad calls before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_indexer_amd as dsa
+from paged_kv_cache_indexer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(dsa_\w+)\(", src, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [s for s in declared() if s not in names]
+    assert not missing, missing
+    L = _lib.load()
+    assert L.dsa_version() == 100
+    for s in declared():
+        assert hasattr(L, s)
+
+
+def test_invalid_arguments_rejected_without_device():
+    L = _lib.load()
+    # negative batch, null pointers, k too large: rejected before any HIP call
+    assert L.dsa_topk(None, 1, None, -1, 1, 8, None, None, 0, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(None, 1, None, 2, 1, 8, None, None, 0, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(ctypes.c_void_p(16), 100, ctypes.c_void_p(16), 2, 1, 9000, ctypes.c_void_p(16), None, 0,
+                      None) == _lib.DSA_ERR_UNSUPPORTED
+    assert L.dsa_page_translate(None, 10, 0, 4, None, None, None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_plan(None, 1, 1, 8, None, None, None, 4, 2, 10, None, None, None, None, None, 1, None,
+                      None) == _lib.DSA_ERR_INVALID_ARG
+    assert b"null" in L.dsa_last_error()
+    rows = _lib.dsa_rows_t()
+    rows.base = 16
+    rows.row_bytes = 1000
+    assert L.dsa_sparse_mla_decode(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(rows), 1, 1, 128, 64,
+                                   ctypes.c_float(0.1), ctypes.c_void_p(16), _lib.DSA_BF16, ctypes.c_void_p(16),
+                                   None, 0, None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_gather_kv(ctypes.c_void_p(16), None, None, 1, 1, 4, None, None, 0, 100, ctypes.c_void_p(16), 0,
+                           None, None) == _lib.DSA_ERR_INVALID_ARG
+    # empty batches are valid no-ops
+    assert L.dsa_topk(None, 1, None, 0, 1, 8, None, None, 0, None) == _lib.DSA_OK

@@ -1,0 +1,319 @@
+"""Parity of each libdsa entry point with the CPU oracle, through the C ABI, on the GPU.
+
+Bars: bit-exact for integer work (page translation, top-k indices, plans, gathers) and
+for indexer scores on the exact fp32 grid; for floating point elsewhere the indexer is
+held to |gpu - oracle| <= 2e-5 * sum_h w_h * sigma_s * sum_d |q_hd k_sd| (fp32 dot-product
+rounding over ~192 terms), and attention to max-abs 2e-2 / mean-abs 2e-3 on o (bf16) and
+max-abs 1e-3 on lse.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_indexer_amd as dsa
+import synth
+from oracle import indexer as o_idx, mla as o_mla, paging as o_pg, plan as o_plan, topk as o_topk
+from oracle.step import decode_request, selected_rows
+from tests.dsa_dev import DevWorkload, bf16_to_f64, host_device_ptr, t_i32, t_u16_as_bf16, DEV
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def indexer_bound(wl, b, t, n):
+    q = o_idx.decode_query(wl.idx_q[b, t], wl.idx_q_dtype)
+    k = o_idx.request_keys(wl, b, np.arange(n))
+    w = wl.idx_w[b, t].astype(np.float64)
+    return 2e-5 * (w @ (np.abs(q) @ np.abs(k).T)) + 1e-30
+
+
+def check_scores(wl, sc_gpu, exact=False):
+    sc = sc_gpu.cpu().numpy()
+    for b in range(wl.B):
+        ref = o_idx.scores(wl, b)
+        L = int(wl.seq_lens[b])
+        got = sc[b, :, :L]
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"-inf pattern differs (b={b})"
+        fin = np.isfinite(ref)
+        if exact:
+            assert np.array_equal(got[fin], ref[fin]), f"scores not bit-exact (b={b})"
+        else:
+            for t in range(wl.Sq):
+                n = o_idx.visible_len(L, wl.Sq, t)
+                bound = indexer_bound(wl, b, t, n)
+                err = np.abs(got[t, :n].astype(np.float64) - ref[t, :n].astype(np.float64))
+                assert (err <= bound).all(), f"b={b} t={t}: max err/bound {(err / bound).max():.3g}"
+
+
+def check_attention(o_gpu, lse_gpu, o_ref, lse_ref):
+    o = bf16_to_f64(o_gpu)
+    d = np.abs(o - o_ref)
+    assert d.max() <= O_MAX and d.mean() <= O_MEAN, f"o max {d.max():.3g} mean {d.mean():.3g}"
+    lg = lse_gpu.cpu().numpy().astype(np.float64)
+    inf = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lg), inf)
+    assert np.abs(lg[~inf] - lse_ref[~inf]).max(initial=0) <= LSE_MAX
+
+
+# ------------------------------------------------------------------ page translation
+def test_page_translate_bit_exact():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([np.arange(5000), rng.integers(0, 1 << 40, 20000), [(1 << 62) + 12345]]).astype(np.int64)
+    xd = torch.from_numpy(x).to(DEV)
+    for p in (1, 2, 64, 128):
+        for N in (1, 2, 3, 4):
+            r = torch.empty(len(x), dtype=torch.int32, device=DEV)
+            l = torch.empty(len(x), dtype=torch.int64, device=DEV)
+            dsa.dsa_page_translate(xd, p, N, r, l)
+            rr, ll = o_pg.owner_local(x, p, N)
+            assert np.array_equal(r.cpu().numpy(), rr) and np.array_equal(l.cpu().numpy(), ll)
+    # negative slots are flagged, not translated
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    xn = torch.tensor([-1, 5, -7], dtype=torch.int64, device=DEV)
+    r = torch.empty(3, dtype=torch.int32, device=DEV)
+    l = torch.empty(3, dtype=torch.int64, device=DEV)
+    dsa.dsa_page_translate(xn, 64, 4, r, l, err=err)
+    assert r.tolist() == [-1, 0, -1] and l.tolist() == [-1, 5, -1] and int(err) == 2
+
+
+# ------------------------------------------------------------------ indexer
+def test_indexer_f32_exact_grid_tiny_config():
+    wl = synth.make_workload(1, with_kv=False)
+    dw = DevWorkload(wl, with_kv=False)
+    check_scores(wl, dw.scores(), exact=True)
+    assert int(dw.err) == 0
+
+
+def test_indexer_f32_exact_grid_mtp_ragged():
+    wl = synth.make_workload(synth.spec(1).scaled(B=3, L=1000, Sq=4), with_kv=False)
+    wl.seq_lens = np.array([1000, 777, 33], dtype=np.int32)
+    check_scores(wl, DevWorkload(wl, with_kv=False).scores(), exact=True)
+
+
+@pytest.mark.parametrize("L", [[1000, 777, 33], [4096, 64, 4095]])
+def test_indexer_bf16_e4m3_within_bound(L):
+    wl = synth.make_workload(synth.spec(2).scaled(B=3, L=max(L)), with_kv=False)
+    wl.seq_lens = np.array(L, dtype=np.int32)
+    dw = DevWorkload(wl, with_kv=False)
+    check_scores(wl, dw.scores())
+    assert int(dw.err) == 0
+
+
+def test_indexer_e4m3_queries_mtp_within_bound():
+    wl = synth.make_workload(synth.spec(3).scaled(B=2, L=1500), with_kv=False)
+    wl.seq_lens = np.array([1500, 1031], dtype=np.int32)
+    check_scores(wl, DevWorkload(wl, with_kv=False).scores())
+
+
+def test_indexer_ready_event_orders_load_before_scan():
+    """The scan waits on the load stream's event; without the wait it reads stale keys."""
+    wl = synth.make_workload(synth.spec(1).scaled(L=2048), with_kv=False)
+    dw = DevWorkload(wl, with_kv=False)
+    real = dw.idx_k.clone()
+    load = torch.cuda.Stream()
+    results = {}
+    for join in (True, False):
+        dw.idx_k.fill_(1000.0)                          # sentinel: not on the [-4, 4] grid
+        torch.cuda.synchronize()
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(load):
+            torch.cuda._sleep(200_000_000)              # a slow host-to-device load
+            dw.idx_k.copy_(real, non_blocking=True)
+            ev.record(load)
+        sc = dw.scores(ready=ev if join else None)
+        torch.cuda.synchronize()
+        results[join] = sc
+    ref = o_idx.scores(wl, 0)
+    got = results[True].cpu().numpy()[0]
+    assert np.array_equal(got[np.isfinite(ref)], ref[np.isfinite(ref)])
+    stale = results[False].cpu().numpy()[0]
+    assert not np.array_equal(stale[np.isfinite(ref)], ref[np.isfinite(ref)]), \
+        "the unjoined scan should have read the sentinel keys"
+
+
+# ------------------------------------------------------------------ top-k
+def _topk_cases():
+    rng = np.random.default_rng(7)
+    cases = []
+    # many exact ties (small integer grid), a signed-zero row, all equal, n <= k, n = k + 1, long rows
+    cases.append((rng.integers(-50, 50, 70000).astype(np.float32), 2048))
+    z = np.zeros(5000, np.float32)
+    z[rng.random(5000) < 0.5] = -0.0
+    z[::97] = 1.0
+    cases.append((z, 300))
+    cases.append((np.full(9000, 3.25, np.float32), 2048))
+    cases.append((rng.standard_normal(100).astype(np.float32), 256))
+    cases.append((rng.standard_normal(256).astype(np.float32), 256))
+    cases.append((rng.standard_normal(257).astype(np.float32), 256))
+    cases.append(((rng.standard_normal(200004) * 1e-3 + 5.0).astype(np.float32), 2048))
+    x = rng.standard_normal(65536).astype(np.float32)
+    x[rng.integers(0, 65536, 3000)] = np.float32(np.inf)
+    cases.append((x, 2048))
+    cases.append((-np.abs(rng.standard_normal(40000)).astype(np.float32), 1))
+    cases.append((rng.standard_normal(33000).astype(np.float32) * np.float32(1e30), 8192))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_topk_standalone_bit_exact(case):
+    s, k = _topk_cases()[case]
+    n = len(s)
+    sc = torch.from_numpy(s[None, None, :].copy()).to(DEV)
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(sc, torch.tensor([n], dtype=torch.int32, device=DEV), idx)
+    assert np.array_equal(idx.cpu().numpy()[0, 0], o_topk.select(s, k))
+
+
+def test_topk_batched_mtp_rows():
+    rng = np.random.default_rng(3)
+    B, Sq, Lmax, k = 3, 4, 5000, 512
+    lens = np.array([5000, 600, 515], dtype=np.int32)
+    s = rng.integers(0, 200, (B, Sq, Lmax)).astype(np.float32)
+    idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        for t in range(Sq):
+            n = o_idx.visible_len(lens[b], Sq, t)
+            assert np.array_equal(got[b, t], o_topk.select(s[b, t, :n], k)), (b, t)
+
+
+# ------------------------------------------------------------------ sparse MLA
+@pytest.mark.parametrize("H,k,L", [(128, 2048, 3000), (16, 256, 4096), (64, 300, 700), (128, 100, 100)])
+def test_mla_against_oracle(H, k, L):
+    wl = synth.make_workload(synth.spec(2).scaled(B=2, L=L, mla_heads=H, topk=k))
+    rng = np.random.default_rng(H + k)
+    idx = np.full((wl.B, 1, k), -1, dtype=np.int32)
+    for b in range(wl.B):
+        n = min(k, L) - (b * 7 if min(k, L) > 7 else 0)          # some padding rows
+        idx[b, 0, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx))
+    o_ref = np.empty((wl.B, 1, H, 512))
+    l_ref = np.empty((wl.B, 1, H))
+    for b in range(wl.B):
+        o_ref[b, 0], l_ref[b, 0] = o_mla.sparse_mla(wl.mla_q[b, 0], selected_rows(wl, b, idx[b, 0]), wl.scale)
+    check_attention(o, lse, o_ref, l_ref)
+    assert int(dw.err) == 0
+
+
+def test_mla_f32_output_and_empty_selection():
+    wl = synth.make_workload(synth.spec(2).scaled(B=2, L=500, topk=64))
+    idx = np.full((2, 1, 64), -1, dtype=np.int32)
+    idx[0, 0, :10] = np.arange(0, 500, 50)
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx), o_dtype=torch.float32)
+    o_ref, l_ref = o_mla.sparse_mla(wl.mla_q[0, 0], selected_rows(wl, 0, idx[0, 0]), wl.scale)
+    check_attention(o[:1], lse[:1], o_ref[None, None], l_ref[None, None])
+    assert (o[1].cpu().numpy() == 0).all() and np.isneginf(lse[1].cpu().numpy()).all()
+
+
+# ------------------------------------------------------------------ end to end, tiny config
+def test_tiny_config_end_to_end():
+    wl = synth.make_workload(1)
+    dw = DevWorkload(wl)
+    sc = dw.scores()
+    idx = dw.topk(sc)
+    o, lse = dw.mla(idx)
+    ref = decode_request(wl, 0)
+    L = int(wl.seq_lens[0])
+    assert np.array_equal(sc.cpu().numpy()[0, :, :L], ref["scores"])
+    assert np.array_equal(idx.cpu().numpy()[0], ref["topk"])
+    check_attention(o, lse, ref["o"][None], ref["lse"][None])
+
+
+# ------------------------------------------------------------------ plan
+def _run_plan_steps(steps_topk, n_sets, W, id_range, Sq=1):
+    """steps_topk: list of int32 [B, Sq, k]; returns per-step GPU and oracle outputs."""
+    B = steps_topk[0].shape[0]
+    pool = torch.full((B, n_sets * W), -1, dtype=torch.int32, device=DEV)
+    its = torch.full((B, id_range), -1, dtype=torch.int32, device=DEV)
+    ptr = torch.zeros((B, n_sets), dtype=torch.int32, device=DEV)
+    state = [o_plan.empty_state(n_sets, W, id_range) for _ in range(B)]
+    for tk in steps_topk:
+        k = tk.shape[-1]
+        E = tk.shape[1] * k
+        is_hit = torch.empty(tk.shape, dtype=torch.uint8, device=DEV)
+        slot = torch.empty(tk.shape, dtype=torch.int32, device=DEV)
+        mpos = torch.full((B, E), -7, dtype=torch.int32, device=DEV)
+        mslot = torch.full((B, E), -7, dtype=torch.int32, device=DEV)
+        mcnt = torch.empty(B, dtype=torch.int32, device=DEV)
+        dsa.dsa_plan(t_i32(tk), pool, its, ptr, n_sets, W, is_hit, slot, mpos, mslot, mcnt, commit=True)
+        for b in range(B):
+            out, state[b] = o_plan.plan_step(tk[b], *state[b], n_sets, W)
+            m = out["miss_count"]
+            assert int(mcnt[b]) == m
+            assert np.array_equal(is_hit[b].cpu().numpy(), out["is_hit"])
+            assert np.array_equal(slot[b].cpu().numpy(), out["slot"])
+            assert np.array_equal(mpos[b, :m].cpu().numpy(), out["miss_pos"])
+            assert np.array_equal(mslot[b, :m].cpu().numpy(), out["miss_slot"])
+            assert np.array_equal(pool[b].cpu().numpy(), state[b][0])
+            assert np.array_equal(its[b].cpu().numpy(), state[b][1])
+            assert np.array_equal(ptr[b].cpu().numpy(), state[b][2])
+
+
+@pytest.mark.parametrize("n_sets,W,k,Sq", [(8, 4, 40, 1), (1, 5, 16, 1), (16, 3, 64, 2), (4, 2, 100, 4)])
+def test_plan_small_bit_exact(n_sets, W, k, Sq):
+    rng = np.random.default_rng(n_sets * 100 + k)
+    id_range, B = 300, 3
+    steps = []
+    for _ in range(8):
+        tk = np.full((B, Sq, k), -1, dtype=np.int32)
+        for b in range(B):
+            for t in range(Sq):
+                n = int(rng.integers(k // 2, k + 1))
+                tk[b, t, :n] = np.sort(rng.choice(id_range, size=n, replace=False))
+        steps.append(tk)
+    _run_plan_steps(steps, n_sets, W, id_range, Sq)
+
+
+def test_plan_pool_group_trajectory_bit_exact():
+    cfg = synth.spec(4).scaled(B=4)
+    traj = synth.gen.topk_trajectory(cfg)
+    _run_plan_steps([traj[s][:, None, :] for s in range(cfg.steps)], cfg.n_sets, cfg.ways, cfg.id_range)
+
+
+# ------------------------------------------------------------------ gather
+def test_gather_serve_and_install_bit_exact():
+    rng = np.random.default_rng(9)
+    B, L, k, n_sets, W = 2, 3000, 256, 32, 4
+    full = rng.integers(0, 1 << 16, (B, L, 576), dtype=np.uint16)
+    full_d = t_u16_as_bf16(full.reshape(B * L, 576))
+    # pinned host copy of the same rows, read over the host link through its device alias
+    host = torch.from_numpy(full.reshape(B * L, 576).view(np.int16)).pin_memory()
+    prev = np.stack([np.sort(rng.choice(L, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    cur = np.stack([np.sort(np.concatenate([rng.choice(prev[b], k // 2, replace=False),
+                                            rng.choice(np.setdiff1d(np.arange(L), prev[b]), k // 2,
+                                                       replace=False)])) for b in range(B)]).astype(np.int32)
+    pool = torch.zeros((B, n_sets * W, 576), dtype=torch.bfloat16, device=DEV)
+    pids = torch.full((B, n_sets * W), -1, dtype=torch.int32, device=DEV)
+    its = torch.full((B, L), -1, dtype=torch.int32, device=DEV)
+    ptr = torch.zeros((B, n_sets), dtype=torch.int32, device=DEV)
+    for tk in (prev, cur):
+        tkd = t_i32(tk[:, None, :])
+        is_hit = torch.empty((B, 1, k), dtype=torch.uint8, device=DEV)
+        slot = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+        mp = torch.empty((B, k), dtype=torch.int32, device=DEV)
+        ms = torch.empty((B, k), dtype=torch.int32, device=DEV)
+        mc = torch.empty(B, dtype=torch.int32, device=DEV)
+        dsa.dsa_plan(tkd, pids, its, ptr, n_sets, W, is_hit, slot, mp, ms, mc, commit=True)
+        for src in (dsa.Rows(full_d, 1152, req_stride=L),
+                    dsa.Rows(host, 1152, req_stride=L, base_ptr=host_device_ptr(host))):
+            sel = torch.empty((B, 1, k, 576), dtype=torch.bfloat16, device=DEV)
+            dsa.dsa_gather_kv(tkd, is_hit, slot, src, pool, sel, dsa.DSA_GATHER_SERVE)
+            torch.cuda.synchronize()
+            got = sel.view(torch.int16).cpu().numpy().view(np.uint16)
+            for b in range(B):
+                assert np.array_equal(got[b, 0], full[b, tk[b]])
+        dsa.dsa_gather_kv(tkd, is_hit, slot, None, pool, sel, dsa.DSA_GATHER_INSTALL)
+        torch.cuda.synchronize()
+        pool_np = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+        pid_np = pids.cpu().numpy()
+        for b in range(B):
+            live = np.nonzero(pid_np[b] >= 0)[0]
+            assert np.array_equal(pool_np[b, live], full[b, pid_np[b, live]])
+    # the second step had hits: they were served from the pool
+    assert int(is_hit.sum()) > 0
