@@ -1,0 +1,163 @@
+"""Benchmark: DSA decode layer-steps/s on one MI355X.
+
+Workload: 32 requests x 65536 cached tokens (page size 64, random page permutation),
+one query token each; indexer 64 heads x 128 (bf16 queries, e4m3 keys with per-token
+scale); top-2048; MLA 128 heads over 576-wide bf16 latent rows.  Seeded synthetic
+inputs, resident in HBM before timing starts.
+
+One step = indexer scan -> top-k -> sparse MLA decode (gather fused into attention through
+the page table) for the whole batch.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def algorithmic_work(B, L, H_idx, D, k, H_mla, ps):
+    """Bytes / flops each kernel must move or compute for one layer-step (no re-reads)."""
+    idx_bytes = (B * L * D            # e4m3 keys
+                 + B * L * 4          # per-token key scale
+                 + B * H_idx * D * 2  # bf16 queries
+                 + B * H_idx * 4      # head weights
+                 + B * (L // ps) * 4  # page table
+                 + B * L * 4)         # scores out
+    idx_flops = 2 * B * H_idx * D * L
+    topk_bytes = B * L * 4 + B * k * 4
+    mla_bytes = (B * k * 1152         # selected latent rows
+                 + B * H_mla * 576 * 2  # q
+                 + B * k * 4          # indices
+                 + B * H_mla * 512 * 2  # o (bf16)
+                 + B * H_mla * 4)     # lse
+    mla_flops = 2 * B * H_mla * k * (576 + 512)
+    return {"indexer": (idx_bytes, idx_flops), "topk": (topk_bytes, 0), "mla": (mla_bytes, mla_flops)}
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """Oracle (single-threaded, float64) on a bounded sample of requests of the same workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle.step import decode_request
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < wl.B:
+            decode_request(wl, done)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    per_req = dt / done
+    return {"value": 1.0 / (per_req * wl.B), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {wl.B} requests of one layer-step (indexer+top-k+MLA), "
+                      f"{dt:.1f} s single-threaded, scaled to the full batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described in DESIGN.md and not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_indexer_amd as dsa
+    import synth
+    from tests.dsa_dev import DevWorkload
+
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(2)
+    dw = DevWorkload(wl)
+    B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
+    H_mla = wl.mla_q.shape[2]
+    scores = torch.empty((B, Sq, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, Sq, k), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, Sq, H_mla, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Sq, H_mla), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H_mla, k)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    names = ["indexer", "topk", "mla"]
+    ev = None
+
+    def step(record):
+        if record:
+            record[0].record(stream)
+        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, dw.k_scale, dw.seq_lens, scores, k_dtype=dw.k_dtype,
+                               err=dw.err, q_dtype=dw.q_dtype, stream=stream)
+        if record:
+            record[1].record(stream)
+        dsa.dsa_topk(scores, dw.seq_lens, idx, stream=stream)
+        if record:
+            record[2].record(stream)
+        dsa.dsa_sparse_mla_decode(dw.mla_q, idx, dw.rows, wl.scale, o, lse, ws=ws, err=dw.err, stream=stream)
+        if record:
+            record[3].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(dw.err) == 0, "device-side index errors during the benchmark"
+
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e-3
+           for j, n in enumerate(names)}                        # seconds per launch
+    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size)
+    kernels = {}
+    for n in names:
+        by, fl = work[n]
+        kernels[n] = {"avg_us": per[n] * 1e6, "algo_bytes": by, "algo_flops": fl,
+                      "GBps": by / per[n] / 1e9, "hbm_frac": by / per[n] / 1e9 / HBM_PEAK_GBS,
+                      "TFLOPs": fl / per[n] / 1e12, "bf16_mfma_frac": fl / per[n] / 1e12 / BF16_PEAK_TFLOPS}
+    dom = max(names, key=lambda n: per[n])
+    by = work[dom][0]
+    roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    ms = wall / args.steps * 1e3
+    out = {
+        "metric": "DSA decode layer-steps/s (B=32, 64K ctx, top-2048); % HBM/MFMA roofline",
+        "value": args.steps / wall,
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)",
+        "config": {"workload": "decode_b32_ctx65536_top2048", "batch": B, "context": L, "query_tokens": Sq,
+                   "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
+                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "keys": "e4m3 + fp32 scale"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
