@@ -68,6 +68,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -89,6 +91,7 @@ def main():
     o = torch.empty((B, Sq, H_mla, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Sq, H_mla), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H_mla, k)), dtype=torch.uint8, device="cuda")
+    ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, k, L)), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     names = ["indexer", "topk", "mla"]
@@ -101,13 +104,19 @@ def main():
                                err=dw.err, q_dtype=dw.q_dtype, stream=stream)
         if record:
             record[1].record(stream)
-        dsa.dsa_topk(scores, dw.seq_lens, idx, stream=stream)
+        dsa.dsa_topk(scores, dw.seq_lens, idx, ws=ws_topk, stream=stream)
         if record:
             record[2].record(stream)
         dsa.dsa_sparse_mla_decode(dw.mla_q, idx, dw.rows, wl.scale, o, lse, ws=ws, err=dw.err, stream=stream)
         if record:
             record[3].record(stream)
 
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()

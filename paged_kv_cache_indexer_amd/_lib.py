@@ -49,7 +49,7 @@ def load() -> ctypes.CDLL:
         "dsa_last_error": (ctypes.c_char_p, []),
         "dsa_indexer_scores": (ctypes.c_int, [vp, ctypes.c_int, vp, prow, ctypes.c_int, vp, vp, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
-        "dsa_topk_workspace_size": (sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+        "dsa_topk_workspace_size": (sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64]),
         "dsa_topk": (ctypes.c_int, [vp, i64, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]),
         "dsa_plan": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp]),

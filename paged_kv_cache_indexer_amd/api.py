@@ -87,14 +87,18 @@ def dsa_indexer_scores(q: torch.Tensor, w: torch.Tensor, keys: Rows, k_scale: Op
                                           _stream(stream)), "dsa_indexer_scores")
 
 
-def dsa_topk_workspace_size(B: int, Sq: int, k: int) -> int:
-    return _lib.load().dsa_topk_workspace_size(B, Sq, k)
+def dsa_topk_workspace_size(B: int, Sq: int, k: int, score_stride: int) -> int:
+    return _lib.load().dsa_topk_workspace_size(B, Sq, k, score_stride)
 
 
 def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor, ws: Optional[torch.Tensor] = None,
              stream=None):
+    """ws: workspace tensor of at least dsa_topk_workspace_size(...) bytes (allocated here if None)."""
     B, Sq, k = idx.shape
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(max(1, dsa_topk_workspace_size(B, Sq, k, scores.shape[-1])), dtype=torch.uint8,
+                         device=idx.device)
+    ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.load().dsa_topk(_ptr(scores), scores.shape[-1], _ptr(seq_lens), B, Sq, k, _ptr(idx), _ptr(ws),
                                 ws_bytes, _stream(stream)), "dsa_topk")
 

@@ -122,6 +122,14 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Load of a wave-uniform address through the constant address space, which lets the
+// backend emit a scalar (SMEM) load: it is counted by lgkmcnt and does not wait behind
+// outstanding vector loads.  Only for data that no kernel writes while it runs.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -11,11 +11,13 @@
 //     the keys widened e4m3 -> bf16 in registers (exact); e4m3 queries use the fp8
 //     v_mfma_scale_f32_32x32x64_f8f6f4 directly on the key bytes.
 //
-// Key loads: lane (n = lane%32, g = lane/32) owns token n of the tile and bytes
-// [64g, 64g+64) of its 128-byte key: four 16-byte loads, all 64 bytes consumed.  The
-// contraction order over d is the same permutation for the A (query) and B (key)
-// operands, so any d -> (lane group, register slot) assignment is valid; this one makes
-// every lane's key bytes contiguous.
+// Key loads: a 32-token tile (4 KB, contiguous inside its page) is read with four 16-byte
+// loads per lane where each instruction covers 1 KB contiguously (lane i, load c: bytes
+// 1024c + 16i), the streaming shape that reaches full HBM bandwidth.  The tile is then
+// re-laid through a per-wave LDS buffer so that lane (n = lane%32, g = lane/32) holds
+// bytes [64g, 64g+64) of token n's key for the MFMA B operand.  The contraction order over
+// d is the same permutation for the A (query) and B (key) operands, so any
+// d -> (lane group, register slot) assignment is valid.
 #include <type_traits>
 
 #include "common.h"
@@ -86,159 +88,199 @@ struct MfmaArgs {
 
 // HMT: 32-row M tiles per query (H / 32); NQ: queries per wave; RG: waves that share one
 // token tile (each covers NQ of the Sq queries).  MT_W = HMT * NQ M tiles per wave.
+//
+// Work is cut into units of up to kUnitTiles tiles inside one request.  A wave loads the
+// request's queries once per unit, then streams the unit's tiles through three fixed
+// register slots (two tiles in flight behind the one being computed).  Every fetch is
+// issued unconditionally (past the unit's end it re-reads the last tile, an L2 hit), and
+// the page lookup is a scalar load, so the steady-state loop never waits on more than
+// the tile it is about to use.
+constexpr int kUnitTiles = 30;   // a multiple of the 3 slots
+
 template <bool QFP8, int HMT, int NQ, int RG>
 __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   constexpr int MT_W = HMT * NQ;
-  constexpr int TS = 4 / RG;                       // token tiles per work-group step
+  constexpr int WPU = 4 / RG;                      // units processed side by side per work-group
   constexpr int KSTEPS = QFP8 ? 2 : 8;
-  __shared__ int64_t tile_off[kMaxB + 1];          // prefix of tiles per request
+  __shared__ int unit_off[kMaxB + 1];              // prefix of units per request
   __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
+  constexpr int kStageStride = 144;                                   // 128-byte key rows, padded
+  __shared__ __attribute__((aligned(16))) char kstage[4][kTile * kStageStride];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = wave % RG;
-  const int ts = wave / RG;
+  const int us = wave / RG;
   const int n = lane & 31;                         // token within tile / row within M tile
   const int g = lane >> 5;                         // lane group
+  const int ps = a.keys.page_size;
 
   if (threadIdx.x == 0) {
-    int64_t acc = 0;
+    int acc = 0;
     for (int b = 0; b < a.B; ++b) {
-      tile_off[b] = acc;
-      acc += (a.seq_lens[b] + kTile - 1) / kTile;
+      unit_off[b] = acc;
+      const int tiles = (a.seq_lens[b] + kTile - 1) / kTile;
+      acc += (tiles + kUnitTiles - 1) / kUnitTiles;
     }
-    tile_off[a.B] = acc;
+    unit_off[a.B] = acc;
   }
   __syncthreads();
-  const int64_t total_tiles = tile_off[a.B];
-  const int64_t total_steps = (total_tiles + TS - 1) / TS;
-  const int64_t step_lo = total_steps * blockIdx.x / gridDim.x;
-  const int64_t step_hi = total_steps * (blockIdx.x + 1) / gridDim.x;
-  int64_t gt = step_lo * TS + ts;
-  const int64_t gt_end = step_hi * TS < total_tiles ? step_hi * TS : total_tiles;
-  if (gt >= gt_end) return;
+  const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
+  const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
   typedef typename std::conditional<QFP8, i32x8, bf16x8>::type qop_t;
   qop_t qa[MT_W][KSTEPS];
-  int cur_b = -1;
-  const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
-  auto tile_b = [&](int64_t t_) {
-    int lo = 0, hi = a.B - 1;                      // last b with tile_off[b] <= t_
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_off[mid] <= t_) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+  struct Slot {
+    u32x4 kb[4];
+    float sig;
+    bool valid;
   };
 
-  u32x4 kb[4], kn[4];
-  float sig = 0.0f, sig_n = 0.0f;
-  int b = 0, b_n = 0;
-  int64_t s0 = 0, s0_n = 0;
-  bool valid = false, valid_n = false;
+  for (int u = blockIdx.x * WPU + us; u < total_units; u += gridDim.x * WPU) {
+    int b = 0;
+    {
+      int lo = 0, hi = a.B - 1;                    // last b with unit_off[b] <= u
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (unit_off[mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      b = __builtin_amdgcn_readfirstlane(lo);
+    }
+    const int L = scalar_load(a.seq_lens + b);
+    const int n_tiles_b = (L + kTile - 1) / kTile;
+    const int t_begin = (u - __builtin_amdgcn_readfirstlane(unit_off[b])) * kUnitTiles;
+    const int t_end = min(t_begin + kUnitTiles, n_tiles_b);
 
-#define DSA_FETCH(GT, KB, SIG, BB, S0, VALID)                                              \
-  do {                                                                                     \
-    BB = tile_b(GT);                                                                       \
-    S0 = ((GT) - tile_off[BB]) * kTile;                                                    \
-    const int64_t r_ = a.keys.row(BB, S0 + n);                                             \
-    VALID = r_ >= 0;                                                                       \
-    const u32x4* kp_ = reinterpret_cast<const u32x4*>(a.keys.base + (VALID ? r_ : 0) * 128 + g * 64); \
-    _Pragma("unroll") for (int c_ = 0; c_ < 4; ++c_) KB[c_] = __builtin_nontemporal_load(kp_ + c_); \
-    SIG = (a.k_scale && VALID) ? a.k_scale[r_] : 1.0f;                                     \
-  } while (0)
-
-  DSA_FETCH(gt, kb, sig, b, s0, valid);
-
-  while (true) {
-    const int64_t gt_next = gt + TS;
-    const bool has_next = gt_next < gt_end;
-    if (has_next) DSA_FETCH(gt_next, kn, sig_n, b_n, s0_n, valid_n);
-
-    if (b != cur_b) {
-      // query operand rows row0 .. row0 + 32*MT_W of request b, and their weights
+    auto fetch = [&](Slot& sl, int t) {
+      t = min(t, t_end - 1);
+      const int64_t s0 = (int64_t)t * kTile;
+      int64_t r0 = -1;
+      if (a.keys.page_table) {
+        const int64_t lp = s0 / ps;
+        if (lp < a.keys.pt_stride) {
+          const int32_t pg = scalar_load(a.keys.page_table + (int64_t)b * a.keys.pt_stride + lp);
+          if (pg >= 0) r0 = (int64_t)pg * ps + (s0 - lp * ps);
+        }
+      } else if (a.keys.req_stride <= 0 || s0 < a.keys.req_stride) {
+        r0 = (int64_t)b * a.keys.req_stride + s0;
+      }
+      sl.valid = r0 >= 0 && r0 + kTile <= a.keys.num_rows;
+      const int64_t r = (sl.valid ? r0 : 0) + n;
+      const char* kp = a.keys.base + (sl.valid ? r0 : 0) * 128 + lane * 16;
 #pragma unroll
-      for (int mt = 0; mt < MT_W; ++mt) {
-        const int64_t qoff = ((int64_t)b * a.Sq * a.H + row0 + mt * 32 + n) * 128;
-        if constexpr (QFP8) {
-          const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qoff + g * 64;
+      for (int c = 0; c < 4; ++c) sl.kb[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + c * 1024));
+      // always issue the scale load (a dummy in-bounds read when there is no scale), so
+      // every fetch adds the same number of outstanding loads
+      const float sv = a.k_scale ? a.k_scale[r] : *reinterpret_cast<const float*>(a.keys.base);
+      sl.sig = a.k_scale ? sv : 1.0f;
+    };
+
+    // queries and weights of request b for this wave's rows
 #pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) {
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(qp + j * 32);
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(qp + j * 32 + 16);
-            qa[mt][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    for (int mt = 0; mt < MT_W; ++mt) {
+      const int64_t qoff = ((int64_t)b * a.Sq * a.H + row0 + mt * 32 + n) * 128;
+      if constexpr (QFP8) {
+        const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qoff + g * 64;
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(qp + j * 32);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(qp + j * 32 + 16);
+          qa[mt][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+      } else {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff + g * 64;
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) qa[mt][j] = *reinterpret_cast<const bf16x8*>(qp + j * 8);
+      }
+    }
+    float wreg[(MT_W * 32 + 63) / 64];
+#pragma unroll
+    for (int r = 0; r < (MT_W * 32 + 63) / 64; ++r) {
+      const int i = lane + 64 * r;
+      wreg[r] = (i < MT_W * 32) ? a.w[(int64_t)b * a.Sq * a.H + row0 + i] : 0.0f;
+    }
+    // tile prefetches go out after the query loads, so the loop below is entered with the
+    // same outstanding-load order as its back edge (no full drain at the loop header)
+    Slot A, Bs, C;
+    fetch(A, t_begin);
+    fetch(Bs, t_begin + 1);
+    fetch(C, t_begin + 2);
+#pragma unroll
+    for (int r = 0; r < (MT_W * 32 + 63) / 64; ++r) {
+      const int i = lane + 64 * r;
+      if (i < MT_W * 32) wsm[wave][i] = wreg[r];
+    }
+
+    auto compute = [&](const Slot& cur, int t, bool live) {
+      // re-lay the tile: load c of lane i holds row 8c + i/8, bytes 16*(i%8) .. +16
+      char* st = kstage[wave];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(st + (c * 8 + (lane >> 3)) * kStageStride + (lane & 7) * 16) = cur.kb[c];
+      u32x4 kb[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const u32x4*>(st + n * kStageStride + g * 64 + c * 16);
+      f32x16 acc[MT_W];
+#pragma unroll
+      for (int mt = 0; mt < MT_W; ++mt) acc[mt] = f32x16{};
+      if constexpr (QFP8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 k0 = kb[2 * j], k1 = kb[2 * j + 1];
+          const i32x8 bop = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                                  (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+          for (int mt = 0; mt < MT_W; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][j], bop, acc[mt], 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4 kc = kb[j >> 1];
+          const bf16x8 bop = (j & 1) ? e4m3x8_to_bf16x8(kc.z, kc.w) : e4m3x8_to_bf16x8(kc.x, kc.y);
+#pragma unroll
+          for (int mt = 0; mt < MT_W; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][j], bop, acc[mt], 0, 0, 0);
+        }
+      }
+      // epilogue: per query, sum over this lane's 16 rows of each M tile, plus the other half
+      const int64_t s = (int64_t)t * kTile + n;
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        float part = 0.0f;
+#pragma unroll
+        for (int hm = 0; hm < HMT; ++hm) {
+          const int mt = qq * HMT + hm;
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(&wsm[wave][mt * 32 + i4 * 8 + g * 4]);
+            part = fmaf(wv.x, fmaxf(acc[mt][i4 * 4 + 0], 0.0f), part);
+            part = fmaf(wv.y, fmaxf(acc[mt][i4 * 4 + 1], 0.0f), part);
+            part = fmaf(wv.z, fmaxf(acc[mt][i4 * 4 + 2], 0.0f), part);
+            part = fmaf(wv.w, fmaxf(acc[mt][i4 * 4 + 3], 0.0f), part);
           }
-        } else {
-          const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff + g * 64;
-#pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) qa[mt][j] = *reinterpret_cast<const bf16x8*>(qp + j * 8);
         }
+        part += __shfl_xor(part, 32);
+        const int tq = rg * NQ + qq;
+        const int vis = L - a.Sq + 1 + tq;
+        float v = part * cur.sig;
+        if (!cur.valid || s >= vis) v = -INFINITY;
+        if (live && g == 0 && s < L) a.scores[((int64_t)b * a.Sq + tq) * a.score_stride + s] = v;
       }
-      for (int i = lane; i < MT_W * 32; i += 64) wsm[wave][i] = a.w[(int64_t)b * a.Sq * a.H + row0 + i];
-      cur_b = b;
-    }
-    f32x16 acc[MT_W];
-#pragma unroll
-    for (int mt = 0; mt < MT_W; ++mt) acc[mt] = f32x16{};
-    if constexpr (QFP8) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4 k0 = kb[2 * j], k1 = kb[2 * j + 1];
-        const i32x8 bop = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
-#pragma unroll
-        for (int mt = 0; mt < MT_W; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][j], bop, acc[mt], 0, 0, 0, 127, 0, 127);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 kc = kb[j >> 1];
-        const bf16x8 bop = (j & 1) ? e4m3x8_to_bf16x8(kc.z, kc.w) : e4m3x8_to_bf16x8(kc.x, kc.y);
-#pragma unroll
-        for (int mt = 0; mt < MT_W; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][j], bop, acc[mt], 0, 0, 0);
-      }
-    }
+      if (live && !cur.valid && lane == 0 && rg == 0) count_error(a.err);
+    };
 
-    // epilogue: per query, sum over this lane's 16 rows of each M tile, plus the other half
-    const int L = a.seq_lens[b];
-    const int64_t s = s0 + n;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      float part = 0.0f;
-#pragma unroll
-      for (int hm = 0; hm < HMT; ++hm) {
-        const int mt = qq * HMT + hm;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(&wsm[wave][mt * 32 + i4 * 8 + g * 4]);
-          part = fmaf(wv.x, fmaxf(acc[mt][i4 * 4 + 0], 0.0f), part);
-          part = fmaf(wv.y, fmaxf(acc[mt][i4 * 4 + 1], 0.0f), part);
-          part = fmaf(wv.z, fmaxf(acc[mt][i4 * 4 + 2], 0.0f), part);
-          part = fmaf(wv.w, fmaxf(acc[mt][i4 * 4 + 3], 0.0f), part);
-        }
-      }
-      part += __shfl_xor(part, 32);
-      const int t = rg * NQ + qq;
-      if (g == 0 && s < L) {
-        const int vis = L - a.Sq + 1 + t;
-        float v = part * sig;
-        if (!valid || s >= vis) v = -INFINITY;
-        a.scores[((int64_t)b * a.Sq + t) * a.score_stride + s] = v;
-      }
+    // fixed-shape body: no exit between the three fetches (tiles past the unit's end are
+    // computed from the clamped tile and not stored)
+    for (int t = t_begin; t < t_end; t += 3) {
+      compute(A, t, true);
+      fetch(A, t + 3);
+      compute(Bs, t + 1, t + 1 < t_end);
+      fetch(Bs, t + 4);
+      compute(C, t + 2, t + 2 < t_end);
+      fetch(C, t + 5);
     }
-    if (!valid && lane == 0 && rg == 0) count_error(a.err);
-
-    if (!has_next) break;
-    gt = gt_next;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kb[c] = kn[c];
-    sig = sig_n;
-    b = b_n;
-    s0 = s0_n;
-    valid = valid_n;
   }
-#undef DSA_FETCH
 }
 
 template <bool QFP8, int HMT, int NQ, int RG>

@@ -32,6 +32,7 @@ constexpr int kVStride = kTT + 8;           // V^T row stride (bf16), 80 B
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;
+constexpr int kMaxSplit = 1024;             // selected rows per split (row offsets kept in LDS)
 
 struct MlaArgs {
   const uint16_t* q;       // [QR, H, 576] bf16
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   constexpr int CPT = (kTileChunks + NT - 1) / NT;      // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t klds[2][kTT * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVDim * kVStride];
-  __shared__ int64_t rowoff[2][kTT];     // byte offset of each selected row, -1 = none
+  __shared__ int64_t rowoff[kMaxSplit];  // byte offset of each selected row of the split, -1 = none
   __shared__ int tvalid[2][kTT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -76,33 +77,30 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   if (e_end > a.k) e_end = a.k;
   const int32_t* idx = a.idx + (int64_t)qr * a.k;
 
-  auto tile_rows = [&](int e0, int bf) {
-    if (tid < kTT) {
-      const int e = e0 + tid;
-      int64_t off = -1;
-      if (e < e_end) {
-        const int32_t p = idx[e];
-        const int64_t row = a.rows.row(b, p);
-        if (row >= 0) off = row * kRowBytes;
-        else if (p >= 0) count_error(a.err);
-      }
-      rowoff[bf][tid] = off;
-    }
-  };
+  // resolve every selected row of this split once: index -> page table -> byte offset
+  for (int e = e_begin + tid; e < e_end; e += NT) {
+    const int32_t p = idx[e];
+    const int64_t row = a.rows.row(b, p);
+    if (row < 0 && p >= 0) count_error(a.err);
+    rowoff[e - e_begin] = row >= 0 ? row * kRowBytes : -1;
+  }
+  for (int e = e_end + tid; e < e_begin + a.per_split && e - e_begin < kMaxSplit; e += NT) rowoff[e - e_begin] = -1;
+  __syncthreads();
+
   u32x4 stage[CPT];
-  auto load_tile = [&](int bf) {
+  auto load_tile = [&](int e0) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + NT * r;
       stage[r] = u32x4{0, 0, 0, 0};
       if (c < kTileChunks) {
         const int tok = c / kChunks, ch = c - tok * kChunks;
-        const int64_t off = rowoff[bf][tok];
+        const int64_t off = rowoff[e0 - e_begin + tok];
         if (off >= 0) stage[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.rows.base + off) + ch);
       }
     }
   };
-  auto store_tile = [&](int bf) {
+  auto store_tile = [&](int bf, int e0) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + NT * r;
@@ -111,18 +109,13 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
         *reinterpret_cast<u32x4*>(&klds[bf][tok * kKStride + ch * 8]) = stage[r];
       }
     }
-    // validity travels with the K buffer: rowoff[bf] is reused for a later tile while this
-    // buffer is still being read
-    if (tid < kTT) tvalid[bf][tid] = rowoff[bf][tid] >= 0;
+    if (tid < kTT) tvalid[bf][tid] = rowoff[e0 - e_begin + tid] >= 0;
   };
 
-  // ---- prologue: tile 0 into K buffer 0, row offsets of tile 1 into slot 1
+  // ---- prologue: tile 0 into K buffer 0
   if (e_begin < e_end) {
-    tile_rows(e_begin, 0);
-    __syncthreads();
-    load_tile(0);
-    store_tile(0);
-    if (e_begin + kTT < e_end) tile_rows(e_begin + kTT, 1);
+    load_tile(e_begin);
+    store_tile(0, e_begin);
   }
 
   // ---- q^T operand: 36 k-steps of 16 over the 576 latent dims
@@ -141,12 +134,13 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) oacc[i] = f32x16{};
   float m_used = -INFINITY;     // log2-domain running max used for p
-  float l_part = 0.0f;          // this lane's share of sum p
+  float l_part = 0.0f;          // this lane's share of sum p (fp32 p: for lse)
+  float lr_part = 0.0f;         // this lane's share of sum bf16(p) (the PV weights: for o)
 
   int cur = 0;
   for (int e0 = e_begin; e0 < e_end; e0 += kTT, cur ^= 1) {
     const bool has_next = e0 + kTT < e_end;
-    __syncthreads();              // K[cur] and rowoff[cur^1] ready; V^T and K[cur^1] free
+    __syncthreads();              // K[cur] ready; V^T and K[cur^1] free
 
     // ---- V^T from K[cur]: 8 tokens x 8 dims blocks, transposed through registers
     for (int blk = tid; blk < 4 * (kVDim / 8); blk += NT) {
@@ -171,17 +165,19 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
       }
     }
     __syncthreads();              // V^T ready
-    if (has_next) load_tile(cur ^ 1);
+    if (has_next) load_tile(e0 + kTT);
 
-    // ---- S^T = K . q^T
+    // ---- S^T = K . q^T; LDS operand reads run 3 MFMAs ahead
     f32x16 s = f32x16{};
     {
       const uint16_t* kp = &klds[cur][n * kKStride + g * 8];
+      bf16x8 ring[4];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) ring[j] = *reinterpret_cast<const bf16x8*>(kp + j * 16);
 #pragma unroll
       for (int j = 0; j < 36; ++j) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kp + j * 16);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[j], s, 0, 0, 0);
-        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound operand prefetch depth
+        if (j + 3 < 36) ring[(j + 3) & 3] = *reinterpret_cast<const bf16x8*>(kp + (j + 3) * 16);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j & 3], qb[j], s, 0, 0, 0);
       }
     }
 
@@ -202,6 +198,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[i] *= alpha;
       l_part *= alpha;
+      lr_part *= alpha;
       m_used = m_new;
     }
     uint32_t pb[8];
@@ -211,33 +208,36 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
       const float p1 = (s[i + 1] == -INFINITY) ? 0.0f : exp2f(s[i + 1] - m_used);
       const uint32_t w = pack_bf16x2(p0, p1);
       pb[i >> 1] = w;
-      l_part += bf16_bits_to_f32(w & 0xffffu) + bf16_bits_to_f32(w >> 16);
+      l_part += p0 + p1;
+      lr_part += bf16_bits_to_f32(w & 0xffffu) + bf16_bits_to_f32(w >> 16);
     }
     const bf16x8 p_lo = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
     const bf16x8 p_hi = __builtin_bit_cast(bf16x8, u32x4{pb[4], pb[5], pb[6], pb[7]});
 
-    // ---- O^T += V^T . P^T over the 512 value dims
+    // ---- O^T += V^T . P^T over the 512 value dims; operand reads run 3 MFMAs ahead
     {
       const uint16_t* vp = vt + n * kVStride + g * 8;
+      auto vop = [&](int i) {   // i = 2*mt + ks
+        return *reinterpret_cast<const bf16x8*>(vp + (i >> 1) * 32 * kVStride + (i & 1) * 16);
+      };
+      bf16x8 ring[4];
 #pragma unroll
-      for (int mt = 0; mt < 16; ++mt) {
-        const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vp + mt * 32 * kVStride);
-        const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vp + mt * 32 * kVStride + 16);
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, p_lo, oacc[mt], 0, 0, 0);
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, p_hi, oacc[mt], 0, 0, 0);
-        if (mt & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 3; ++i) ring[i] = vop(i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + 3 < 32) ring[(i + 3) & 3] = vop(i + 3);
+        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i & 3], (i & 1) ? p_hi : p_lo, oacc[i >> 1], 0,
+                                                               0, 0);
       }
     }
 
-    if (has_next) {
-      store_tile(cur ^ 1);
-      if (e0 + 2 * kTT < e_end) tile_rows(e0 + 2 * kTT, cur);
-    }
+    if (has_next) store_tile(cur ^ 1, e0 + kTT);
   }
 
   // ---- finish: l over both lane groups, normalise, write
   const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+  const float lr_tot = lr_part + __shfl_xor(lr_part, 32);
+  const float inv = (lr_tot > 0.0f) ? 1.0f / lr_tot : 0.0f;
   const float lse = (l_tot > 0.0f) ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   if (!head_ok) return;
   const bool direct = a.splits == 1;
@@ -315,7 +315,8 @@ static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_sp
   int s = (int)((device_cus() + wgs - 1) / wgs);
   if (s < 1) s = 1;
   if (s > tiles) s = tiles;
-  if (s > 64) s = 64;
+  const int min_s = (tiles + kMaxSplit / kTT - 1) / (kMaxSplit / kTT);
+  if (s < min_s) s = min_s;
   const int tps = (tiles + s - 1) / s;
   per_split = tps * kTT;
   splits = (k + per_split - 1) / per_split;

@@ -2,12 +2,21 @@
 // §2.1: the 2048 best positions per query feed sparse attention).
 //
 // Order: score descending, then position ascending; -0.0 == +0.0.  Scores map to
-// order-preserving uint32 keys; an MSB-first radix select (digits of up to 11 bits,
-// starting below the bits every key of the row shares) finds the k-th largest key T
-// and how many keys equal to T are taken ("need").  A final ordered compaction emits
-// every position with key > T plus the first `need` positions with key == T, so the
-// output is ascending by position.  One 1024-thread work-group per query row; the row
-// is re-read from L2 on each pass.
+// order-preserving uint32 keys.
+//
+// Stage 1 (many work-groups per row): the row is cut into chunks of C positions; each
+// chunk is staged in LDS and reduced to its own top-min(k, len) under the same total
+// order, emitted in position order as (key, position) candidates.  Every member of the
+// row's top-k is in its chunk's top-k (fewer than k elements of the whole row precede
+// it), so the candidates contain the answer.
+// Stage 2 (one work-group per row): the exact select over the candidates, which are
+// already in ascending position order and stay in L2, then an ordered compaction that
+// writes the k positions ascending.
+//
+// Both stages use the same select: an MSB-first radix search for the k-th largest key T
+// (digits of up to 11 bits, starting below the bits that the smallest and the largest
+// key share) and `need`, the number of keys equal to T that are taken (lowest positions
+// first).
 #include "common.h"
 
 namespace dsa {
@@ -16,6 +25,16 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
+constexpr int kMaxChunkElems = 32768;     // stage-1 LDS staging: 128 KB of keys
+constexpr int kTargetChunks = 8;
+
+struct TopkShared {
+  uint32_t hist[kBins];
+  int wave_tot[2 * kTopkWaves + 1];
+  uint32_t red[2 * kTopkWaves];
+  uint32_t sel_digit;
+  int sel_above;
+};
 
 // block-wide exclusive scan of one int per thread; returns prefix, writes total
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
@@ -46,32 +65,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
   return res;
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ scores, int64_t stride,
-                                                            const int32_t* __restrict__ seq_lens, int Sq, int k,
-                                                            int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ int wave_tot[2 * kTopkWaves + 1];
-  __shared__ uint32_t red[2 * kTopkWaves];
-  __shared__ uint32_t sel_digit;
-  __shared__ int sel_above;
-
-  const int row = blockIdx.x;
-  const int b = row / Sq, t = row % Sq;
-  int n = seq_lens[b] - Sq + 1 + t;
-  if (n < 0) n = 0;
-  int32_t* out = idx + (int64_t)row * k;
-  const float* src = scores + (int64_t)row * stride;
+// k-th largest key T among keys[0..n) (n > k) and how many keys == T are taken.
+// KEY(i) returns the i-th key; reads are repeated once per pass.
+template <typename KeyFn>
+__device__ void radix_select(KeyFn KEY, int n, int k, TopkShared& sh, uint32_t& T_out, int& need_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = (i < n) ? i : -1;
-    return;
-  }
-
-  // ---- pass 0: min / max key of the row
   uint32_t kmin = 0xffffffffu, kmax = 0;
   for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t key = float_key(src[i]);
+    const uint32_t key = KEY(i);
     kmin = min(kmin, key);
     kmax = max(kmax, key);
   }
@@ -81,18 +82,16 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
   }
   if (lane == 0) {
-    red[wave] = kmin;
-    red[kTopkWaves + wave] = kmax;
+    sh.red[wave] = kmin;
+    sh.red[kTopkWaves + wave] = kmax;
   }
   __syncthreads();
   kmin = 0xffffffffu;
   kmax = 0;
   for (int w = 0; w < kTopkWaves; ++w) {
-    kmin = min(kmin, red[w]);
-    kmax = max(kmax, red[kTopkWaves + w]);
+    kmin = min(kmin, sh.red[w]);
+    kmax = max(kmax, sh.red[kTopkWaves + w]);
   }
-
-  // ---- radix select of the k-th largest key
   uint32_t prefix;
   int remaining = k;
   int hi;                                   // bits >= hi of the answer are known
@@ -106,76 +105,234 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
   }
   while (hi > 0) {
     const int nb = hi < kDigitBits ? hi : kDigitBits;
-    const int sh = hi - nb;
+    const int sh_ = hi - nb;
     const uint32_t dmask = (1u << nb) - 1u;
-    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = float_key(src[i]);
+      const uint32_t key = KEY(i);
       const bool match = (hi == 32) ? true : ((key >> hi) == (prefix >> hi));
-      if (match) atomicAdd(&hist[(key >> sh) & dmask], 1u);
+      if (match) atomicAdd(&sh.hist[(key >> sh_) & dmask], 1u);
     }
     __syncthreads();
     // suffix counts from the top digit down; thread i covers digits 2047-2i, 2046-2i
     const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
-    const int c_hi = (int)hist[d_hi], c_lo = (int)hist[d_lo];
+    const int c_hi = (int)sh.hist[d_hi], c_lo = (int)sh.hist[d_lo];
     int tot;
-    const int before = block_exclusive_scan(c_hi + c_lo, wave_tot, tot);
+    const int before = block_exclusive_scan(c_hi + c_lo, sh.wave_tot, tot);
     if (before < remaining && remaining <= before + c_hi) {
-      sel_digit = (uint32_t)d_hi;
-      sel_above = before;
+      sh.sel_digit = (uint32_t)d_hi;
+      sh.sel_above = before;
     } else if (before + c_hi < remaining && remaining <= before + c_hi + c_lo) {
-      sel_digit = (uint32_t)d_lo;
-      sel_above = before + c_hi;
+      sh.sel_digit = (uint32_t)d_lo;
+      sh.sel_above = before + c_hi;
     }
     __syncthreads();
-    prefix |= sel_digit << sh;
-    remaining -= sel_above;
-    hi = sh;
+    prefix |= sh.sel_digit << sh_;
+    remaining -= sh.sel_above;
+    hi = sh_;
     __syncthreads();
   }
-  const uint32_t T = prefix;
-  const int need = remaining;               // keys == T to take, lowest positions first
+  T_out = prefix;
+  need_out = remaining;
+}
 
-  // ---- ordered compaction
+// Ordered compaction: for i ascending, take i if key > T, or key == T among the first
+// `need` such; EMIT(slot, i, key) for each taken element.  Each thread owns PER
+// consecutive elements per round so the scan order is element order.
+template <int PER, typename KeyFn, typename EmitFn>
+__device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, TopkShared& sh, EmitFn EMIT) {
+  const int tid = threadIdx.x;
   int sel_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < n && sel_base < k; c0 += kTopkThreads) {
-    const int i = c0 + tid;
-    const uint32_t key = (i < n) ? float_key(src[i]) : 0u;
-    const bool gt = (i < n) && key > T;
-    const bool eq = (i < n) && key == T;
-    int eq_tot;
-    const int eq_rank = eq_base + block_exclusive_scan(eq ? 1 : 0, wave_tot, eq_tot);
-    const bool take = gt || (eq && eq_rank < need);
+  for (int c0 = 0; c0 < n && sel_base < k; c0 += kTopkThreads * PER) {
+    uint32_t key[PER];
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = c0 + tid * PER + r;
+      key[r] = (i < n) ? KEY(i) : 0u;
+      n_gt += (i < n && key[r] > T);
+      n_eq += (i < n && key[r] == T);
+    }
+    int eq_tot, gt_tot;
+    int eq_rank = eq_base + block_exclusive_scan(n_eq, sh.wave_tot, eq_tot);
+    // taken by this thread: all its > T, plus its == T while the rank is below need
+    int take_eq = need - eq_rank;
+    take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
     int sel_tot;
-    const int pos = sel_base + block_exclusive_scan(take ? 1 : 0, wave_tot, sel_tot);
-    if (take && pos < k) out[pos] = i;
+    int pos = sel_base + block_exclusive_scan(n_gt + take_eq, sh.wave_tot, sel_tot);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = c0 + tid * PER + r;
+      if (i >= n) break;
+      bool take = key[r] > T;
+      if (key[r] == T) {
+        take = eq_rank < need;
+        ++eq_rank;
+      }
+      if (take) {
+        if (pos < k) EMIT(pos, i, key[r]);
+        ++pos;
+      }
+    }
+    (void)gt_tot;
     sel_base += sel_tot;
     eq_base += eq_tot;
   }
-  for (int i = sel_base + tid; i < k; i += kTopkThreads) out[i] = -1;   // unreachable when n > k
+}
+
+struct TopkArgs {
+  const float* scores;
+  int64_t stride;
+  const int32_t* seq_lens;
+  int Sq, k;
+  int chunk;          // C: positions per stage-1 chunk
+  int max_chunks;     // chunk slots per row in the workspace
+  uint2* cand;        // [rows, max_chunks, k] (key, position)
+  int32_t* idx;
+};
+
+__device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
+  const int b = row / a.Sq, t = row % a.Sq;
+  const int n = a.seq_lens[b] - a.Sq + 1 + t;
+  return n < 0 ? 0 : n;
+}
+
+// stage 1: grid (max_chunks, rows)
+__global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
+  extern __shared__ uint32_t skeys[];
+  __shared__ TopkShared sh;
+  const int row = blockIdx.y, c = blockIdx.x;
+  const int n = row_len(a, row);
+  if (n <= a.k) return;                       // stage 2 writes 0..n-1 directly
+  const int lo = c * a.chunk;
+  if (lo >= n) return;
+  const int len = min(a.chunk, n - lo);
+  const float* src = a.scores + (int64_t)row * a.stride + lo;
+  uint2* out = a.cand + ((int64_t)row * a.max_chunks + c) * a.k;
+  for (int i0 = 0; i0 < len; i0 += 8 * kTopkThreads) {      // 8 independent loads in flight
+    float v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = i0 + r * kTopkThreads + threadIdx.x;
+      v[r] = (i < len) ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = i0 + r * kTopkThreads + threadIdx.x;
+      if (i < len) skeys[i] = float_key(v[r]);
+    }
+  }
+  __syncthreads();
+  if (len <= a.k) {
+    for (int i = threadIdx.x; i < len; i += kTopkThreads) out[i] = make_uint2(skeys[i], (uint32_t)(lo + i));
+    return;
+  }
+  uint32_t T;
+  int need;
+  radix_select([&](int i) { return skeys[i]; }, len, a.k, sh, T, need);
+  ordered_take<8>([&](int i) { return skeys[i]; }, len, T, need, a.k, sh,
+                  [&](int slot, int i, uint32_t key) { out[slot] = make_uint2(key, (uint32_t)(lo + i)); });
+}
+
+// stage 2: one work-group per row.  Every chunk but the last contributes exactly k
+// candidates, so the row's candidates are contiguous in the workspace in position order.
+constexpr int kMergeLds = 16384;           // candidate keys staged in LDS (64 KB)
+__global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(TopkArgs a) {
+  extern __shared__ uint32_t ckeys[];
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;
+  const int n = row_len(a, row);
+  int32_t* out = a.idx + (int64_t)row * a.k;
+  if (n <= a.k) {
+    for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const int nch = (n + a.chunk - 1) / a.chunk;
+  const int last_len = n - (nch - 1) * a.chunk;
+  const int n_cand = (nch - 1) * a.k + min(a.k, last_len);
+  const uint2* cand = a.cand + (int64_t)row * a.max_chunks * a.k;
+  uint32_t T;
+  int need;
+  if (n_cand <= kMergeLds) {
+    for (int j0 = 0; j0 < n_cand; j0 += 8 * kTopkThreads) {
+      uint2 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int j = j0 + r * kTopkThreads + threadIdx.x;
+        v[r] = (j < n_cand) ? cand[j] : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int j = j0 + r * kTopkThreads + threadIdx.x;
+        if (j < n_cand) ckeys[j] = v[r].x;
+      }
+    }
+    __syncthreads();
+    radix_select([&](int j) { return ckeys[j]; }, n_cand, a.k, sh, T, need);
+    ordered_take<8>([&](int j) { return ckeys[j]; }, n_cand, T, need, a.k, sh,
+                    [&](int slot, int j, uint32_t) { out[slot] = (int32_t)cand[j].y; });
+  } else {
+    radix_select([&](int j) { return cand[j].x; }, n_cand, a.k, sh, T, need);
+    ordered_take<4>([&](int j) { return cand[j].x; }, n_cand, T, need, a.k, sh,
+                    [&](int slot, int j, uint32_t) { out[slot] = (int32_t)cand[j].y; });
+  }
+}
+
+static void topk_geometry(int64_t stride, int k, int& chunk, int& max_chunks) {
+  // about kTargetChunks chunks of the longest row, at least k positions each, at most 128 KB
+  int64_t c = (stride + kTargetChunks - 1) / kTargetChunks;
+  if (c < k) c = k;
+  c = (c + 1023) / 1024 * 1024;
+  if (c > kMaxChunkElems) c = kMaxChunkElems;
+  chunk = (int)c;
+  max_chunks = (int)((stride + c - 1) / c);
 }
 
 }  // namespace dsa
 
-extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k) {
-  (void)B;
-  (void)Sq;
-  (void)k;
-  return 0;
+extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
+  if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
+  int chunk, max_chunks;
+  dsa::topk_geometry(score_stride, k, chunk, max_chunks);
+  return (size_t)B * Sq * max_chunks * k * sizeof(uint2);
 }
 
 extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int Sq,
                                  int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+  using namespace dsa;
   DSA_CHECK_ARG(B >= 0 && Sq >= 1 && k >= 1, "dsa_topk: bad sizes");
   if (B == 0) return DSA_OK;
   DSA_CHECK_ARG(scores && seq_lens && idx, "dsa_topk: null pointer");
-  DSA_CHECK_ARG(score_stride >= 1, "dsa_topk: score_stride < 1");
+  DSA_CHECK_ARG(score_stride >= 1 && score_stride < ((int64_t)1 << 31), "dsa_topk: bad score_stride");
   DSA_CHECK_SUPPORTED(k <= 8192, "dsa_topk: k > 8192");
-  DSA_CHECK_ARG((int64_t)B * Sq <= 0x7fffffff, "dsa_topk: too many rows");
-  hipLaunchKernelGGL(dsa::topk_kernel, dim3((unsigned)(B * Sq)), dim3(dsa::kTopkThreads), 0, stream, scores,
-                     score_stride, seq_lens, Sq, k, idx);
-  return dsa::launch_status("dsa_topk");
+  DSA_CHECK_ARG((int64_t)B * Sq <= 65535, "dsa_topk: more than 65535 rows");
+  const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
+  if (ws == nullptr || ws_bytes < need) {
+    set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
+    return DSA_ERR_WORKSPACE;
+  }
+  TopkArgs a{};
+  a.scores = scores;
+  a.stride = score_stride;
+  a.seq_lens = seq_lens;
+  a.Sq = Sq;
+  a.k = k;
+  topk_geometry(score_stride, k, a.chunk, a.max_chunks);
+  a.cand = static_cast<uint2*>(ws);
+  a.idx = idx;
+  const size_t lds = (size_t)a.chunk * sizeof(uint32_t);
+  static bool attr = false;
+  if (!attr) {
+    hipFuncSetAttribute((const void*)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)(kMaxChunkElems * sizeof(uint32_t)));
+    hipFuncSetAttribute((const void*)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)(kMergeLds * sizeof(uint32_t)));
+    attr = true;
+  }
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
+  dsa_status_t st = launch_status("dsa_topk(chunk)");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(B * Sq), dim3(kTopkThreads), kMergeLds * sizeof(uint32_t), stream, a);
+  return launch_status("dsa_topk(merge)");
 }
