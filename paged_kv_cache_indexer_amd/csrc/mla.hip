@@ -4,19 +4,20 @@
 // attention reads only the top-k positions).  Split-KV decode with fp32 partial
 // (o, lse) and an LSE-rescaling merge (TokenSpeed audit, two-stage split-KV decode).
 //
-// Work-group = NW waves (NW = 1, 2 or 4) for 32*NW heads of one query row and one split
-// of its selected rows; one work-group per CU, one wave per SIMD, so each wave owns the
-// full 512-entry register file.  Wave w handles heads [32w, 32w+32):
-//   S^T[32 tokens x 32 heads] = K_tile[32 x 576] . q^T     (bf16 MFMA 32x32x16, 36 steps)
-//     with q^T resident in VGPRs for the whole split;
-//   O^T[512 dims x 32 heads] += V^T[512 x 32 tokens] . P^T  (bf16 MFMA 32x32x16)
-//     heads sit on the N axis, so each lane owns one head's running max / sum and the
-//     rescale is a per-lane scalar; P^T is the S^T accumulator itself (rounded to
-//     bf16), and V^T is written to LDS in the token order that layout implies.
+// Work-group = 2*HG waves (one per SIMD) for 32*HG heads of one query row and one split
+// of its selected rows.  Wave (hg, half) owns heads [32hg, 32hg+32) and
+//   S^T[32 tokens x 32 heads] partial = K_tile[:, half] . q^T[half]   (bf16 MFMA 32x32x16,
+//     18 steps over its 288 of the 576 latent dims, q^T resident in VGPRs); the two
+//     halves of a head group swap partial S^T through LDS and both hold the full sum;
+//   O^T[256 dims x 32 heads] += V^T[half] . P^T                        (bf16 MFMA 32x32x16)
+//     over its 256 of the 512 value dims.  Heads sit on the N axis, so each lane owns one
+//     head's running max / sum and the rescale is a per-lane scalar; P^T is the S^T
+//     accumulator itself (rounded to bf16), and V^T is written to LDS in the token order
+//     that layout implies.
 // The K tile is double-buffered in LDS; the next tile's rows are loaded into registers
 // while the current one is computed.
-// Online softmax in base 2 with a lazy rescale (the running max is only moved when
-// it grows by more than 2^8), which leaves o and lse mathematically unchanged.
+// Online softmax in base 2 with a lazy rescale (the running max is only moved when it
+// grows by more than 2^8), which leaves o and lse mathematically unchanged.
 #include "common.h"
 
 namespace dsa {
@@ -53,23 +54,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-template <int NW>
-__global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
+template <int HG>
+__global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
+  constexpr int NW = 2 * HG;
   constexpr int NT = 64 * NW;
   constexpr int CPT = (kTileChunks + NT - 1) / NT;      // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t klds[2][kTT * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVDim * kVStride];
+  __shared__ __attribute__((aligned(16))) float xch[NW][16][64];      // partial S^T exchange
   __shared__ int64_t rowoff[kMaxSplit];  // byte offset of each selected row of the split, -1 = none
   __shared__ int tvalid[2][kTT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = wave >> 1, half = wave & 1;
   const int n = lane & 31, g = lane >> 5;
-  const int nhb = (a.H + 32 * NW - 1) / (32 * NW);
+  const int nhb = (a.H + 32 * HG - 1) / (32 * HG);
   const int qr = blockIdx.y / nhb;
   const int hb = blockIdx.y % nhb;
   const int b = qr / a.Sq;
   const int split = blockIdx.x;
-  const int head = hb * 32 * NW + wave * 32 + n;
+  const int head = hb * 32 * HG + hg * 32 + n;
   const bool head_ok = head < a.H;
 
   const int e_begin = split * a.per_split;
@@ -118,21 +122,21 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
     store_tile(0, e_begin);
   }
 
-  // ---- q^T operand: 36 k-steps of 16 over the 576 latent dims
-  bf16x8 qb[36];
+  // ---- q^T operand: 18 k-steps of 16 over this wave's 288 latent dims
+  bf16x8 qb[18];
   {
-    const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + g * 8;
+    const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + half * 288 + g * 8;
 #pragma unroll
-    for (int j = 0; j < 36; ++j) {
+    for (int j = 0; j < 18; ++j) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + j * 16);
       if (!head_ok) v = bf16x8{};
       qb[j] = v;
     }
   }
 
-  f32x16 oacc[16];
+  f32x16 oacc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < 8; ++i) oacc[i] = f32x16{};
   float m_used = -INFINITY;     // log2-domain running max used for p
   float l_part = 0.0f;          // this lane's share of sum p (fp32 p: for lse)
   float lr_part = 0.0f;         // this lane's share of sum bf16(p) (the PV weights: for o)
@@ -140,7 +144,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   int cur = 0;
   for (int e0 = e_begin; e0 < e_end; e0 += kTT, cur ^= 1) {
     const bool has_next = e0 + kTT < e_end;
-    __syncthreads();              // K[cur] ready; V^T and K[cur^1] free
+    __syncthreads();              // K[cur] ready; V^T, xch and K[cur^1] free
 
     // ---- V^T from K[cur]: 8 tokens x 8 dims blocks, transposed through registers
     for (int blk = tid; blk < 4 * (kVDim / 8); blk += NT) {
@@ -164,22 +168,26 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
         *reinterpret_cast<u32x4*>(vt + (db * 8 + e) * kVStride + ks * 16 + gg * 8) = ov;
       }
     }
-    __syncthreads();              // V^T ready
     if (has_next) load_tile(e0 + kTT);
 
-    // ---- S^T = K . q^T; LDS operand reads run 3 MFMAs ahead
+    // ---- partial S^T over this wave's half of the latent dims; operand reads run ahead
     f32x16 s = f32x16{};
     {
-      const uint16_t* kp = &klds[cur][n * kKStride + g * 8];
+      const uint16_t* kp = &klds[cur][n * kKStride + half * 288 + g * 8];
       bf16x8 ring[4];
 #pragma unroll
       for (int j = 0; j < 3; ++j) ring[j] = *reinterpret_cast<const bf16x8*>(kp + j * 16);
 #pragma unroll
-      for (int j = 0; j < 36; ++j) {
-        if (j + 3 < 36) ring[(j + 3) & 3] = *reinterpret_cast<const bf16x8*>(kp + (j + 3) * 16);
+      for (int j = 0; j < 18; ++j) {
+        if (j + 3 < 18) ring[(j + 3) & 3] = *reinterpret_cast<const bf16x8*>(kp + (j + 3) * 16);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j & 3], qb[j], s, 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xch[wave][i][lane] = s[i];
+    __syncthreads();              // partial S^T of both halves and V^T ready
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] += xch[wave ^ 1][i][lane];
 
     // ---- online softmax for head n (tokens of lane group g)
     float tmax = -INFINITY;
@@ -196,7 +204,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
       const float m_new = grow ? tmax : m_used;
       const float alpha = (m_used == -INFINITY) ? 0.0f : exp2f(m_used - m_new);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[i] *= alpha;
+      for (int i = 0; i < 8; ++i) oacc[i] *= alpha;
       l_part *= alpha;
       lr_part *= alpha;
       m_used = m_new;
@@ -214,9 +222,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
     const bf16x8 p_lo = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
     const bf16x8 p_hi = __builtin_bit_cast(bf16x8, u32x4{pb[4], pb[5], pb[6], pb[7]});
 
-    // ---- O^T += V^T . P^T over the 512 value dims; operand reads run 3 MFMAs ahead
+    // ---- O^T += V^T . P^T over this wave's 256 value dims; operand reads run ahead
     {
-      const uint16_t* vp = vt + n * kVStride + g * 8;
+      const uint16_t* vp = vt + (half * 256 + n) * kVStride + g * 8;
       auto vop = [&](int i) {   // i = 2*mt + ks
         return *reinterpret_cast<const bf16x8*>(vp + (i >> 1) * 32 * kVStride + (i & 1) * 16);
       };
@@ -224,8 +232,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
 #pragma unroll
       for (int i = 0; i < 3; ++i) ring[i] = vop(i);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + 3 < 32) ring[(i + 3) & 3] = vop(i + 3);
+      for (int i = 0; i < 16; ++i) {
+        if (i + 3 < 16) ring[(i + 3) & 3] = vop(i + 3);
         oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i & 3], (i & 1) ? p_hi : p_lo, oacc[i >> 1], 0,
                                                                0, 0);
       }
@@ -234,35 +242,42 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
     if (has_next) store_tile(cur ^ 1, e0 + kTT);
   }
 
-  // ---- finish: l over both lane groups, normalise, write
+  // ---- finish: l over both lane groups, normalise, write this wave's 256 dims
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   const float lr_tot = lr_part + __shfl_xor(lr_part, 32);
   const float inv = (lr_tot > 0.0f) ? 1.0f / lr_tot : 0.0f;
   const float lse = (l_tot > 0.0f) ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   if (!head_ok) return;
   const bool direct = a.splits == 1;
-  const int64_t obase = direct ? ((int64_t)qr * a.H + head) * kVDim
-                               : ((((int64_t)qr * a.splits + split) * a.H + head)) * kVDim;
+  const int64_t obase = (direct ? ((int64_t)qr * a.H + head) : ((((int64_t)qr * a.splits + split) * a.H + head))) *
+                            kVDim + half * 256;
+  if (!direct) {
 #pragma unroll
-  for (int mt = 0; mt < 16; ++mt) {
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = mt * 32 + i4 * 8 + g * 4;
-      const float v0 = oacc[mt][i4 * 4 + 0] * inv, v1 = oacc[mt][i4 * 4 + 1] * inv;
-      const float v2 = oacc[mt][i4 * 4 + 2] * inv, v3 = oacc[mt][i4 * 4 + 3] * inv;
-      if (!direct) {
-        *reinterpret_cast<f32x4*>(a.part_o + obase + d) = f32x4{v0, v1, v2, v3};
-      } else if (a.o_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + obase + d) = f32x4{v0, v1, v2, v3};
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + d) =
-            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-      }
-    }
-  }
-  if (g == 0) {
-    if (direct) a.lse[(int64_t)qr * a.H + head] = lse;
-    else a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(a.part_o + obase + mt * 32 + i4 * 8 + g * 4) =
+            f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
+                  oacc[mt][i4 * 4 + 3] * inv};
+    if (g == 0 && half == 0) a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
+  } else if (a.o_f32) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + obase + mt * 32 + i4 * 8 + g * 4) =
+            f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
+                  oacc[mt][i4 * 4 + 3] * inv};
+    if (g == 0 && half == 0) a.lse[(int64_t)qr * a.H + head] = lse;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + mt * 32 + i4 * 8 + g * 4) =
+            u32x2{pack_bf16x2(oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv),
+                  pack_bf16x2(oacc[mt][i4 * 4 + 2] * inv, oacc[mt][i4 * 4 + 3] * inv)};
+    if (g == 0 && half == 0) a.lse[(int64_t)qr * a.H + head] = lse;
   }
 }
 
@@ -308,7 +323,7 @@ static int device_cus() {
 }
 
 static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_split) {
-  const int wg_heads = (H >= 128) ? 128 : (H > 32 ? 64 : 32);
+  const int wg_heads = (H > 32) ? 64 : 32;
   const int64_t wgs = (int64_t)B * Sq * ((H + wg_heads - 1) / wg_heads);
   const int tiles = (k + kTT - 1) / kTT;
   // one work-group per CU
@@ -371,12 +386,10 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
     a.part_lse = a.part_o + (size_t)B * Sq * splits * H * kVDim;
   }
   const int QR = B * Sq;
-  if (H >= 128) {
-    hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(splits, QR * ((H + 127) / 128)), dim3(256), 0, stream, a);
-  } else if (H > 32) {
-    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(splits, QR * ((H + 63) / 64)), dim3(128), 0, stream, a);
+  if (H > 32) {
+    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(splits, QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(splits, QR), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(splits, QR), dim3(128), 0, stream, a);
   }
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
