@@ -5,17 +5,25 @@
 // (o, lse) and an LSE-rescaling merge (TokenSpeed audit, two-stage split-KV decode).
 //
 // Work-group = 2*HG waves (one per SIMD) for 32*HG heads of one query row and one split
-// of its selected rows.  Wave (hg, half) owns heads [32hg, 32hg+32) and
+// of its selected rows.  Wave (hg, half) owns heads [32hg, 32hg+32) and computes
 //   S^T[32 tokens x 32 heads] partial = K_tile[:, half] . q^T[half]   (bf16 MFMA 32x32x16,
 //     18 steps over its 288 of the 576 latent dims, q^T resident in VGPRs); the two
 //     halves of a head group swap partial S^T through LDS and both hold the full sum;
 //   O^T[256 dims x 32 heads] += V^T[half] . P^T                        (bf16 MFMA 32x32x16)
 //     over its 256 of the 512 value dims.  Heads sit on the N axis, so each lane owns one
 //     head's running max / sum and the rescale is a per-lane scalar; P^T is the S^T
-//     accumulator itself (rounded to bf16), and V^T is written to LDS in the token order
-//     that layout implies.
-// The K tile is double-buffered in LDS; the next tile's rows are loaded into registers
-// while the current one is computed.
+//     accumulator itself (rounded to bf16).  The V^T operand is read straight from the
+//     token-major K tile with LDS transpose reads (ds_read_b64_tr_b16: within each 16-lane
+//     group, lane i receives element i%4 of the 8-byte rows addressed by lanes i/4, 4+i/4,
+//     8+i/4, 12+i/4), so no transposed copy is made.
+// Selected rows stream into a ring of three LDS tiles with LDS-direct loads
+// (global_load_lds_dwordx4: lane i of a wave instruction lands at M0 + 16 i), two tiles
+// ahead of the one being computed; no VGPRs hold rows in flight.  A tile is stored as
+// 1 KB blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one
+// wave instruction fetches eight whole 128-byte lines and each lane streams one row.
+// Inside a block, 16-byte chunk c of token m sits at position m*8 + ((c%8) ^ swz(m)),
+// which keeps both the K reads (one chunk of 32 tokens) and the transpose reads (two
+// chunks of 4 tokens) free of LDS bank conflicts.
 // Online softmax in base 2 with a lazy rescale (the running max is only moved when it
 // grows by more than 2^8), which leaves o and lse mathematically unchanged.
 #include "common.h"
@@ -27,9 +35,9 @@ constexpr int kVDim = 512;
 constexpr int kRowBytes = kRowEl * 2;
 constexpr int kTT = 32;                     // tokens per tile
 constexpr int kChunks = kRowBytes / 16;     // 72 x 16 B per row
-constexpr int kTileChunks = kTT * kChunks;  // 2304
-constexpr int kKStride = kRowEl + 8;        // K tile row stride (bf16), 1168 B
-constexpr int kVStride = kTT + 8;           // V^T row stride (bf16), 80 B
+constexpr int kTileSlots = kTT * kChunks;   // 2304 chunk slots per tile
+constexpr int kTileBytes = kTileSlots * 16; // 36864
+constexpr int kRing = 3;                    // LDS tiles: one computed, two in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;
@@ -54,73 +62,92 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
+// chunk swizzle of token m (mod 8) inside a 1 KB block
+__device__ __forceinline__ int chunk_swz(int m) { return ((m << 1) & 6) | ((m >> 2) & 1); }
+
+// byte offset of 16-byte chunk c of token n inside a tile
+__device__ __forceinline__ int chunk_byte(int n, int c) {
+  return ((((c >> 3) << 2) + (n >> 3)) * 64 + (n & 7) * 8 + ((c & 7) ^ chunk_swz(n & 7))) * 16;
+}
+
+// 16 bytes from global memory into LDS at M0 + 16 * lane (M0 = lds_addr, wave-uniform).  No
+// instruction offset is used: it would move the LDS destination as well.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr) : "m0");
+}
+
+// LDS-direct loads R..CPT-1 of one tile: load r fetches chunk group r / NSRC of the row in
+// src[r % NSRC] into 1 KB block r * NW of the wave's stripe
+template <int R, int CPT, int NSRC, int NW>
+__device__ __forceinline__ void dma_tile(const char* const* src, uint32_t dst) {
+  if constexpr (R < CPT) {
+    lds_dma16(src[R % NSRC] + (R / NSRC) * 128, dst + R * NW * 1024);
+    dma_tile<R + 1, CPT, NSRC, NW>(src, dst);
+  }
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_u8* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// grid position -> (unit = query row x split, head block).  The head blocks of one unit
+// read the same rows; they are placed on one XCD (work-groups go round-robin over the 8
+// XCDs) so that the second reader finds the rows in that XCD's L2.
+__device__ __forceinline__ void mla_block_unit(int nhb, int& unit, int& hb) {
+  const int x = blockIdx.x, G = gridDim.x;
+  if (G % (8 * nhb) == 0) {
+    const int xcd = x & 7, kk = x >> 3;
+    hb = kk % nhb;
+    unit = (kk / nhb) * 8 + xcd;
+  } else {
+    hb = x % nhb;
+    unit = x / nhb;
+  }
+}
+
 template <int HG>
 __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   constexpr int NW = 2 * HG;
   constexpr int NT = 64 * NW;
-  constexpr int CPT = (kTileChunks + NT - 1) / NT;      // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t klds[2][kTT * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kVDim * kVStride];
-  __shared__ __attribute__((aligned(16))) float xch[NW][16][64];      // partial S^T exchange
-  __shared__ int64_t rowoff[kMaxSplit];  // byte offset of each selected row of the split, -1 = none
-  __shared__ int tvalid[2][kTT];
+  constexpr int CPT = kTileSlots / NT;      // LDS-direct loads per thread per tile
+  static_assert(kTileSlots % NT == 0, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kTileBytes];
+  __shared__ f32x4 xch[NW][4][64];          // partial S^T exchange between the halves
+  __shared__ int64_t rowoff[kMaxSplit];     // byte offset of each selected row of the split, -1 = none
+  __shared__ uint32_t tmask[kMaxSplit / kTT];  // valid-row bits per tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave >> 1, half = wave & 1;
   const int n = lane & 31, g = lane >> 5;
   const int nhb = (a.H + 32 * HG - 1) / (32 * HG);
-  const int qr = blockIdx.y / nhb;
-  const int hb = blockIdx.y % nhb;
+  int unit, hb;
+  mla_block_unit(nhb, unit, hb);
+  const int qr = unit / a.splits;
+  const int split = unit - qr * a.splits;
   const int b = qr / a.Sq;
-  const int split = blockIdx.x;
   const int head = hb * 32 * HG + hg * 32 + n;
   const bool head_ok = head < a.H;
 
   const int e_begin = split * a.per_split;
-  int e_end = e_begin + a.per_split;
-  if (e_end > a.k) e_end = a.k;
+  const int e_end = min(e_begin + a.per_split, a.k);
+  const int ntiles = (e_end - e_begin + kTT - 1) / kTT;
   const int32_t* idx = a.idx + (int64_t)qr * a.k;
-
-  // resolve every selected row of this split once: index -> page table -> byte offset
-  for (int e = e_begin + tid; e < e_end; e += NT) {
-    const int32_t p = idx[e];
-    const int64_t row = a.rows.row(b, p);
-    if (row < 0 && p >= 0) count_error(a.err);
-    rowoff[e - e_begin] = row >= 0 ? row * kRowBytes : -1;
-  }
-  for (int e = e_end + tid; e < e_begin + a.per_split && e - e_begin < kMaxSplit; e += NT) rowoff[e - e_begin] = -1;
-  __syncthreads();
-
-  u32x4 stage[CPT];
-  auto load_tile = [&](int e0) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + NT * r;
-      stage[r] = u32x4{0, 0, 0, 0};
-      if (c < kTileChunks) {
-        const int tok = c / kChunks, ch = c - tok * kChunks;
-        const int64_t off = rowoff[e0 - e_begin + tok];
-        if (off >= 0) stage[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.rows.base + off) + ch);
-      }
-    }
-  };
-  auto store_tile = [&](int bf, int e0) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + NT * r;
-      if (c < kTileChunks) {
-        const int tok = c / kChunks, ch = c - tok * kChunks;
-        *reinterpret_cast<u32x4*>(&klds[bf][tok * kKStride + ch * 8]) = stage[r];
-      }
-    }
-    if (tid < kTT) tvalid[bf][tid] = rowoff[e0 - e_begin + tid] >= 0;
-  };
-
-  // ---- prologue: tile 0 into K buffer 0
-  if (e_begin < e_end) {
-    load_tile(e_begin);
-    store_tile(0, e_begin);
-  }
+  // rows that are padding or unresolvable are loaded from this query row instead (finite
+  // values; their probabilities are exactly zero)
+  const char* stand_in = reinterpret_cast<const char*>(a.q + (int64_t)qr * a.H * kRowEl);
 
   // ---- q^T operand: 18 k-steps of 16 over this wave's 288 latent dims
   bf16x8 qb[18];
@@ -134,6 +161,64 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
     }
   }
 
+  // ---- resolve every selected row of this split once: index -> page table -> byte offset
+  for (int e = tid; e < ntiles * kTT; e += NT) {
+    int64_t off = -1;
+    if (e_begin + e < e_end) {
+      const int32_t p = idx[e_begin + e];
+      const int64_t row = a.rows.row(b, p);
+      if (row < 0 && p >= 0) count_error(a.err);
+      if (row >= 0) off = row * kRowBytes;
+    }
+    rowoff[e] = off;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(off >= 0);
+    if (lane == 0) {            // e is a multiple of 64 here: lanes 0-31 and 32-63 are two tiles
+      tmask[e >> 5] = (uint32_t)m;
+      if ((e >> 5) + 1 < ntiles) tmask[(e >> 5) + 1] = (uint32_t)(m >> 32);
+    }
+  }
+
+  // ---- per-lane constants of the three access patterns
+  constexpr int NSRC = 4 / NW;  // token groups one lane streams per tile
+  // LDS-direct load r of this lane: token group (wave + NW * (r % NSRC)), chunk group
+  // r / NSRC; the lane fetches chunk ((lane & 7) ^ swz) of token 8 * group + lane / 8
+  const int dlane = ((lane & 7) ^ chunk_swz(lane >> 3)) * 16;
+  int qoff[4];                  // K operand of k-step j: qoff[j % 4] + 4096 (j / 4)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qoff[j] = chunk_byte(n, half * 36 + 2 * j + g);
+  int voff[2];                  // V^T operand (transpose read) of m-tile mt: voff[mt % 2] + 4096 (mt / 2)
+  {
+    const int blk = lane >> 4, s16 = lane & 15, jj = s16 >> 2, qq = s16 & 3;
+    const int tok = (blk >> 1) * 4 + jj;
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp)
+      voff[mp] = chunk_byte(tok, half * 32 + mp * 4 + (blk & 1) * 2 + (qq >> 1)) + (qq & 1) * 8;
+  }
+  wait_vmcnt<0>();              // q^T is resident before any row load is in flight
+  __syncthreads();              // rowoff / tmask ready
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
+  const char* nsrc[NSRC];       // rows of the next tile to issue
+  auto prepare = [&](int t) {
+#pragma unroll
+    for (int p = 0; p < NSRC; ++p) {
+      const int64_t off = rowoff[t * kTT + (wave + NW * p) * 8 + (lane >> 3)];
+      nsrc[p] = (off >= 0 ? a.rows.base + off : stand_in) + dlane;
+    }
+  };
+  auto issue = [&](int t) {
+    const uint32_t dst = ring_lds + (uint32_t)((t % kRing) * kTileBytes + wave * 1024);
+    dma_tile<0, CPT, NSRC, NW>(nsrc, dst);
+  };
+
+  prepare(0);
+  issue(0);
+  if (ntiles > 1) {
+    prepare(1);
+    issue(1);
+  }
+  if (ntiles > 2) prepare(2);
+
   f32x16 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x16{};
@@ -141,105 +226,99 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   float l_part = 0.0f;          // this lane's share of sum p (fp32 p: for lse)
   float lr_part = 0.0f;         // this lane's share of sum bf16(p) (the PV weights: for o)
 
-  int cur = 0;
-  for (int e0 = e_begin; e0 < e_end; e0 += kTT, cur ^= 1) {
-    const bool has_next = e0 + kTT < e_end;
-    __syncthreads();              // K[cur] ready; V^T, xch and K[cur^1] free
-
-    // ---- V^T from K[cur]: 8 tokens x 8 dims blocks, transposed through registers
-    for (int blk = tid; blk < 4 * (kVDim / 8); blk += NT) {
-      const int grp = blk & 3, db = blk >> 2;        // token group (ks, gg), dim block
-      const int ks = grp >> 1, gg = grp & 1;
-      u32x4 r8[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int tok = ks * 16 + (s >> 2) * 8 + gg * 4 + (s & 3);
-        r8[s] = *reinterpret_cast<const u32x4*>(&klds[cur][tok * kKStride + db * 8]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-        u32x4 ov;
-        ov.x = __builtin_amdgcn_perm(r8[1][w], r8[0][w], sel);
-        ov.y = __builtin_amdgcn_perm(r8[3][w], r8[2][w], sel);
-        ov.z = __builtin_amdgcn_perm(r8[5][w], r8[4][w], sel);
-        ov.w = __builtin_amdgcn_perm(r8[7][w], r8[6][w], sel);
-        *reinterpret_cast<u32x4*>(vt + (db * 8 + e) * kVStride + ks * 16 + gg * 8) = ov;
-      }
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles)
+      wait_vmcnt<CPT>();        // this wave's loads of tile t are done (tile t+1 may be in flight)
+    else
+      wait_vmcnt<0>();
+    __syncthreads();            // tile t complete for all waves; slot (t+2)%3 and xch free
+    if (t + 2 < ntiles) {
+      issue(t + 2);
+      if (t + 3 < ntiles) prepare(t + 3);
     }
-    if (has_next) load_tile(e0 + kTT);
+    const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((t % kRing) * kTileBytes));
 
     // ---- partial S^T over this wave's half of the latent dims; operand reads run ahead
     f32x16 s = f32x16{};
     {
-      const uint16_t* kp = &klds[cur][n * kKStride + half * 288 + g * 8];
-      bf16x8 ring[4];
+      auto kop = [&](int j) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + qoff[j & 3] + (j >> 2) * 4096);
+      };
+      bf16x8 rk[4];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) ring[j] = *reinterpret_cast<const bf16x8*>(kp + j * 16);
+      for (int j = 0; j < 3; ++j) rk[j] = kop(j);
 #pragma unroll
       for (int j = 0; j < 18; ++j) {
-        if (j + 3 < 18) ring[(j + 3) & 3] = *reinterpret_cast<const bf16x8*>(kp + (j + 3) * 16);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j & 3], qb[j], s, 0, 0, 0);
+        if (j + 3 < 18) rk[(j + 3) & 3] = kop(j + 3);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rk[j & 3], qb[j], s, 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xch[wave][i][lane] = s[i];
-    __syncthreads();              // partial S^T of both halves and V^T ready
+    for (int i4 = 0; i4 < 4; ++i4) xch[wave][i4][lane] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
+    __syncthreads();            // partial S^T of both halves ready
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] += xch[wave ^ 1][i][lane];
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 o = xch[wave ^ 1][i4][lane];
+      s[4 * i4] += o.x;
+      s[4 * i4 + 1] += o.y;
+      s[4 * i4 + 2] += o.z;
+      s[4 * i4 + 3] += o.w;
+    }
 
     // ---- online softmax for head n (tokens of lane group g)
-    float tmax = -INFINITY;
+    const uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[t]);
+    if (vmask != 0xffffffffu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = (i >> 2) * 8 + g * 4 + (i & 3);
-      const float x = tvalid[cur][tok] ? s[i] * a.scale_log2 : -INFINITY;
-      s[i] = x;
-      tmax = fmaxf(tmax, x);
+      for (int i = 0; i < 16; ++i) {
+        const int tok = (i >> 2) * 8 + g * 4 + (i & 3);
+        if (!((vmask >> tok) & 1u)) s[i] = -INFINITY;
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    float tmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;   // scale > 0 keeps the order
     const bool grow = tmax > m_used + kLazy || (m_used == -INFINITY && tmax > -INFINITY);
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? tmax : m_used;
-      const float alpha = (m_used == -INFINITY) ? 0.0f : exp2f(m_used - m_new);
+      const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
 #pragma unroll
       for (int i = 0; i < 8; ++i) oacc[i] *= alpha;
       l_part *= alpha;
       lr_part *= alpha;
       m_used = m_new;
     }
+    const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
     uint32_t pb[8];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_used);
-      const float p1 = (s[i + 1] == -INFINITY) ? 0.0f : exp2f(s[i + 1] - m_used);
-      const uint32_t w = pack_bf16x2(p0, p1);
-      pb[i >> 1] = w;
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], a.scale_log2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], a.scale_log2, -msub));
+      const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+      pb[i] = w;
       l_part += p0 + p1;
-      lr_part += bf16_bits_to_f32(w & 0xffffu) + bf16_bits_to_f32(w >> 16);
+      lr_part += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
     }
     const bf16x8 p_lo = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
     const bf16x8 p_hi = __builtin_bit_cast(bf16x8, u32x4{pb[4], pb[5], pb[6], pb[7]});
 
     // ---- O^T += V^T . P^T over this wave's 256 value dims; operand reads run ahead
     {
-      const uint16_t* vp = vt + (half * 256 + n) * kVStride + g * 8;
-      auto vop = [&](int i) {   // i = 2*mt + ks
-        return *reinterpret_cast<const bf16x8*>(vp + (i >> 1) * 32 * kVStride + (i & 1) * 16);
+      auto vop = [&](int i) {   // i = 2*mt + ks: tokens ks*16 + {g*4.., 8 + g*4..}
+        const lds_u8* p = tile + voff[(i >> 1) & 1] + (i >> 2) * 4096 + (i & 1) * 2048;   // ks: token groups 2ks, 2ks+1
+        const u32x2 lo = lds_read_tr16(p);
+        const u32x2 hi = lds_read_tr16(p + 1024);
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       };
-      bf16x8 ring[4];
+      bf16x8 rv[4];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) ring[i] = vop(i);
+      for (int i = 0; i < 3; ++i) rv[i] = vop(i);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (i + 3 < 16) ring[(i + 3) & 3] = vop(i + 3);
-        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i & 3], (i & 1) ? p_hi : p_lo, oacc[i >> 1], 0,
-                                                               0, 0);
+        if (i + 3 < 16) rv[(i + 3) & 3] = vop(i + 3);
+        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv[i & 3], (i & 1) ? p_hi : p_lo, oacc[i >> 1], 0, 0, 0);
       }
     }
-
-    if (has_next) store_tile(cur ^ 1, e0 + kTT);
   }
 
   // ---- finish: l over both lane groups, normalise, write this wave's 256 dims
@@ -359,6 +438,7 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   DSA_CHECK_ARG(((uintptr_t)rows->base & 15) == 0 && ((uintptr_t)q & 15) == 0,
                 "dsa_sparse_mla_decode: rows and q must be 16-byte aligned");
   DSA_CHECK_ARG(o_dtype == DSA_BF16 || o_dtype == DSA_F32, "dsa_sparse_mla_decode: o_dtype must be BF16 or F32");
+  DSA_CHECK_ARG(scale > 0.0f && scale < INFINITY, "dsa_sparse_mla_decode: scale must be positive and finite");
   DSA_CHECK_SUPPORTED(H % 16 == 0 && k <= 65536, "dsa_sparse_mla_decode: needs H %% 16 == 0 and k <= 65536");
   if (rows->page_table) DSA_CHECK_ARG(rows->page_size > 0, "dsa_sparse_mla_decode: bad page_size");
   int splits, per;
@@ -387,9 +467,9 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   }
   const int QR = B * Sq;
   if (H > 32) {
-    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(splits, QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(splits * QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(splits, QR), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(splits * QR), dim3(128), 0, stream, a);
   }
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
