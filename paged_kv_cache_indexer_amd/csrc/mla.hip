@@ -53,7 +53,7 @@ struct MlaArgs {
   void* o;                 // [QR, H, 512] (o_f32 ? float : bf16)   -- splits == 1
   int o_f32;
   float* lse;              // [QR, H]                                 -- splits == 1
-  float* part_o;           // [QR, splits, H, 512]                    -- splits > 1
+  void* part_o;            // [QR, splits, H, 512] in o's dtype, normalised   -- splits > 1
   float* part_lse;         // [QR, splits, H]
   int32_t* err;
 };
@@ -331,13 +331,24 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   const int64_t obase = (direct ? ((int64_t)qr * a.H + head) : ((((int64_t)qr * a.splits + split) * a.H + head))) *
                             kVDim + half * 256;
   if (!direct) {
+    // split partials keep the precision of the final output
+    if (a.o_f32) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<f32x4*>(a.part_o + obase + mt * 32 + i4 * 8 + g * 4) =
-            f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
-                  oacc[mt][i4 * 4 + 3] * inv};
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + obase + mt * 32 + i4 * 8 + g * 4) =
+              f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
+                    oacc[mt][i4 * 4 + 3] * inv};
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + obase + mt * 32 + i4 * 8 + g * 4) =
+              u32x2{pack_bf16x2(oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv),
+                    pack_bf16x2(oacc[mt][i4 * 4 + 2] * inv, oacc[mt][i4 * 4 + 3] * inv)};
+    }
     if (g == 0 && half == 0) a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
   } else if (a.o_f32) {
 #pragma unroll
@@ -360,35 +371,54 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   }
 }
 
-// merge of split partials: one work-group of 128 threads per (query row, head)
-__global__ void __launch_bounds__(128) mla_merge_kernel(MlaArgs a) {
-  const int qr = blockIdx.y, head = blockIdx.x;
+// merge of split partials: 64 threads per (query row, head), 8 value dims per thread
+constexpr int kMergeHeads = 4;   // heads per 256-thread work-group
+
+__global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) {
+  const int qr = blockIdx.y;
+  const int head = blockIdx.x * kMergeHeads + (threadIdx.x >> 6);
+  if (head >= a.H) return;
   const int S = a.splits;
+  const int d = (threadIdx.x & 63) * 8;
+  const float* pl = a.part_lse + (int64_t)qr * S * a.H + head;
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[((int64_t)qr * S + s) * a.H + head]);
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * a.H]);
   float wsum = 0.0f;
-  f32x4 acc = {0, 0, 0, 0};
-  const int d = threadIdx.x * 4;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (mx > -INFINITY) {
     for (int s = 0; s < S; ++s) {
-      const int64_t pb = ((int64_t)qr * S + s) * a.H + head;
-      const float l = a.part_lse[pb];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - mx);
+      const float l = pl[(int64_t)s * a.H];
+      const float w = (l == -INFINITY) ? 0.0f : __expf(l - mx);
       wsum += w;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + pb * kVDim + d);
-      acc += w * v;
+      const int64_t pb = (((int64_t)qr * S + s) * a.H + head) * kVDim + d;
+      if (a.o_f32) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + pb);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + pb + 4);
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += w * v0[i];
+          acc[4 + i] += w * v1[i];
+        }
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + pb);
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += w * __uint_as_float(v[i] << 16);
+          acc[2 * i + 1] += w * __uint_as_float(v[i] & 0xffff0000u);
+        }
+      }
     }
-    acc *= 1.0f / wsum;
+    const float inv = 1.0f / wsum;
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
   }
   const int64_t ob = ((int64_t)qr * a.H + head) * kVDim + d;
   if (a.o_f32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ob) = acc;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ob) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ob + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   } else {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + ob) =
-        u32x2{pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + ob) =
+        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+              pack_bf16x2(acc[6], acc[7])};
   }
-  if (threadIdx.x == 0) a.lse[(int64_t)qr * a.H + head] = (mx > -INFINITY) ? mx + __logf(wsum) : -INFINITY;
+  if ((threadIdx.x & 63) == 0) a.lse[(int64_t)qr * a.H + head] = (mx > -INFINITY) ? mx + __logf(wsum) : -INFINITY;
 }
 
 static int device_cus() {
@@ -462,8 +492,8 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   a.o_f32 = (o_dtype == DSA_F32);
   a.lse = lse;
   if (splits > 1) {
-    a.part_o = static_cast<float*>(ws);
-    a.part_lse = a.part_o + (size_t)B * Sq * splits * H * kVDim;
+    a.part_lse = static_cast<float*>(ws);
+    a.part_o = a.part_lse + (size_t)B * Sq * splits * H;
   }
   const int QR = B * Sq;
   if (H > 32) {
@@ -473,6 +503,7 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   }
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(H, QR), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
+                     stream, a);
   return launch_status("dsa_sparse_mla_decode(merge)");
 }
