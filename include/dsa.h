@@ -218,8 +218,11 @@ dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int
  *   rows   row store of latent rows, row_bytes = 1152
  *   o      [B, Sq, H, 512], o_dtype BF16 (round-to-nearest-even) or F32
  *   lse    [B, Sq, H] float32
- *   ws     workspace of dsa_sparse_mla_workspace_size(B, Sq, H, k) bytes
- * Supported: H a multiple of 16 (H % 128 == 0 runs the full-width kernel), k <= 65536.
+ *   scale  softmax scale, positive and finite (else DSA_ERR_INVALID_ARG)
+ *   ws     workspace of dsa_sparse_mla_workspace_size(B, Sq, H, k) bytes (16-byte aligned);
+ *          NULL allowed when that size is 0.  Holds the split partials: lse as float32,
+ *          o normalised in o_dtype.  Its contents are scratch between calls.
+ * Supported: H a multiple of 16 (H > 32 runs 64-head work-groups), k <= 65536.
  */
 size_t dsa_sparse_mla_workspace_size(int B, int Sq, int H, int k);
 dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_rows_t* rows,
