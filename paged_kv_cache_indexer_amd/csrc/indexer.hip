@@ -89,13 +89,70 @@ struct MfmaArgs {
 // HMT: 32-row M tiles per query (H / 32); NQ: queries per wave; RG: waves that share one
 // token tile (each covers NQ of the Sq queries).  MT_W = HMT * NQ M tiles per wave.
 //
-// Work is cut into units of up to kUnitTiles tiles inside one request.  A wave loads the
+// Work is cut into units of up to `ut` tiles inside one request.  A wave loads the
 // request's queries once per unit, then streams the unit's tiles through three fixed
 // register slots (two tiles in flight behind the one being computed).  Every fetch is
 // issued unconditionally (past the unit's end it re-reads the last tile, an L2 hit), and
 // the page lookup is a scalar load, so the steady-state loop never waits on more than
-// the tile it is about to use.
-constexpr int kUnitTiles = 30;   // a multiple of the 3 slots
+// the tile it is about to use.  The unit size is derived on the device from the total
+// tile count so that the units fill the grid's wave slots in one round.
+constexpr int kPrefixPerThread = (kMaxB + 255) / 256;
+
+// unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; returns ut
+__device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int* unit_off, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tiles[kPrefixPerThread];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPrefixPerThread; ++i) {
+    const int b = tid * kPrefixPerThread + i;
+    tiles[i] = (b < B) ? (seq_lens[b] + kTile - 1) / kTile : 0;
+    mine += tiles[i];
+  }
+  auto block_scan = [&](int v, int& total) {     // exclusive scan over the 256 threads
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int s = wsum[w];
+      if (w < wave) before += s;
+      total += s;
+    }
+    __syncthreads();
+    return before + incl - v;
+  };
+  int total_tiles = 0;
+  block_scan(mine, total_tiles);
+  int ut = (total_tiles + wave_slots - 1) / wave_slots;
+  ut = ((ut + 2) / 3) * 3;                        // whole passes over the three slots
+  if (ut < 3) ut = 3;
+  int units[kPrefixPerThread];
+  int my_units = 0;
+#pragma unroll
+  for (int i = 0; i < kPrefixPerThread; ++i) {
+    units[i] = (tiles[i] + ut - 1) / ut;
+    my_units += units[i];
+  }
+  int total_units = 0;
+  int off = block_scan(my_units, total_units);
+#pragma unroll
+  for (int i = 0; i < kPrefixPerThread; ++i) {
+    const int b = tid * kPrefixPerThread + i;
+    if (b < B) unit_off[b] = off;
+    off += units[i];
+  }
+  if (tid == 0) unit_off[B] = total_units;
+  __syncthreads();
+  return ut;
+}
 
 template <bool QFP8, int HMT, int NQ, int RG>
 __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
@@ -114,16 +171,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   const int g = lane >> 5;                         // lane group
   const int ps = a.keys.page_size;
 
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int b = 0; b < a.B; ++b) {
-      unit_off[b] = acc;
-      const int tiles = (a.seq_lens[b] + kTile - 1) / kTile;
-      acc += (tiles + kUnitTiles - 1) / kUnitTiles;
-    }
-    unit_off[a.B] = acc;
-  }
-  __syncthreads();
+  __shared__ int scan_wsum[4];
+  const int ut = __builtin_amdgcn_readfirstlane(indexer_units(a.seq_lens, a.B, gridDim.x * WPU, unit_off, scan_wsum));
   const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
   const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
@@ -148,8 +197,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
     }
     const int L = scalar_load(a.seq_lens + b);
     const int n_tiles_b = (L + kTile - 1) / kTile;
-    const int t_begin = (u - __builtin_amdgcn_readfirstlane(unit_off[b])) * kUnitTiles;
-    const int t_end = min(t_begin + kUnitTiles, n_tiles_b);
+    const int t_begin = (u - __builtin_amdgcn_readfirstlane(unit_off[b])) * ut;
+    const int t_end = min(t_begin + ut, n_tiles_b);
 
     auto fetch = [&](Slot& sl, int t) {
       t = min(t, t_end - 1);
@@ -170,9 +219,9 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) sl.kb[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + c * 1024));
       // always issue the scale load (a dummy in-bounds read when there is no scale), so
-      // every fetch adds the same number of outstanding loads
-      const float sv = a.k_scale ? a.k_scale[r] : *reinterpret_cast<const float*>(a.keys.base);
-      sl.sig = a.k_scale ? sv : 1.0f;
+      // every fetch adds the same number of outstanding loads; the value is only looked
+      // at in the epilogue, so nothing waits for it here
+      sl.sig = a.k_scale ? a.k_scale[r] : *reinterpret_cast<const float*>(a.keys.base);
     };
 
     // queries and weights of request b for this wave's rows
@@ -263,7 +312,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
         part += __shfl_xor(part, 32);
         const int tq = rg * NQ + qq;
         const int vis = L - a.Sq + 1 + tq;
-        float v = part * cur.sig;
+        float v = a.k_scale ? part * cur.sig : part;
         if (!cur.valid || s >= vis) v = -INFINITY;
         if (live && g == 0 && s < L) a.scores[((int64_t)b * a.Sq + tq) * a.score_stride + s] = v;
       }
