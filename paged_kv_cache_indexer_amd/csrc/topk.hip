@@ -4,16 +4,17 @@
 // Order: score descending, then position ascending; -0.0 == +0.0.  Scores map to
 // order-preserving uint32 keys.
 //
-// Stage 1 (many work-groups per row): the row is cut into chunks of C positions; each
-// chunk is staged in LDS and reduced to its own top-min(k, len) under the same total
-// order, emitted in position order as (key, position) candidates.  Every member of the
-// row's top-k is in its chunk's top-k (fewer than k elements of the whole row precede
-// it), so the candidates contain the answer.
-// Stage 2 (one work-group per row): the exact select over the candidates, which are
-// already in ascending position order and stay in L2, then an ordered compaction that
-// writes the k positions ascending.
+// Stage 1 (many work-groups per row): the row's n positions are cut into chunks of C
+// positions; chunk c (len_c positions) finds its r_c-th largest key X_c, with
+// r_c = ceil(k * len_c / n), so the r_c add up to at least k.
+// Stage 2 (one work-group per row): M = the largest X_c such that the chunks whose X is
+// >= X_c hold at least k keys >= X_c between them, which makes M a lower bound of the
+// row's k-th largest key.  The keys >= M (about k of them on smooth data) are compacted
+// in position order into LDS; the exact select runs over them and an ordered compaction
+// writes the k positions ascending.  If ties at the bound leave more keys than LDS
+// holds, the select runs over the whole row instead.
 //
-// Both stages use the same select: an MSB-first radix search for the k-th largest key T
+// Both stages use the same select: an MSB-first radix search for the r-th largest key T
 // (digits of up to 11 bits, starting below the bits that the smallest and the largest
 // key share) and `need`, the number of keys equal to T that are taken (lowest positions
 // first).
@@ -188,7 +189,7 @@ struct TopkArgs {
   int Sq, k;
   int chunk;          // C: positions per stage-1 chunk
   int max_chunks;     // chunk slots per row in the workspace
-  uint2* cand;        // [rows, max_chunks, k] (key, position)
+  uint32_t* xc;       // [rows, max_chunks] bound key of each chunk
   int32_t* idx;
 };
 
@@ -198,8 +199,15 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
   return n < 0 ? 0 : n;
 }
 
-// stage 1: grid (max_chunks, rows)
-__global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
+// rank of the bound key of a chunk of `len` of the row's `n` positions: the chunks' ranks
+// add up to at least k, and each is at most len (k < n)
+__device__ __forceinline__ int chunk_rank(int k, int len, int n) {
+  return (int)(((int64_t)k * len + n - 1) / n);
+}
+
+// stage 1, grid (max_chunks, rows): X_c = the r_c-th largest key of chunk c, so chunk c
+// holds at least r_c keys >= X_c.
+__global__ void __launch_bounds__(kTopkThreads) topk_bound_kernel(TopkArgs a) {
   extern __shared__ uint32_t skeys[];
   __shared__ TopkShared sh;
   const int row = blockIdx.y, c = blockIdx.x;
@@ -208,39 +216,57 @@ __global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
   const int lo = c * a.chunk;
   if (lo >= n) return;
   const int len = min(a.chunk, n - lo);
+  const int r = chunk_rank(a.k, len, n);
   const float* src = a.scores + (int64_t)row * a.stride + lo;
-  uint2* out = a.cand + ((int64_t)row * a.max_chunks + c) * a.k;
+  uint32_t kmin = 0xffffffffu;
   for (int i0 = 0; i0 < len; i0 += 8 * kTopkThreads) {      // 8 independent loads in flight
     float v[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = i0 + r * kTopkThreads + threadIdx.x;
-      v[r] = (i < len) ? src[i] : 0.0f;
+    for (int q = 0; q < 8; ++q) {                 // unconditional (clamped) loads stay in flight together
+      const int i = i0 + q * kTopkThreads + threadIdx.x;
+      v[q] = src[min(i, len - 1)];
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = i0 + r * kTopkThreads + threadIdx.x;
-      if (i < len) skeys[i] = float_key(v[r]);
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + q * kTopkThreads + threadIdx.x;
+      if (i < len) {
+        const uint32_t key = float_key(v[q]);
+        skeys[i] = key;
+        kmin = min(kmin, key);
+      }
     }
   }
   __syncthreads();
-  if (len <= a.k) {
-    for (int i = threadIdx.x; i < len; i += kTopkThreads) out[i] = make_uint2(skeys[i], (uint32_t)(lo + i));
-    return;
-  }
   uint32_t T;
-  int need;
-  radix_select([&](int i) { return skeys[i]; }, len, a.k, sh, T, need);
-  ordered_take<8>([&](int i) { return skeys[i]; }, len, T, need, a.k, sh,
-                  [&](int slot, int i, uint32_t key) { out[slot] = make_uint2(key, (uint32_t)(lo + i)); });
+  if (r >= len) {                              // the bound is the chunk's smallest key
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = kmin;
+    __syncthreads();
+    T = 0xffffffffu;
+    for (int w = 0; w < kTopkWaves; ++w) T = min(T, sh.red[w]);
+  } else {
+    int need;
+    radix_select([&](int i) { return skeys[i]; }, len, r, sh, T, need);
+  }
+  if (threadIdx.x == 0) a.xc[(int64_t)row * a.max_chunks + c] = T;
 }
 
-// stage 2: one work-group per row.  Every chunk but the last contributes exactly k
-// candidates, so the row's candidates are contiguous in the workspace in position order.
-constexpr int kMergeLds = 16384;           // candidate keys staged in LDS (64 KB)
-__global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(TopkArgs a) {
-  extern __shared__ uint32_t ckeys[];
+// stage 2: one work-group per row.  The bound M is the largest X_c such that the chunks
+// with X_c' >= X_c guarantee at least k keys >= it; every key of the row's top k is
+// >= M.  The row's keys >= M are compacted in position order into LDS (normally little
+// more than k of them) and the exact select runs there.
+constexpr int kFiltPer = 16;                       // keys per thread per filter round
+constexpr int kFiltLds = 8192;                     // filtered keys kept in LDS
+static_assert(kFiltPer * kTopkWaves == 256, "the filter scan covers 4 counts per lane of one wave");
+constexpr int kSelectLds = kFiltLds * 2;           // 32-bit words of dynamic LDS: keys + positions
+constexpr int kMaxChunks = 64;                     // chunk bounds one wave combines
+__global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
+  extern __shared__ uint32_t fl[];                 // [kFiltLds] keys, then [kFiltLds] positions
   __shared__ TopkShared sh;
+  __shared__ uint32_t m_sh;
+  __shared__ int fcnt[kFiltPer * kTopkWaves];
+  __shared__ int ftot;
   const int row = blockIdx.x;
   const int n = row_len(a, row);
   int32_t* out = a.idx + (int64_t)row * a.k;
@@ -248,41 +274,103 @@ __global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < n) ? i : -1;
     return;
   }
+  const float* src = a.scores + (int64_t)row * a.stride;
   const int nch = (n + a.chunk - 1) / a.chunk;
-  const int last_len = n - (nch - 1) * a.chunk;
-  const int n_cand = (nch - 1) * a.k + min(a.k, last_len);
-  const uint2* cand = a.cand + (int64_t)row * a.max_chunks * a.k;
-  uint32_t T;
-  int need;
-  if (n_cand <= kMergeLds) {
-    for (int j0 = 0; j0 < n_cand; j0 += 8 * kTopkThreads) {
-      uint2 v[8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    // lane j tests X_j as the bound: keys guaranteed >= X_j = sum of r_c over X_c >= X_j
+    uint32_t xj = 0;
+    int64_t guaranteed = 0;
+    if (lane < nch) xj = a.xc[(int64_t)row * a.max_chunks + lane];
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t x = (uint32_t)__shfl((int)xj, c);
+      const int len = min(a.chunk, n - c * a.chunk);
+      if (x >= xj) guaranteed += chunk_rank(a.k, len, n);
+    }
+    uint32_t m = (lane < nch && guaranteed >= a.k) ? xj : 0u;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int j = j0 + r * kTopkThreads + threadIdx.x;
-        v[r] = (j < n_cand) ? cand[j] : make_uint2(0, 0);
-      }
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if (lane == 0) m_sh = m;
+  }
+  __syncthreads();
+  const uint32_t M = m_sh;
+  uint32_t* fkey = fl;
+  uint32_t* fpos = fl + kFiltLds;
+  // ordered compaction of the keys >= M.  Loads are coalesced (i = round base + q*1024 +
+  // thread); order is (q, wave, lane), so a ballot per load plus one scan over the
+  // (q, wave) counts gives every kept key its position-ordered slot.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int n_f = 0;
+  for (int i0 = 0; i0 < n; i0 += kTopkThreads * kFiltPer) {
+    uint32_t key[kFiltPer];
+    uint64_t keep[kFiltPer];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int j = j0 + r * kTopkThreads + threadIdx.x;
-        if (j < n_cand) ckeys[j] = v[r].x;
-      }
+    for (int q = 0; q < kFiltPer; ++q) {          // unconditional (clamped) loads stay in flight together
+      const int i = i0 + q * kTopkThreads + threadIdx.x;
+      key[q] = float_key(src[min(i, n - 1)]);
+    }
+#pragma unroll
+    for (int q = 0; q < kFiltPer; ++q) {
+      const int i = i0 + q * kTopkThreads + threadIdx.x;
+      keep[q] = __builtin_amdgcn_ballot_w64(i < n && key[q] >= M);
+      if (lane == 0) fcnt[q * kTopkWaves + wave] = __builtin_popcountll(keep[q]);
     }
     __syncthreads();
-    radix_select([&](int j) { return ckeys[j]; }, n_cand, a.k, sh, T, need);
-    ordered_take<8>([&](int j) { return ckeys[j]; }, n_cand, T, need, a.k, sh,
-                    [&](int slot, int j, uint32_t) { out[slot] = (int32_t)cand[j].y; });
-  } else {
-    radix_select([&](int j) { return cand[j].x; }, n_cand, a.k, sh, T, need);
-    ordered_take<4>([&](int j) { return cand[j].x; }, n_cand, T, need, a.k, sh,
-                    [&](int slot, int j, uint32_t) { out[slot] = (int32_t)cand[j].y; });
+    if (wave == 0) {                               // exclusive scan of the 256 (q, wave) counts
+      int c4[4], s = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = fcnt[lane * 4 + i];
+        s += c4[i];
+      }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      int run = incl - s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fcnt[lane * 4 + i] = run;
+        run += c4[i];
+      }
+      if (lane == 63) ftot = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kFiltPer; ++q) {
+      if ((keep[q] >> lane) & 1ull) {
+        const int pos = n_f + fcnt[q * kTopkWaves + wave] + __builtin_popcountll(keep[q] & lt_mask);
+        if (pos < kFiltLds) {
+          fkey[pos] = key[q];
+          fpos[pos] = (uint32_t)(i0 + q * kTopkThreads + threadIdx.x);
+        }
+      }
+    }
+    n_f += ftot;
+    __syncthreads();
+  }
+  uint32_t T;
+  int need;
+  if (n_f <= kFiltLds) {
+    if (n_f <= a.k) {                              // only when ties make the bound keep exactly k
+      for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < n_f) ? (int32_t)fpos[i] : -1;
+      return;
+    }
+    radix_select([&](int j) { return fkey[j]; }, n_f, a.k, sh, T, need);
+    ordered_take<4>([&](int j) { return fkey[j]; }, n_f, T, need, a.k, sh,
+                    [&](int slot, int j, uint32_t) { out[slot] = (int32_t)fpos[j]; });
+  } else {                                         // many keys tie at the bound: select over the whole row
+    radix_select([&](int i) { return float_key(src[i]); }, n, a.k, sh, T, need);
+    ordered_take<4>([&](int i) { return float_key(src[i]); }, n, T, need, a.k, sh,
+                    [&](int slot, int i, uint32_t) { out[slot] = i; });
   }
 }
 
-static void topk_geometry(int64_t stride, int k, int& chunk, int& max_chunks) {
-  // about kTargetChunks chunks of the longest row, at least k positions each, at most 128 KB
+static void topk_geometry(int64_t stride, int& chunk, int& max_chunks) {
+  // about kTargetChunks chunks of the longest row, at most 128 KB of keys each
   int64_t c = (stride + kTargetChunks - 1) / kTargetChunks;
-  if (c < k) c = k;
   c = (c + 1023) / 1024 * 1024;
   if (c > kMaxChunkElems) c = kMaxChunkElems;
   chunk = (int)c;
@@ -294,8 +382,8 @@ static void topk_geometry(int64_t stride, int k, int& chunk, int& max_chunks) {
 extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
   if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
   int chunk, max_chunks;
-  dsa::topk_geometry(score_stride, k, chunk, max_chunks);
-  return (size_t)B * Sq * max_chunks * k * sizeof(uint2);
+  dsa::topk_geometry(score_stride, chunk, max_chunks);
+  return (size_t)B * Sq * max_chunks * sizeof(uint32_t);
 }
 
 extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int Sq,
@@ -307,32 +395,33 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   DSA_CHECK_ARG(score_stride >= 1 && score_stride < ((int64_t)1 << 31), "dsa_topk: bad score_stride");
   DSA_CHECK_SUPPORTED(k <= 8192, "dsa_topk: k > 8192");
   DSA_CHECK_ARG((int64_t)B * Sq <= 65535, "dsa_topk: more than 65535 rows");
-  const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
-  if (ws == nullptr || ws_bytes < need) {
-    set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
-    return DSA_ERR_WORKSPACE;
-  }
   TopkArgs a{};
   a.scores = scores;
   a.stride = score_stride;
   a.seq_lens = seq_lens;
   a.Sq = Sq;
   a.k = k;
-  topk_geometry(score_stride, k, a.chunk, a.max_chunks);
-  a.cand = static_cast<uint2*>(ws);
+  topk_geometry(score_stride, a.chunk, a.max_chunks);
+  DSA_CHECK_SUPPORTED(a.max_chunks <= kMaxChunks, "dsa_topk: score_stride above %d", kMaxChunks * kMaxChunkElems);
+  const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
+  if (ws == nullptr || ws_bytes < need) {
+    set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
+    return DSA_ERR_WORKSPACE;
+  }
+  a.xc = static_cast<uint32_t*>(ws);
   a.idx = idx;
   const size_t lds = (size_t)a.chunk * sizeof(uint32_t);
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)topk_bound_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)(kMaxChunkElems * sizeof(uint32_t)));
-    hipFuncSetAttribute((const void*)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)(kMergeLds * sizeof(uint32_t)));
+    hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)(kSelectLds * sizeof(uint32_t)));
     attr = true;
   }
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
-  dsa_status_t st = launch_status("dsa_topk(chunk)");
+  hipLaunchKernelGGL(topk_bound_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
+  dsa_status_t st = launch_status("dsa_topk(bound)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(B * Sq), dim3(kTopkThreads), kMergeLds * sizeof(uint32_t), stream, a);
-  return launch_status("dsa_topk(merge)");
+  hipLaunchKernelGGL(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
+  return launch_status("dsa_topk(select)");
 }
