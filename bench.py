@@ -77,39 +77,17 @@ def main():
         sys.exit(2)
 
     import torch
-    import paged_kv_cache_indexer_amd as dsa
     import synth
-    from tests.dsa_dev import DevWorkload
+    from tests.dsa_dev import DevWorkload, DecodeStep, HipMark
 
     torch.cuda.set_device(0)
     wl = synth.make_workload(2)
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
-    scores = torch.empty((B, Sq, L), dtype=torch.float32, device="cuda")
-    idx = torch.empty((B, Sq, k), dtype=torch.int32, device="cuda")
-    o = torch.empty((B, Sq, H_mla, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Sq, H_mla), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H_mla, k)), dtype=torch.uint8, device="cuda")
-    ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, k, L)), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
+    step = DecodeStep(dw)
     names = ["indexer", "topk", "mla"]
-    ev = None
-
-    def step(record):
-        if record:
-            record[0].record(stream)
-        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, dw.k_scale, dw.seq_lens, scores, k_dtype=dw.k_dtype,
-                               err=dw.err, q_dtype=dw.q_dtype, stream=stream)
-        if record:
-            record[1].record(stream)
-        dsa.dsa_topk(scores, dw.seq_lens, idx, ws=ws_topk, stream=stream)
-        if record:
-            record[2].record(stream)
-        dsa.dsa_sparse_mla_decode(dw.mla_q, idx, dw.rows, wl.scale, o, lse, ws=ws, err=dw.err, stream=stream)
-        if record:
-            record[3].record(stream)
+    stream = torch.cuda.Stream()            # non-default stream: the step is captured and replayed
 
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
@@ -117,19 +95,45 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step(None)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step.run(stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    # The K timed steps are one HIP graph (launch overhead of the five kernels removed, as
+    # a serving loop would run them); one untimed replay uploads the graph first.  HIP
+    # timing events cannot be read back from inside a replayed graph, so the per-kernel
+    # durations come from HIP events recorded on the launch stream around eager launches of
+    # the same K steps, right after the timed region.
+    mode = "hip_graph"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                step.run(stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        run_timed = graph.replay
+    except Exception as e:                  # capture unsupported: time eager launches
+        print(f"bench.py: graph capture failed ({e}); timing eager launches", file=sys.stderr)
+        mode = "eager"
+        torch.cuda.synchronize()
+
+        def run_timed():
+            for i in range(args.steps):
+                step.run(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    run_timed()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    evs = [[HipMark() for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step.run(stream, evs[i])
+    torch.cuda.synchronize()
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
 
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e-3
+    per = {n: float(np.mean([evs[i][j].elapsed_ms(evs[i][j + 1]) for i in range(args.steps)])) * 1e-3
            for j, n in enumerate(names)}                        # seconds per launch
     work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size)
     kernels = {}
@@ -158,6 +162,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)",
+        "launch": mode,
+        "kernel_timing": "HIP events on the launch stream around eager launches of the same K steps",
         "config": {"workload": "decode_b32_ctx65536_top2048", "batch": B, "context": L, "query_tokens": Sq,
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
                    "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "keys": "e4m3 + fp32 scale"},

@@ -32,6 +32,14 @@ dsa_status_t launch_status(const char* what);
     }                                           \
   } while (0)
 
+// Kernel launch that first clears any error an earlier, unrelated HIP call left behind,
+// so that launch_status() afterwards reports this launch only.
+#define DSA_LAUNCH(...)                         \
+  do {                                          \
+    (void)hipGetLastError();                    \
+    hipLaunchKernelGGL(__VA_ARGS__);            \
+  } while (0)
+
 #define DSA_CHECK_SUPPORTED(cond, ...)          \
   do {                                          \
     if (!(cond)) {                              \

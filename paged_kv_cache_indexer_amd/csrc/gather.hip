@@ -132,8 +132,8 @@ extern "C" dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit
   int64_t blocks = (items + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (mode == DSA_GATHER_SERVE)
-    hipLaunchKernelGGL(serve_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+    DSA_LAUNCH(serve_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   else
-    hipLaunchKernelGGL(install_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+    DSA_LAUNCH(install_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   return launch_status("dsa_gather_kv");
 }

@@ -345,7 +345,7 @@ static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
       per_cu = 1;
     grid = cus * per_cu;
   }
-  hipLaunchKernelGGL((indexer_mfma_kernel<QFP8, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
+  DSA_LAUNCH((indexer_mfma_kernel<QFP8, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
   return launch_status("dsa_indexer_scores");
 }
 
@@ -378,7 +378,7 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
     DSA_CHECK_ARG(keys->row_bytes == D * 4, "dsa_indexer_scores: row_bytes != D*4");
     DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
     const int64_t gx = (score_stride + 255) / 256;
-    hipLaunchKernelGGL(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
+    DSA_LAUNCH(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
                        static_cast<const float*>(q), w, ks, k_scale, seq_lens, Sq, H, D, score_stride, scores,
                        err_count);
     return launch_status("dsa_indexer_scores");

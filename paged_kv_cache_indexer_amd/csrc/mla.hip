@@ -497,13 +497,13 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   }
   const int QR = B * Sq;
   if (H > 32) {
-    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(splits * QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
+    DSA_LAUNCH(mla_decode_kernel<2>, dim3(splits * QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(splits * QR), dim3(128), 0, stream, a);
+    DSA_LAUNCH(mla_decode_kernel<1>, dim3(splits * QR), dim3(128), 0, stream, a);
   }
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
+  DSA_LAUNCH(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
                      stream, a);
   return launch_status("dsa_sparse_mla_decode(merge)");
 }

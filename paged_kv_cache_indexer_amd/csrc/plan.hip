@@ -331,6 +331,6 @@ extern "C" dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int3
   }
   PlanArgs args{topk, Sq, k, pool_ids, id_to_slot, ptr, n_sets, ways, id_range, is_hit, slot,
                 miss_pos, miss_slot, miss_count, commit, err_count};
-  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)B), dim3(kPlanThreads), plan_smem(), stream, args);
+  DSA_LAUNCH(plan_kernel, dim3((unsigned)B), dim3(kPlanThreads), plan_smem(), stream, args);
   return launch_status("dsa_plan");
 }

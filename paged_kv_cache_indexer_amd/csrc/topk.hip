@@ -419,9 +419,9 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
                         (int)(kSelectLds * sizeof(uint32_t)));
     attr = true;
   }
-  hipLaunchKernelGGL(topk_bound_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
+  DSA_LAUNCH(topk_bound_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
   dsa_status_t st = launch_status("dsa_topk(bound)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
+  DSA_LAUNCH(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
   return launch_status("dsa_topk(select)");
 }

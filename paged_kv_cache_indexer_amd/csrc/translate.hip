@@ -33,7 +33,7 @@ extern "C" dsa_status_t dsa_page_translate(const int64_t* x, int64_t n, int page
   DSA_CHECK_ARG(x && rank && local_row, "dsa_page_translate: null pointer");
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(dsa::page_translate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
+  DSA_LAUNCH(dsa::page_translate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
                      (int64_t)page_size, (int64_t)n_ranks, rank, local_row, err_count);
   return dsa::launch_status("dsa_page_translate");
 }

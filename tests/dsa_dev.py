@@ -82,6 +82,37 @@ class DevWorkload:
         return o, lse
 
 
+class HipMark:
+    """A HIP timing event recorded on a stream; `external=True` records it as an external
+    event node when the stream is being captured into a graph, so its time stays readable
+    after each replay."""
+
+    _hip = None
+
+    def __init__(self, external: bool = False):
+        import ctypes
+        if HipMark._hip is None:
+            HipMark._hip = ctypes.CDLL("libamdhip64.so")
+            HipMark._hip.hipEventRecordWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+            HipMark._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                         ctypes.c_void_p]
+        self.ev = ctypes.c_void_p()
+        rc = HipMark._hip.hipEventCreate(ctypes.byref(self.ev))
+        assert rc == 0, f"hipEventCreate failed ({rc})"
+        self.flags = 1 if external else 0          # hipEventRecordExternal
+
+    def record(self, stream):
+        rc = HipMark._hip.hipEventRecordWithFlags(self.ev, stream.cuda_stream, self.flags)
+        assert rc == 0, f"hipEventRecordWithFlags failed ({rc})"
+
+    def elapsed_ms(self, end: "HipMark") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = HipMark._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return ms.value
+
+
 def host_device_ptr(t: torch.Tensor) -> int:
     """Device alias of a pinned host tensor (hipHostGetDevicePointer)."""
     import ctypes
@@ -94,3 +125,42 @@ def host_device_ptr(t: torch.Tensor) -> int:
 
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
+
+
+class DecodeStep:
+    """One decode step (indexer -> top-k -> sparse MLA) over fixed device buffers.
+
+    All buffers are allocated once, so the step can be captured into a HIP graph and
+    replayed.  `run(stream, marks)` enqueues the three entry points on `stream`; if
+    `marks` (four objects with a `record(stream)` method, e.g. HipMark) is given, they are
+    recorded before, between and after the stages.
+    """
+
+    def __init__(self, dw: DevWorkload):
+        wl = dw.wl
+        self.dw = dw
+        B, Sq, L, k = dw.B, dw.Sq, dw.Lmax, wl.topk
+        H = wl.mla_q.shape[2]
+        self.scores = torch.empty((B, Sq, L), dtype=torch.float32, device=DEV)
+        self.idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
+        self.o = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=DEV)
+        self.lse = torch.empty((B, Sq, H), dtype=torch.float32, device=DEV)
+        self.ws_mla = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H, k)), dtype=torch.uint8,
+                                  device=DEV)
+        self.ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, k, L)), dtype=torch.uint8, device=DEV)
+
+    def run(self, stream, marks=None):
+        dw = self.dw
+        if marks:
+            marks[0].record(stream)
+        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, dw.k_scale, dw.seq_lens, self.scores,
+                               k_dtype=dw.k_dtype, err=dw.err, q_dtype=dw.q_dtype, stream=stream)
+        if marks:
+            marks[1].record(stream)
+        dsa.dsa_topk(self.scores, dw.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
+        if marks:
+            marks[2].record(stream)
+        dsa.dsa_sparse_mla_decode(dw.mla_q, self.idx, dw.rows, dw.wl.scale, self.o, self.lse, ws=self.ws_mla,
+                                  err=dw.err, stream=stream)
+        if marks:
+            marks[3].record(stream)

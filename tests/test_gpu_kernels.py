@@ -16,7 +16,7 @@ import paged_kv_cache_indexer_amd as dsa
 import synth
 from oracle import indexer as o_idx, mla as o_mla, paging as o_pg, plan as o_plan, topk as o_topk
 from oracle.step import decode_request, selected_rows
-from tests.dsa_dev import DevWorkload, bf16_to_f64, host_device_ptr, t_i32, t_u16_as_bf16, DEV
+from tests.dsa_dev import DecodeStep, DevWorkload, bf16_to_f64, host_device_ptr, t_i32, t_u16_as_bf16, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -317,3 +317,36 @@ def test_gather_serve_and_install_bit_exact():
             assert np.array_equal(pool_np[b, live], full[b, pid_np[b, live]])
     # the second step had hits: they were served from the pool
     assert int(is_hit.sum()) > 0
+
+
+@pytest.mark.gpu
+def test_decode_step_graph_replay_matches_eager():
+    """The whole step captured in a HIP graph gives the eager result on every replay.
+
+    Outputs are overwritten with garbage between replays, and eager work and
+    synchronisations run between them; every kernel is deterministic, so the comparison is
+    bit-exact.
+    """
+    wl = synth.make_workload(synth.spec(2).scaled(B=4, L=20000))
+    dw = DevWorkload(wl)
+    step = DecodeStep(dw)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step.run(stream)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.scores, step.idx, step.o, step.lse)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step.run(stream)
+    for rep in range(4):
+        for t in (step.scores, step.idx, step.o, step.lse):
+            t.view(torch.uint8).fill_(0x7F + rep)
+        other = DecodeStep(dw)                      # eager work between the replays
+        with torch.cuda.stream(stream):
+            other.run(stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((step.scores, step.idx, step.o, step.lse), ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}"
+    assert int(dw.err) == 0
