@@ -62,6 +62,64 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"{dt:.1f} s single-threaded, scaled to the full batch"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.json")
+# entry point -> (kernel name prefixes in rocprofv3 output, sources the kernels are built from)
+ENTRY_KERNELS = {
+    "indexer": (["void dsa::indexer_mfma_kernel<false, 2, 1, 1>"], ["indexer.hip"]),
+    "topk": (["dsa::topk_bound_kernel", "dsa::topk_select_kernel"], ["topk.hip"]),
+    "mla": (["void dsa::mla_decode_kernel<2>", "dsa::mla_merge_kernel"], ["mla.hip"]),
+}
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0   # counter KiB -> bytes/1024, from a 256 MiB device copy
+
+
+def source_digest(entry):
+    """sha256 over the files the entry point's kernels are compiled from (and the build flags)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_indexer_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in ENTRY_KERNELS[entry][1]]
+    files += [os.path.join(csrc, "common.h"), os.path.join(ROOT, "paged_kv_cache_indexer_amd", "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def record_traffic(fetch_csv, write_csv):
+    """Average FETCH_SIZE / WRITE_SIZE per launch of each entry point (sum over its kernels),
+    from two rocprofv3 --pmc passes, written with the sources' digest."""
+    import csv
+    out = {"factors": {"FETCH_SIZE": FETCH_FACTOR, "WRITE_SIZE": WRITE_FACTOR}, "entries": {}}
+    vals = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                for entry, (prefixes, _) in ENTRY_KERNELS.items():
+                    for pfx in prefixes:
+                        if r["Kernel_Name"].startswith(pfx):
+                            vals.setdefault((entry, pfx, counter), []).append(float(r["Counter_Value"]))
+    for entry, (prefixes, _) in ENTRY_KERNELS.items():
+        kib = {c: sum(float(np.mean(vals[(entry, p, c)])) for p in prefixes) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        out["entries"][entry] = {"fetch_kib": kib["FETCH_SIZE"], "write_kib": kib["WRITE_SIZE"],
+                                 "bytes": (kib["FETCH_SIZE"] * FETCH_FACTOR + kib["WRITE_SIZE"] * WRITE_FACTOR) * 1024,
+                                 "sha256": source_digest(entry)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic(entry):
+    """HBM bytes per launch from the recorded counters, or None if the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)["entries"][entry]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes"] if rec["sha256"] == source_digest(entry) else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,7 +128,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from two rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is described in DESIGN.md and not built", file=sys.stderr)
@@ -145,7 +208,7 @@ def main():
     dom = max(names, key=lambda n: per[n])
     by = work[dom][0]
     roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+                "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     ms = wall / args.steps * 1e3
