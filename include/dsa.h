@@ -129,10 +129,11 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float*
  *
  *   scores   [B, Sq, score_stride] float32 (positions < vis(b,t) are read; no NaNs)
  *   idx      [B, Sq, k] int32 output
- *   ws       workspace of at least dsa_topk_workspace_size(B, Sq, k, score_stride) bytes:
- *            one bound key per row chunk of a two-stage select (each chunk's key of rank
- *            ceil(k * chunk_len / row_len) gives a lower bound of the row's k-th key;
- *            the exact select then runs over the keys at or above that bound)
+ *   ws       workspace of at least dsa_topk_workspace_size(B, Sq, k, score_stride) bytes,
+ *            8-byte aligned: per row chunk, its best keys as candidates and its cut key,
+ *            for a two-stage select (chunk c keeps twice its share ceil(k*len_c/n) of
+ *            the k; the exact select over the candidates is checked against the cut
+ *            keys and redone over the row's scores when a chunk could hold more)
  * Supported: 1 <= k <= 8192, B*Sq <= 65535, score_stride <= 2^21.
  */
 size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride);

@@ -5,19 +5,19 @@
 // order-preserving uint32 keys.
 //
 // Stage 1 (many work-groups per row): the row's n positions are cut into chunks of C
-// positions; chunk c (len_c positions) finds its r_c-th largest key X_c, with
-// r_c = ceil(k * len_c / n), so the r_c add up to at least k.
-// Stage 2 (one work-group per row): M = the largest X_c such that the chunks whose X is
-// >= X_c hold at least k keys >= X_c between them, which makes M a lower bound of the
-// row's k-th largest key.  The keys >= M (about k of them on smooth data) are compacted
-// in position order into LDS; the exact select runs over them and an ordered compaction
-// writes the k positions ascending.  If ties at the bound leave more keys than LDS
-// holds, the select runs over the whole row instead.
+// positions; chunk c (len_c positions) keeps its r_c = min(len_c, 2 ceil(k len_c / n)) best
+// keys as candidates, in position order, and records its r_c-th largest key X_c.
+// Stage 2 (one work-group per row): the exact select over the ~2k candidates gives the
+// row's k-th key T; it is the row's answer whenever every chunk that left keys out has
+// X_c < T.  Otherwise the row is selected again from its scores, filtered by a lower bound
+// of the k-th key derived from the X_c (see topk_select_kernel).
 //
 // Both stages use the same select: an MSB-first radix search for the r-th largest key T
 // (digits of up to 11 bits, starting below the bits that the smallest and the largest
 // key share) and `need`, the number of keys equal to T that are taken (lowest positions
 // first).
+#include <algorithm>
+
 #include "common.h"
 
 namespace dsa {
@@ -189,7 +189,9 @@ struct TopkArgs {
   int Sq, k;
   int chunk;          // C: positions per stage-1 chunk
   int max_chunks;     // chunk slots per row in the workspace
-  uint32_t* xc;       // [rows, max_chunks] bound key of each chunk
+  int cap;            // candidate slots per chunk: min(C, 2k)
+  uint32_t* xc;       // [rows, max_chunks] cut key of each chunk
+  uint2* cand;        // [rows, max_chunks, cap] (key, position) candidates
   int32_t* idx;
 };
 
@@ -199,15 +201,17 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
   return n < 0 ? 0 : n;
 }
 
-// rank of the bound key of a chunk of `len` of the row's `n` positions: the chunks' ranks
-// add up to at least k, and each is at most len (k < n)
-__device__ __forceinline__ int chunk_rank(int k, int len, int n) {
-  return (int)(((int64_t)k * len + n - 1) / n);
+// candidates kept by a chunk of `len` of the row's `n` positions: twice its share
+// ceil(k * len / n) of the k, at most len.  The shares add up to at least k.
+__device__ __forceinline__ int chunk_keep(int k, int len, int n) {
+  const int share = (int)(((int64_t)k * len + n - 1) / n);
+  return min(len, 2 * share);
 }
 
-// stage 1, grid (max_chunks, rows): X_c = the r_c-th largest key of chunk c, so chunk c
-// holds at least r_c keys >= X_c.
-__global__ void __launch_bounds__(kTopkThreads) topk_bound_kernel(TopkArgs a) {
+// stage 1, grid (max_chunks, rows): chunk c keeps its r_c best keys (r_c = chunk_keep) as
+// (key, position) candidates in position order; X_c = its r_c-th largest key, so every key
+// it left out is < X_c, or == X_c at a later position.
+__global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
   extern __shared__ uint32_t skeys[];
   __shared__ TopkShared sh;
   const int row = blockIdx.y, c = blockIdx.x;
@@ -216,8 +220,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_bound_kernel(TopkArgs a) {
   const int lo = c * a.chunk;
   if (lo >= n) return;
   const int len = min(a.chunk, n - lo);
-  const int r = chunk_rank(a.k, len, n);
+  const int r = chunk_keep(a.k, len, n);
   const float* src = a.scores + (int64_t)row * a.stride + lo;
+  uint2* out = a.cand + ((int64_t)row * a.max_chunks + c) * a.cap;
   uint32_t kmin = 0xffffffffu;
   for (int i0 = 0; i0 < len; i0 += 8 * kTopkThreads) {      // 8 independent loads in flight
     float v[8];
@@ -238,33 +243,43 @@ __global__ void __launch_bounds__(kTopkThreads) topk_bound_kernel(TopkArgs a) {
   }
   __syncthreads();
   uint32_t T;
-  if (r >= len) {                              // the bound is the chunk's smallest key
+  if (r >= len) {                              // the whole chunk is kept; X_c = its smallest key
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
     if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = kmin;
     __syncthreads();
     T = 0xffffffffu;
     for (int w = 0; w < kTopkWaves; ++w) T = min(T, sh.red[w]);
+    for (int i = threadIdx.x; i < len; i += kTopkThreads) out[i] = make_uint2(skeys[i], (uint32_t)(lo + i));
   } else {
     int need;
     radix_select([&](int i) { return skeys[i]; }, len, r, sh, T, need);
+    ordered_take<8>([&](int i) { return skeys[i]; }, len, T, need, r, sh,
+                    [&](int slot, int i, uint32_t key) { out[slot] = make_uint2(key, (uint32_t)(lo + i)); });
   }
   if (threadIdx.x == 0) a.xc[(int64_t)row * a.max_chunks + c] = T;
 }
 
-// stage 2: one work-group per row.  The bound M is the largest X_c such that the chunks
-// with X_c' >= X_c guarantee at least k keys >= it; every key of the row's top k is
-// >= M.  The row's keys >= M are compacted in position order into LDS (normally little
-// more than k of them) and the exact select runs there.
+// stage 2: one work-group per row.  The chunks' candidates (about 2k, concatenated in
+// chunk order, so in position order) are staged in LDS and the exact select runs there,
+// giving the k-th key T.  The answer is exact if every chunk that left keys out has
+// X_c < T: all keys it left out are then below T.  Otherwise (ties at a chunk's cut, or
+// more than twice a chunk's share in the answer) the row is selected again from its
+// scores: the bound M is the largest X_c such that the chunks whose X is >= X_c hold at
+// least k keys >= it, which makes M a lower bound of the row's k-th key; the row's keys
+// >= M are compacted in position order into LDS and selected exactly; if ties at the
+// bound leave more keys than LDS holds, the select runs over the whole row.
 constexpr int kFiltPer = 16;                       // keys per thread per filter round
-constexpr int kFiltLds = 8192;                     // filtered keys kept in LDS
+constexpr int kFiltLds = 8192;                     // candidates / filtered keys kept in LDS
 static_assert(kFiltPer * kTopkWaves == 256, "the filter scan covers 4 counts per lane of one wave");
 constexpr int kSelectLds = kFiltLds * 2;           // 32-bit words of dynamic LDS: keys + positions
-constexpr int kMaxChunks = 64;                     // chunk bounds one wave combines
+constexpr int kMaxChunks = 64;                     // chunks one wave combines
 __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   extern __shared__ uint32_t fl[];                 // [kFiltLds] keys, then [kFiltLds] positions
   __shared__ TopkShared sh;
   __shared__ uint32_t m_sh;
+  __shared__ int ok_sh;
+  __shared__ int coff[kMaxChunks + 1];
   __shared__ int fcnt[kFiltPer * kTopkWaves];
   __shared__ int ftot;
   const int row = blockIdx.x;
@@ -277,15 +292,75 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   const float* src = a.scores + (int64_t)row * a.stride;
   const int nch = (n + a.chunk - 1) / a.chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* fkey = fl;
+  uint32_t* fpos = fl + kFiltLds;
+  uint32_t xj = 0;                                 // wave 0, lane j < nch: X_j
+  int rj = 0, lenj = 0;
+  if (wave == 0) {
+    if (lane < nch) {
+      xj = a.xc[(int64_t)row * a.max_chunks + lane];
+      lenj = min(a.chunk, n - lane * a.chunk);
+      rj = chunk_keep(a.k, lenj, n);
+    }
+    int incl = rj;                                 // candidate offsets of the chunks
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane < nch) coff[lane] = incl - rj;
+    if (lane == nch - 1) coff[nch] = incl;
+  }
+  __syncthreads();
+  const int n_cand = coff[nch];
+  uint32_t T;
+  int need;
+  if (n_cand <= kFiltLds) {
+    // stage the candidates: slot j belongs to the last chunk whose offset is <= j
+    for (int j0 = 0; j0 < n_cand; j0 += 4 * kTopkThreads) {
+      uint2 v[4];
+      int jj[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = min(j0 + q * kTopkThreads + (int)threadIdx.x, n_cand - 1);
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (coff[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        jj[q] = j;
+        v[q] = a.cand[((int64_t)row * a.max_chunks + lo) * a.cap + (j - coff[lo])];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j0 + q * kTopkThreads + (int)threadIdx.x < n_cand) {
+          fkey[jj[q]] = v[q].x;
+          fpos[jj[q]] = v[q].y;
+        }
+      }
+    }
+    __syncthreads();
+    radix_select([&](int j) { return fkey[j]; }, n_cand, a.k, sh, T, need);
+    if (wave == 0) {
+      const bool bad = lane < nch && rj < lenj && !(xj < T);
+      const uint64_t any_bad = __builtin_amdgcn_ballot_w64(bad);
+      if (lane == 0) ok_sh = (any_bad == 0);
+    }
+    __syncthreads();
+    if (ok_sh) {
+      ordered_take<4>([&](int j) { return fkey[j]; }, n_cand, T, need, a.k, sh,
+                      [&](int slot, int j, uint32_t) { out[slot] = (int32_t)fpos[j]; });
+      return;
+    }
+  }
+  // ---- select again from the row's scores
   if (wave == 0) {
     // lane j tests X_j as the bound: keys guaranteed >= X_j = sum of r_c over X_c >= X_j
-    uint32_t xj = 0;
     int64_t guaranteed = 0;
-    if (lane < nch) xj = a.xc[(int64_t)row * a.max_chunks + lane];
     for (int c = 0; c < nch; ++c) {
       const uint32_t x = (uint32_t)__shfl((int)xj, c);
-      const int len = min(a.chunk, n - c * a.chunk);
-      if (x >= xj) guaranteed += chunk_rank(a.k, len, n);
+      const int r = __shfl(rj, c);
+      if (x >= xj) guaranteed += r;
     }
     uint32_t m = (lane < nch && guaranteed >= a.k) ? xj : 0u;
 #pragma unroll
@@ -294,8 +369,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   }
   __syncthreads();
   const uint32_t M = m_sh;
-  uint32_t* fkey = fl;
-  uint32_t* fpos = fl + kFiltLds;
   // ordered compaction of the keys >= M.  Loads are coalesced (i = round base + q*1024 +
   // thread); order is (q, wave, lane), so a ballot per load plus one scan over the
   // (q, wave) counts gives every kept key its position-ordered slot.
@@ -351,8 +424,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
     n_f += ftot;
     __syncthreads();
   }
-  uint32_t T;
-  int need;
   if (n_f <= kFiltLds) {
     if (n_f <= a.k) {                              // only when ties make the bound keep exactly k
       for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < n_f) ? (int32_t)fpos[i] : -1;
@@ -368,22 +439,23 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   }
 }
 
-static void topk_geometry(int64_t stride, int& chunk, int& max_chunks) {
+static void topk_geometry(int64_t stride, int k, int& chunk, int& max_chunks, int& cap) {
   // about kTargetChunks chunks of the longest row, at most 128 KB of keys each
   int64_t c = (stride + kTargetChunks - 1) / kTargetChunks;
   c = (c + 1023) / 1024 * 1024;
   if (c > kMaxChunkElems) c = kMaxChunkElems;
   chunk = (int)c;
   max_chunks = (int)((stride + c - 1) / c);
+  cap = (int)std::min<int64_t>(c, 2 * (int64_t)k);
 }
 
 }  // namespace dsa
 
 extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
   if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
-  int chunk, max_chunks;
-  dsa::topk_geometry(score_stride, chunk, max_chunks);
-  return (size_t)B * Sq * max_chunks * sizeof(uint32_t);
+  int chunk, max_chunks, cap;
+  dsa::topk_geometry(score_stride, k, chunk, max_chunks, cap);
+  return (size_t)B * Sq * max_chunks * ((size_t)cap * sizeof(uint2) + sizeof(uint32_t));
 }
 
 extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int Sq,
@@ -401,26 +473,29 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   a.seq_lens = seq_lens;
   a.Sq = Sq;
   a.k = k;
-  topk_geometry(score_stride, a.chunk, a.max_chunks);
+  topk_geometry(score_stride, k, a.chunk, a.max_chunks, a.cap);
   DSA_CHECK_SUPPORTED(a.max_chunks <= kMaxChunks, "dsa_topk: score_stride above %d", kMaxChunks * kMaxChunkElems);
   const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
   if (ws == nullptr || ws_bytes < need) {
     set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
     return DSA_ERR_WORKSPACE;
   }
-  a.xc = static_cast<uint32_t*>(ws);
+  DSA_CHECK_ARG(((uintptr_t)ws & 7) == 0, "dsa_topk: workspace not 8-byte aligned");
+  const size_t rows = (size_t)B * Sq;
+  a.cand = static_cast<uint2*>(ws);
+  a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.max_chunks * a.cap);
   a.idx = idx;
   const size_t lds = (size_t)a.chunk * sizeof(uint32_t);
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)topk_bound_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)(kMaxChunkElems * sizeof(uint32_t)));
     hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)(kSelectLds * sizeof(uint32_t)));
     attr = true;
   }
-  DSA_LAUNCH(topk_bound_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
-  dsa_status_t st = launch_status("dsa_topk(bound)");
+  DSA_LAUNCH(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
+  dsa_status_t st = launch_status("dsa_topk(chunk)");
   if (st != DSA_OK) return st;
   DSA_LAUNCH(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
   return launch_status("dsa_topk(select)");
