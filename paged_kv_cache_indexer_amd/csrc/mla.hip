@@ -4,26 +4,27 @@
 // attention reads only the top-k positions).  Split-KV decode with fp32 partial
 // (o, lse) and an LSE-rescaling merge (TokenSpeed audit, two-stage split-KV decode).
 //
-// Work-group = 2*HG waves (one per SIMD) for 32*HG heads of one query row and one split
-// of its selected rows.  Wave (hg, half) owns heads [32hg, 32hg+32) and computes
-//   S^T[32 tokens x 32 heads] partial = K_tile[:, half] . q^T[half]   (bf16 MFMA 32x32x16,
-//     18 steps over its 288 of the 576 latent dims, q^T resident in VGPRs); the two
-//     halves of a head group swap partial S^T through LDS and both hold the full sum;
-//   O^T[256 dims x 32 heads] += V^T[half] . P^T                        (bf16 MFMA 32x32x16)
-//     over its 256 of the 512 value dims.  Heads sit on the N axis, so each lane owns one
-//     head's running max / sum and the rescale is a per-lane scalar; P^T is the S^T
-//     accumulator itself (rounded to bf16).  The V^T operand is read straight from the
-//     token-major K tile with LDS transpose reads (ds_read_b64_tr_b16: within each 16-lane
-//     group, lane i receives element i%4 of the 8-byte rows addressed by lanes i/4, 4+i/4,
-//     8+i/4, 12+i/4), so no transposed copy is made.
+// Work-group = NW waves (one per SIMD) for 16*NW heads of one query row and one split of
+// its selected rows.  Each wave owns 16 heads over the whole latent row:
+//   S^T[32 tokens x 16 heads] = K_tile . q^T       (bf16 MFMA 16x16x32: two 16-token
+//     M tiles x 18 steps of 32 latent dims, q^T resident in VGPRs)
+//   O^T[512 dims x 16 heads] += V^T . P^T           (bf16 MFMA 16x16x32: 32 M tiles of 16
+//     value dims, K = the tile's 32 tokens)
+// No partial sums cross waves, so a tile needs one barrier (the ring's).  Heads sit on the
+// N axis: the four lanes of a head (lane % 16) hold its running max / sums, and P^T is the
+// S^T accumulator itself rounded to bf16; lane group g = lane / 16 holds tokens 4g..4g+3
+// and 16+4g..16+4g+3, which are also its eight K slots of the PV product.  The V^T operand
+// is read straight from the token-major K tile with LDS transpose reads
+// (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of the
+// 8-byte rows addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so no transposed copy is made.
 // Selected rows stream into a ring of three LDS tiles with LDS-direct loads
 // (global_load_lds_dwordx4: lane i of a wave instruction lands at M0 + 16 i), two tiles
 // ahead of the one being computed; no VGPRs hold rows in flight.  A tile is stored as
 // 1 KB blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one
 // wave instruction fetches eight whole 128-byte lines and each lane streams one row.
 // Inside a block, 16-byte chunk c of token m sits at position m*8 + ((c%8) ^ swz(m)),
-// which keeps both the K reads (one chunk of 32 tokens) and the transpose reads (two
-// chunks of 4 tokens) free of LDS bank conflicts.
+// which keeps both the K reads (one chunk of 8 consecutive tokens per 128 bytes) and the
+// transpose reads (two chunks of 4 tokens) free of LDS bank conflicts.
 // Online softmax in base 2 with a lazy rescale (the running max is only moved when it
 // grows by more than 2^8), which leaves o and lse mathematically unchanged.
 #include "common.h"
@@ -58,8 +59,9 @@ struct MlaArgs {
   int32_t* err;
 };
 
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // chunk swizzle of token m (mod 8) inside a 1 KB block
@@ -117,28 +119,29 @@ __device__ __forceinline__ void mla_block_unit(int nhb, int& unit, int& hb) {
   }
 }
 
-template <int HG>
-__global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
-  constexpr int NW = 2 * HG;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int CPT = kTileSlots / NT;      // LDS-direct loads per thread per tile
   static_assert(kTileSlots % NT == 0, "tile must split evenly over the threads");
+  constexpr int NSRC = (4 + NW - 1) / NW;   // token groups one lane streams per tile
+  static_assert(NSRC * NW == 4, "NW must divide the 4 token groups of a tile");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kTileBytes];
-  __shared__ f32x4 xch[NW][4][64];          // partial S^T exchange between the halves
   __shared__ int64_t rowoff[kMaxSplit];     // byte offset of each selected row of the split, -1 = none
   __shared__ uint32_t tmask[kMaxSplit / kTT];  // valid-row bits per tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave >> 1, half = wave & 1;
-  const int n = lane & 31, g = lane >> 5;
-  const int nhb = (a.H + 32 * HG - 1) / (32 * HG);
+  const int n = lane & 15, g = lane >> 4;
+  const int nhb = (a.H + 16 * NW - 1) / (16 * NW);
   int unit, hb;
   mla_block_unit(nhb, unit, hb);
   const int qr = unit / a.splits;
   const int split = unit - qr * a.splits;
   const int b = qr / a.Sq;
-  const int head = hb * 32 * HG + hg * 32 + n;
+  const int head = hb * 16 * NW + wave * 16 + n;
   const bool head_ok = head < a.H;
 
   const int e_begin = split * a.per_split;
@@ -149,13 +152,13 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   // values; their probabilities are exactly zero)
   const char* stand_in = reinterpret_cast<const char*>(a.q + (int64_t)qr * a.H * kRowEl);
 
-  // ---- q^T operand: 18 k-steps of 16 over this wave's 288 latent dims
+  // ---- q^T operand: 18 k-steps of 32 latent dims; lane (n, g) holds dims 32j + 8g .. +8
   bf16x8 qb[18];
   {
-    const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + half * 288 + g * 8;
+    const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + g * 8;
 #pragma unroll
     for (int j = 0; j < 18; ++j) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + j * 16);
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + j * 32);
       if (!head_ok) v = bf16x8{};
       qb[j] = v;
     }
@@ -179,20 +182,20 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   }
 
   // ---- per-lane constants of the three access patterns
-  constexpr int NSRC = 4 / NW;  // token groups one lane streams per tile
   // LDS-direct load r of this lane: token group (wave + NW * (r % NSRC)), chunk group
   // r / NSRC; the lane fetches chunk ((lane & 7) ^ swz) of token 8 * group + lane / 8
   const int dlane = ((lane & 7) ^ chunk_swz(lane >> 3)) * 16;
-  int qoff[4];                  // K operand of k-step j: qoff[j % 4] + 4096 (j / 4)
+  int koff[2][2];               // K operand of M tile mt, k-step j: koff[j % 2][mt] + 4096 (j / 2)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) qoff[j] = chunk_byte(n, half * 36 + 2 * j + g);
-  int voff[2];                  // V^T operand (transpose read) of m-tile mt: voff[mt % 2] + 4096 (mt / 2)
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) koff[j][mt] = chunk_byte(n + 16 * mt, 4 * j + g);
+  int voff[4];                  // V^T operand (transpose read) of value tile vt: voff[vt % 4] + 4096 (vt / 4)
   {
-    const int blk = lane >> 4, s16 = lane & 15, jj = s16 >> 2, qq = s16 & 3;
-    const int tok = (blk >> 1) * 4 + jj;
+    const int jj = n >> 2, qq = n & 3;          // source lane n = 4 jj + qq of this 16-lane group
+    const int tok = 4 * g + jj;
 #pragma unroll
-    for (int mp = 0; mp < 2; ++mp)
-      voff[mp] = chunk_byte(tok, half * 32 + mp * 4 + (blk & 1) * 2 + (qq >> 1)) + (qq & 1) * 8;
+    for (int vm = 0; vm < 4; ++vm) voff[vm] = chunk_byte(tok, 2 * vm + (qq >> 1)) + (qq & 1) * 8;
   }
   wait_vmcnt<0>();              // q^T is resident before any row load is in flight
   __syncthreads();              // rowoff / tmask ready
@@ -219,9 +222,9 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
   }
   if (ntiles > 2) prepare(2);
 
-  f32x16 oacc[8];
+  f32x4 oacc[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < 32; ++i) oacc[i] = f32x4{};
   float m_used = -INFINITY;     // log2-domain running max used for p
   float l_part = 0.0f;          // this lane's share of sum p (fp32 p: for lse)
   float lr_part = 0.0f;         // this lane's share of sum bf16(p) (the PV weights: for o)
@@ -231,67 +234,63 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
       wait_vmcnt<CPT>();        // this wave's loads of tile t are done (tile t+1 may be in flight)
     else
       wait_vmcnt<0>();
-    __syncthreads();            // tile t complete for all waves; slot (t+2)%3 and xch free
+    __syncthreads();            // tile t complete for all waves; slot (t+2)%3 free
     if (t + 2 < ntiles) {
       issue(t + 2);
       if (t + 3 < ntiles) prepare(t + 3);
     }
     const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((t % kRing) * kTileBytes));
 
-    // ---- partial S^T over this wave's half of the latent dims; operand reads run ahead
-    f32x16 s = f32x16{};
+    // ---- S^T over the 576 latent dims: two independent 16-token chains
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
     {
-      auto kop = [&](int j) {
-        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + qoff[j & 3] + (j >> 2) * 4096);
+      auto kop = [&](int j, int mt) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + koff[j & 1][mt] +
+                                                                                 (j >> 1) * 4096);
       };
-      bf16x8 rk[4];
-#pragma unroll
-      for (int j = 0; j < 3; ++j) rk[j] = kop(j);
+      bf16x8 r0[2], r1[2];
+      r0[0] = kop(0, 0);
+      r1[0] = kop(0, 1);
 #pragma unroll
       for (int j = 0; j < 18; ++j) {
-        if (j + 3 < 18) rk[(j + 3) & 3] = kop(j + 3);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rk[j & 3], qb[j], s, 0, 0, 0);
+        if (j + 1 < 18) {
+          r0[(j + 1) & 1] = kop(j + 1, 0);
+          r1[(j + 1) & 1] = kop(j + 1, 1);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0[j & 1], qb[j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1[j & 1], qb[j], s1, 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) xch[wave][i4][lane] = f32x4{s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]};
-    __syncthreads();            // partial S^T of both halves ready
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 o = xch[wave ^ 1][i4][lane];
-      s[4 * i4] += o.x;
-      s[4 * i4 + 1] += o.y;
-      s[4 * i4 + 2] += o.z;
-      s[4 * i4 + 3] += o.w;
-    }
+    float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};   // tokens 4g+i, 16+4g+i
 
-    // ---- online softmax for head n (tokens of lane group g)
+    // ---- online softmax for head n
     const uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[t]);
     if (vmask != 0xffffffffu) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = (i >> 2) * 8 + g * 4 + (i & 3);
+      for (int i = 0; i < 8; ++i) {
+        const int tok = (i >> 2) * 16 + g * 4 + (i & 3);
         if (!((vmask >> tok) & 1u)) s[i] = -INFINITY;
       }
     }
     float tmax = s[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;   // scale > 0 keeps the order
     const bool grow = tmax > m_used + kLazy || (m_used == -INFINITY && tmax > -INFINITY);
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? tmax : m_used;
       const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) oacc[i] *= alpha;
+      for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
       l_part *= alpha;
       lr_part *= alpha;
       m_used = m_new;
     }
     const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
-    uint32_t pb[8];
+    uint32_t pb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], a.scale_log2, -msub));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], a.scale_log2, -msub));
       const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
@@ -299,75 +298,54 @@ __global__ void __launch_bounds__(128 * HG, 1) mla_decode_kernel(MlaArgs a) {
       l_part += p0 + p1;
       lr_part += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
     }
-    const bf16x8 p_lo = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
-    const bf16x8 p_hi = __builtin_bit_cast(bf16x8, u32x4{pb[4], pb[5], pb[6], pb[7]});
+    const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
 
-    // ---- O^T += V^T . P^T over this wave's 256 value dims; operand reads run ahead
+    // ---- O^T += V^T . P^T over 32 value tiles of 16 dims; operand reads run ahead
     {
-      auto vop = [&](int i) {   // i = 2*mt + ks: tokens ks*16 + {g*4.., 8 + g*4..}
-        const lds_u8* p = tile + voff[(i >> 1) & 1] + (i >> 2) * 4096 + (i & 1) * 2048;   // ks: token groups 2ks, 2ks+1
+      auto vop = [&](int vt) {  // tokens 4g.. (first 8 bytes) and 16+4g.. (last 8 bytes)
+        const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4096;
         const u32x2 lo = lds_read_tr16(p);
-        const u32x2 hi = lds_read_tr16(p + 1024);
+        const u32x2 hi = lds_read_tr16(p + 2048);
         return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       };
       bf16x8 rv[4];
 #pragma unroll
       for (int i = 0; i < 3; ++i) rv[i] = vop(i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + 3 < 16) rv[(i + 3) & 3] = vop(i + 3);
-        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv[i & 3], (i & 1) ? p_hi : p_lo, oacc[i >> 1], 0, 0, 0);
+      for (int vt = 0; vt < 32; ++vt) {
+        if (vt + 3 < 32) rv[(vt + 3) & 3] = vop(vt + 3);
+        oacc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[vt & 3], pt, oacc[vt], 0, 0, 0);
       }
     }
   }
 
-  // ---- finish: l over both lane groups, normalise, write this wave's 256 dims
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float lr_tot = lr_part + __shfl_xor(lr_part, 32);
+  // ---- finish: l over the head's four lanes, normalise, write 512 dims
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float lr_tot = lr_part + __shfl_xor(lr_part, 16);
+  lr_tot += __shfl_xor(lr_tot, 32);
   const float inv = (lr_tot > 0.0f) ? 1.0f / lr_tot : 0.0f;
   const float lse = (l_tot > 0.0f) ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   if (!head_ok) return;
   const bool direct = a.splits == 1;
   const int64_t obase = (direct ? ((int64_t)qr * a.H + head) : ((((int64_t)qr * a.splits + split) * a.H + head))) *
-                            kVDim + half * 256;
-  if (!direct) {
-    // split partials keep the precision of the final output
-    if (a.o_f32) {
+                            kVDim + g * 4;
+  void* dst = direct ? a.o : a.part_o;
+  if (a.o_f32) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + obase + mt * 32 + i4 * 8 + g * 4) =
-              f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
-                    oacc[mt][i4 * 4 + 3] * inv};
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + obase + mt * 32 + i4 * 8 + g * 4) =
-              u32x2{pack_bf16x2(oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv),
-                    pack_bf16x2(oacc[mt][i4 * 4 + 2] * inv, oacc[mt][i4 * 4 + 3] * inv)};
-    }
-    if (g == 0 && half == 0) a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
-  } else if (a.o_f32) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + obase + mt * 32 + i4 * 8 + g * 4) =
-            f32x4{oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv, oacc[mt][i4 * 4 + 2] * inv,
-                  oacc[mt][i4 * 4 + 3] * inv};
-    if (g == 0 && half == 0) a.lse[(int64_t)qr * a.H + head] = lse;
+    for (int vt = 0; vt < 32; ++vt)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + obase + vt * 16) = oacc[vt] * inv;
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + mt * 32 + i4 * 8 + g * 4) =
-            u32x2{pack_bf16x2(oacc[mt][i4 * 4 + 0] * inv, oacc[mt][i4 * 4 + 1] * inv),
-                  pack_bf16x2(oacc[mt][i4 * 4 + 2] * inv, oacc[mt][i4 * 4 + 3] * inv)};
-    if (g == 0 && half == 0) a.lse[(int64_t)qr * a.H + head] = lse;
+    for (int vt = 0; vt < 32; ++vt)
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + obase + vt * 16) =
+          u32x2{pack_bf16x2(oacc[vt].x * inv, oacc[vt].y * inv), pack_bf16x2(oacc[vt].z * inv, oacc[vt].w * inv)};
+  }
+  if (g == 0) {
+    if (direct)
+      a.lse[(int64_t)qr * a.H + head] = lse;
+    else
+      a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
   }
 }
 
@@ -431,8 +409,11 @@ static int device_cus() {
   return cus;
 }
 
+// waves per work-group: 16 heads each, up to one per SIMD
+static int mla_waves(int H) { return H >= 64 ? 4 : (H > 16 ? 2 : 1); }
+
 static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_split) {
-  const int wg_heads = (H > 32) ? 64 : 32;
+  const int wg_heads = 16 * mla_waves(H);
   const int64_t wgs = (int64_t)B * Sq * ((H + wg_heads - 1) / wg_heads);
   const int tiles = (k + kTT - 1) / kTT;
   // one work-group per CU
@@ -496,11 +477,14 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
     a.part_o = a.part_lse + (size_t)B * Sq * splits * H;
   }
   const int QR = B * Sq;
-  if (H > 32) {
-    DSA_LAUNCH(mla_decode_kernel<2>, dim3(splits * QR * ((H + 63) / 64)), dim3(256), 0, stream, a);
-  } else {
-    DSA_LAUNCH(mla_decode_kernel<1>, dim3(splits * QR), dim3(128), 0, stream, a);
-  }
+  const int nw = mla_waves(H);
+  const int nhb = (H + 16 * nw - 1) / (16 * nw);
+  if (nw == 4)
+    DSA_LAUNCH(mla_decode_kernel<4>, dim3(splits * QR * nhb), dim3(256), 0, stream, a);
+  else if (nw == 2)
+    DSA_LAUNCH(mla_decode_kernel<2>, dim3(splits * QR * nhb), dim3(128), 0, stream, a);
+  else
+    DSA_LAUNCH(mla_decode_kernel<1>, dim3(splits * QR * nhb), dim3(64), 0, stream, a);
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
   DSA_LAUNCH(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
