@@ -21,10 +21,8 @@
 // (global_load_lds_dwordx4: lane i of a wave instruction lands at M0 + 16 i), two tiles
 // ahead of the one being computed; no VGPRs hold rows in flight.  A tile is stored as
 // 1 KB blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one
-// wave instruction fetches eight whole 128-byte lines and each lane streams one row.
-// Inside a block, 16-byte chunk c of token m sits at position m*8 + ((c%8) ^ swz(m)),
-// which keeps both the K reads (one chunk of 8 consecutive tokens per 128 bytes) and the
-// transpose reads (two chunks of 4 tokens) free of LDS bank conflicts.
+// wave instruction fetches eight whole 128-byte lines; the placement inside a block
+// (chunk_byte) keeps both operand reads free of LDS bank conflicts.
 // Online softmax in base 2 with a lazy rescale (the running max is only moved when it
 // grows by more than 2^8), which leaves o and lse mathematically unchanged.
 #include "common.h"
@@ -37,8 +35,7 @@ constexpr int kRowBytes = kRowEl * 2;
 constexpr int kTT = 32;                     // tokens per tile
 constexpr int kChunks = kRowBytes / 16;     // 72 x 16 B per row
 constexpr int kTileSlots = kTT * kChunks;   // 2304 chunk slots per tile
-constexpr int kTileBytes = kTileSlots * 16; // 36864
-constexpr int kRing = 3;                    // LDS tiles: one computed, two in flight
+constexpr int kTileBytes = 36 * 1040;       // 36 blocks of 8 tokens x 128 bytes at a 1040-byte stride
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;
@@ -64,12 +61,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// chunk swizzle of token m (mod 8) inside a 1 KB block
-__device__ __forceinline__ int chunk_swz(int m) { return ((m << 1) & 6) | ((m >> 2) & 1); }
-
-// byte offset of 16-byte chunk c of token n inside a tile
+// Byte offset of 16-byte chunk c of token n inside a tile.  Token group tg = n / 8 and
+// chunk group cg = c / 8 select block cg * 4 + tg (1 KB of data at a 1040-byte stride);
+// inside it, chunk cc = c % 8 of token m = n % 8 sits at 16-byte slot m * 8 + (cc ^ 2(m/2)).
+// One LDS-direct load instruction fills a block with eight whole 128-byte lines (eight
+// consecutive lanes per token).  With 64 four-byte LDS banks (256 bytes per cycle) both
+// operand reads are conflict-free: within a block a K read (one chunk of 8 tokens) covers
+// one bank parity and the 16-byte stride padding moves the next token group's block to the
+// other parity; a transpose read (two chunks of 8 tokens) covers all 64 banks.
+constexpr int kBlockBytes = 1040;
 __device__ __forceinline__ int chunk_byte(int n, int c) {
-  return ((((c >> 3) << 2) + (n >> 3)) * 64 + (n & 7) * 8 + ((c & 7) ^ chunk_swz(n & 7))) * 16;
+  const int m = n & 7, cc = c & 7;
+  return (((c >> 3) << 2) + (n >> 3)) * kBlockBytes + (m * 8 + (cc ^ ((m >> 1) << 1))) * 16;
 }
 
 // 16 bytes from global memory into LDS at M0 + 16 * lane (M0 = lds_addr, wave-uniform).  No
@@ -79,11 +82,11 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
 }
 
 // LDS-direct loads R..CPT-1 of one tile: load r fetches chunk group r / NSRC of the row in
-// src[r % NSRC] into 1 KB block r * NW of the wave's stripe
+// src[r % NSRC] into block r * NW of the wave's stripe
 template <int R, int CPT, int NSRC, int NW>
 __device__ __forceinline__ void dma_tile(const char* const* src, uint32_t dst) {
   if constexpr (R < CPT) {
-    lds_dma16(src[R % NSRC] + (R / NSRC) * 128, dst + R * NW * 1024);
+    lds_dma16(src[R % NSRC] + (R / NSRC) * 128, dst + R * NW * kBlockBytes);
     dma_tile<R + 1, CPT, NSRC, NW>(src, dst);
   }
 }
@@ -121,19 +124,27 @@ __device__ __forceinline__ void mla_block_unit(int nhb, int& unit, int& hb) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int NW>
-__global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
-  constexpr int NT = 64 * NW;
-  constexpr int CPT = kTileSlots / NT;      // LDS-direct loads per thread per tile
-  static_assert(kTileSlots % NT == 0, "tile must split evenly over the threads");
-  constexpr int NSRC = (4 + NW - 1) / NW;   // token groups one lane streams per tile
+// NW waves per stream (16 heads each), NS token streams: stream s handles tiles T with
+// T % NS == s, so NS waves share each SIMD and hide each other's latencies.  Each stream
+// keeps its own online-softmax state; the streams are merged through LDS at the end.
+template <int NW, int NS>
+__global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) {
+  constexpr int NT = 64 * NW * NS;
+  constexpr int NTS = 64 * NW;              // threads of one stream
+  constexpr int CPT = kTileSlots / NTS;     // LDS-direct loads per thread per tile
+  static_assert(kTileSlots % NTS == 0, "tile must split evenly over a stream's threads");
+  constexpr int NSRC = 4 / NW;              // token groups one lane streams per tile
   static_assert(NSRC * NW == 4, "NW must divide the 4 token groups of a tile");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kTileBytes];
+  constexpr int PD = (NS == 1) ? 2 : 1;     // iterations a tile is loaded ahead
+  constexpr int RING = NS * (PD + 1);       // LDS tiles
+  static_assert(RING * kTileBytes + kMaxSplit * 8 + 128 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RING][kTileBytes];
   __shared__ int64_t rowoff[kMaxSplit];     // byte offset of each selected row of the split, -1 = none
   __shared__ uint32_t tmask[kMaxSplit / kTT];  // valid-row bits per tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int stream = wave / NW, ws = wave % NW;
   const int n = lane & 15, g = lane >> 4;
   const int nhb = (a.H + 16 * NW - 1) / (16 * NW);
   int unit, hb;
@@ -141,7 +152,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   const int qr = unit / a.splits;
   const int split = unit - qr * a.splits;
   const int b = qr / a.Sq;
-  const int head = hb * 16 * NW + wave * 16 + n;
+  const int head = hb * 16 * NW + ws * 16 + n;
   const bool head_ok = head < a.H;
 
   const int e_begin = split * a.per_split;
@@ -182,15 +193,15 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   }
 
   // ---- per-lane constants of the three access patterns
-  // LDS-direct load r of this lane: token group (wave + NW * (r % NSRC)), chunk group
-  // r / NSRC; the lane fetches chunk ((lane & 7) ^ swz) of token 8 * group + lane / 8
-  const int dlane = ((lane & 7) ^ chunk_swz(lane >> 3)) * 16;
-  int koff[2][2];               // K operand of M tile mt, k-step j: koff[j % 2][mt] + 4096 (j / 2)
+  // LDS-direct load r of this lane: token group tg = ws + NW * (r % NSRC), chunk group
+  // r / NSRC; the lane fetches chunk (lane % 8) ^ 2(m/2) of token m = 8 tg + lane / 8
+  const int dlane = ((lane & 7) ^ (((lane >> 4) & 3) << 1)) * 16;
+  int koff[2][2];               // K operand of M tile mt, k-step j: koff[j % 2][mt] + 4 blocks (j / 2)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) koff[j][mt] = chunk_byte(n + 16 * mt, 4 * j + g);
-  int voff[4];                  // V^T operand (transpose read) of value tile vt: voff[vt % 4] + 4096 (vt / 4)
+  int voff[4];                  // V^T operand (transpose read) of value tile vt: voff[vt % 4] + 4 blocks (vt / 4)
   {
     const int jj = n >> 2, qq = n & 3;          // source lane n = 4 jj + qq of this 16-lane group
     const int tok = 4 * g + jj;
@@ -201,26 +212,29 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   __syncthreads();              // rowoff / tmask ready
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
-  const char* nsrc[NSRC];       // rows of the next tile to issue
-  auto prepare = [&](int t) {
+  const char* nsrc[NSRC];       // rows of the next tile this wave issues
+  auto prepare = [&](int T) {
 #pragma unroll
     for (int p = 0; p < NSRC; ++p) {
-      const int64_t off = rowoff[t * kTT + (wave + NW * p) * 8 + (lane >> 3)];
+      const int64_t off = rowoff[T * kTT + (ws + NW * p) * 8 + (lane >> 3)];
       nsrc[p] = (off >= 0 ? a.rows.base + off : stand_in) + dlane;
     }
   };
-  auto issue = [&](int t) {
-    const uint32_t dst = ring_lds + (uint32_t)((t % kRing) * kTileBytes + wave * 1024);
+  auto issue = [&](int T) {
+    const uint32_t dst = ring_lds + (uint32_t)((T % RING) * kTileBytes + ws * kBlockBytes);
     dma_tile<0, CPT, NSRC, NW>(nsrc, dst);
   };
 
-  prepare(0);
-  issue(0);
-  if (ntiles > 1) {
-    prepare(1);
-    issue(1);
+  const int iters = (ntiles + NS - 1) / NS;  // tile of iteration i for this stream: i*NS + stream
+#pragma unroll
+  for (int i = 0; i < PD; ++i) {
+    const int T = i * NS + stream;
+    if (T < ntiles) {
+      prepare(T);
+      issue(T);
+    }
   }
-  if (ntiles > 2) prepare(2);
+  if (PD * NS + stream < ntiles) prepare(PD * NS + stream);
 
   f32x4 oacc[32];
 #pragma unroll
@@ -229,52 +243,63 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
   float l_part = 0.0f;          // this lane's share of sum p (fp32 p: for lse)
   float lr_part = 0.0f;         // this lane's share of sum bf16(p) (the PV weights: for o)
 
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles)
-      wait_vmcnt<CPT>();        // this wave's loads of tile t are done (tile t+1 may be in flight)
+  for (int i = 0; i < iters; ++i) {
+    const int T = i * NS + stream;
+    if (PD == 2 && T + NS < ntiles)
+      wait_vmcnt<CPT>();        // this wave's loads of tile T are done (the next one may be in flight)
     else
       wait_vmcnt<0>();
-    __syncthreads();            // tile t complete for all waves; slot (t+2)%3 free
-    if (t + 2 < ntiles) {
-      issue(t + 2);
-      if (t + 3 < ntiles) prepare(t + 3);
+    __syncthreads();            // this iteration's tiles complete; the slots of iteration i-1 are free
+    const int Tn = T + PD * NS;
+    if (Tn < ntiles) {
+      issue(Tn);
+      if (Tn + NS < ntiles) prepare(Tn + NS);
     }
-    const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((t % kRing) * kTileBytes));
+    if (T >= ntiles) continue;  // stream without a tile in the last iteration
+    const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((T % RING) * kTileBytes));
 
     // ---- S^T over the 576 latent dims: two independent 16-token chains
     f32x4 s0 = f32x4{}, s1 = f32x4{};
     {
       auto kop = [&](int j, int mt) {
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + koff[j & 1][mt] +
-                                                                                 (j >> 1) * 4096);
+                                                                                 (j >> 1) * 4 * kBlockBytes);
       };
-      bf16x8 r0[2], r1[2];
-      r0[0] = kop(0, 0);
-      r1[0] = kop(0, 1);
+      constexpr int RK = (NS == 1) ? 2 : 1;    // operand reads issued ahead (none under the tighter budget)
+      bf16x8 r0[RK], r1[RK];
+      if constexpr (RK == 2) {
+        r0[0] = kop(0, 0);
+        r1[0] = kop(0, 1);
+      }
 #pragma unroll
       for (int j = 0; j < 18; ++j) {
-        if (j + 1 < 18) {
-          r0[(j + 1) & 1] = kop(j + 1, 0);
-          r1[(j + 1) & 1] = kop(j + 1, 1);
+        if constexpr (RK == 2) {
+          if (j + 1 < 18) {
+            r0[(j + 1) & 1] = kop(j + 1, 0);
+            r1[(j + 1) & 1] = kop(j + 1, 1);
+          }
+        } else {
+          r0[0] = kop(j, 0);
+          r1[0] = kop(j, 1);
         }
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0[j & 1], qb[j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1[j & 1], qb[j], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0[j % RK], qb[j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1[j % RK], qb[j], s1, 0, 0, 0);
       }
     }
     float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};   // tokens 4g+i, 16+4g+i
 
     // ---- online softmax for head n
-    const uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[t]);
+    const uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[T]);
     if (vmask != 0xffffffffu) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i >> 2) * 16 + g * 4 + (i & 3);
-        if (!((vmask >> tok) & 1u)) s[i] = -INFINITY;
+      for (int c = 0; c < 8; ++c) {
+        const int tok = (c >> 2) * 16 + g * 4 + (c & 3);
+        if (!((vmask >> tok) & 1u)) s[c] = -INFINITY;
       }
     }
     float tmax = s[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
+    for (int c = 1; c < 8; ++c) tmax = fmaxf(tmax, s[c]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;   // scale > 0 keeps the order
     const bool grow = tmax > m_used + kLazy || (m_used == -INFINITY && tmax > -INFINITY);
@@ -282,7 +307,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
       const float m_new = grow ? tmax : m_used;
       const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
+      for (int c = 0; c < 32; ++c) oacc[c] *= alpha;
       l_part *= alpha;
       lr_part *= alpha;
       m_used = m_new;
@@ -290,11 +315,11 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
     const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
     uint32_t pb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], a.scale_log2, -msub));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], a.scale_log2, -msub));
-      const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-      pb[i] = w;
+    for (int c = 0; c < 4; ++c) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c], a.scale_log2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + 1], a.scale_log2, -msub));
+      const uint32_t w = pack_bf16x2(p0, p1);
+      pb[c] = w;
       l_part += p0 + p1;
       lr_part += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
     }
@@ -303,20 +328,47 @@ __global__ void __launch_bounds__(64 * NW, 1) mla_decode_kernel(MlaArgs a) {
     // ---- O^T += V^T . P^T over 32 value tiles of 16 dims; operand reads run ahead
     {
       auto vop = [&](int vt) {  // tokens 4g.. (first 8 bytes) and 16+4g.. (last 8 bytes)
-        const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4096;
+        const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4 * kBlockBytes;
         const u32x2 lo = lds_read_tr16(p);
-        const u32x2 hi = lds_read_tr16(p + 2048);
+        const u32x2 hi = lds_read_tr16(p + 2 * kBlockBytes);   // tokens + 16: two token groups on
         return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       };
-      bf16x8 rv[4];
+      constexpr int RV = (NS == 1) ? 4 : 2;    // operand reads in flight (2 under the tighter register budget)
+      bf16x8 rv[RV];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) rv[i] = vop(i);
+      for (int c = 0; c < RV - 1; ++c) rv[c] = vop(c);
 #pragma unroll
       for (int vt = 0; vt < 32; ++vt) {
-        if (vt + 3 < 32) rv[(vt + 3) & 3] = vop(vt + 3);
-        oacc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[vt & 3], pt, oacc[vt], 0, 0, 0);
+        if (vt + RV - 1 < 32) rv[(vt + RV - 1) % RV] = vop(vt + RV - 1);
+        oacc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[vt % RV], pt, oacc[vt], 0, 0, 0);
       }
     }
+  }
+
+  if constexpr (NS == 2) {
+    // ---- merge stream 1 into stream 0 through the (now idle) ring
+    __syncthreads();
+    f32x4* xo = reinterpret_cast<f32x4*>(&ring[0][0]);                  // [NW][32][64]
+    float* xs = reinterpret_cast<float*>(xo + NW * 32 * 64);             // [NW][3][64]
+    static_assert(NW * 32 * 64 * 16 + NW * 3 * 64 * 4 <= RING * kTileBytes, "merge staging fits the ring");
+    if (stream == 1) {
+#pragma unroll
+      for (int vt = 0; vt < 32; ++vt) xo[(ws * 32 + vt) * 64 + lane] = oacc[vt];
+      xs[(ws * 3 + 0) * 64 + lane] = m_used;
+      xs[(ws * 3 + 1) * 64 + lane] = l_part;
+      xs[(ws * 3 + 2) * 64 + lane] = lr_part;
+    }
+    __syncthreads();
+    if (stream == 1) return;
+    const float m1 = xs[(ws * 3 + 0) * 64 + lane];
+    const float m_new = fmaxf(m_used, m1);
+    const float a0 = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - m_new);
+    l_part = l_part * a0 + xs[(ws * 3 + 1) * 64 + lane] * a1;
+    lr_part = lr_part * a0 + xs[(ws * 3 + 2) * 64 + lane] * a1;
+#pragma unroll
+    for (int vt = 0; vt < 32; ++vt) oacc[vt] = oacc[vt] * a0 + xo[(ws * 32 + vt) * 64 + lane] * a1;
+    m_used = m_new;
   }
 
   // ---- finish: l over the head's four lanes, normalise, write 512 dims
@@ -479,12 +531,13 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   const int QR = B * Sq;
   const int nw = mla_waves(H);
   const int nhb = (H + 16 * nw - 1) / (16 * nw);
+  const dim3 grid(splits * QR * nhb);
   if (nw == 4)
-    DSA_LAUNCH(mla_decode_kernel<4>, dim3(splits * QR * nhb), dim3(256), 0, stream, a);
+    DSA_LAUNCH((mla_decode_kernel<4, 2>), grid, dim3(512), 0, stream, a);
   else if (nw == 2)
-    DSA_LAUNCH(mla_decode_kernel<2>, dim3(splits * QR * nhb), dim3(128), 0, stream, a);
+    DSA_LAUNCH((mla_decode_kernel<2, 2>), grid, dim3(256), 0, stream, a);
   else
-    DSA_LAUNCH(mla_decode_kernel<1>, dim3(splits * QR * nhb), dim3(64), 0, stream, a);
+    DSA_LAUNCH((mla_decode_kernel<1, 2>), grid, dim3(128), 0, stream, a);
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
   DSA_LAUNCH(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
