@@ -127,13 +127,15 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float*
  * (lowest position wins a tie); -0.0 and +0.0 compare equal.  Output per (b,t) is the
  * selected positions in ascending order, padded with -1 when vis(b,t) < k.
  *
- *   scores   [B, Sq, score_stride] float32 (positions < vis(b,t) are read; no NaNs)
+ *   scores   [B, Sq, score_stride] float32 (positions < vis(b,t) are read; no NaNs;
+ *            a vis(b,t) above score_stride is clamped to score_stride)
  *   idx      [B, Sq, k] int32 output
  *   ws       workspace of at least dsa_topk_workspace_size(B, Sq, k, score_stride) bytes,
- *            8-byte aligned: per row chunk, its best keys as candidates and its cut key,
- *            for a two-stage select (chunk c keeps twice its share ceil(k*len_c/n) of
- *            the k; the exact select over the candidates is checked against the cut
- *            keys and redone over the row's scores when a chunk could hold more)
+ *            8-byte aligned, contents on entry ignored: per row, the best keys of each
+ *            8192-position chunk as candidates plus each chunk's cut key, for a
+ *            two-stage select (chunk c keeps twice its share ceil(k*len_c/n) of the k;
+ *            the exact select over the candidates is checked against the cut keys and
+ *            redone over the row's scores when a chunk could hold more)
  * Supported: 1 <= k <= 8192, B*Sq <= 65535, score_stride <= 2^21.
  */
 size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride);

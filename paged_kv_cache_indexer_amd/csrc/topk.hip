@@ -4,18 +4,21 @@
 // Order: score descending, then position ascending; -0.0 == +0.0.  Scores map to
 // order-preserving uint32 keys.
 //
-// Stage 1 (many work-groups per row): the row's n positions are cut into chunks of C
-// positions; chunk c (len_c positions) keeps its r_c = min(len_c, 2 ceil(k len_c / n)) best
-// keys as candidates, in position order, and records its r_c-th largest key X_c.
-// Stage 2 (one work-group per row): the exact select over the ~2k candidates gives the
-// row's k-th key T; it is the row's answer whenever every chunk that left keys out has
-// X_c < T.  Otherwise the row is selected again from its scores, filtered by a lower bound
-// of the k-th key derived from the X_c (see topk_select_kernel).
+// Stage 1 (one work-group per chunk of kChunk positions of a row): chunk c (len_c
+// positions) keeps its r_c = min(len_c, 2 ceil(k len_c / n)) best keys as candidates, in
+// position order, and records a cut key X_c: every key it left out is <= X_c, and one
+// equal to X_c sits after every kept key equal to it.  The chunks' candidates are written
+// back to back per row, so the row's candidate list is in position order.
+// Stage 2 (one work-group per row): the exact select over the ~2k candidates is the
+// row's answer whenever every chunk that left keys out has X_c below the smallest key
+// the answer may take.  Otherwise the row is selected again from its scores, filtered by
+// a lower bound of the k-th key derived from the X_c (see topk_select_kernel).
 //
-// Both stages use the same select: an MSB-first radix search for the r-th largest key T
-// (digits of up to 11 bits, starting below the bits that the smallest and the largest
-// key share) and `need`, the number of keys equal to T that are taken (lowest positions
-// first).
+// Hot paths keep each thread's kPer keys in registers: an MSB-first radix search (digits
+// of up to 11 bits, starting below the bits the smallest and largest key share; two
+// barriers per digit; it stops as soon as the chosen digit's keys are all taken), then
+// one ordered take from per-wave ballots.  The rare re-select runs the same search over
+// keys staged in LDS.
 #include <algorithm>
 
 #include "common.h"
@@ -24,21 +27,29 @@ namespace dsa {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kPer = 8;                            // keys per thread held in registers
+constexpr int kChunk = kTopkThreads * kPer;        // stage-1 chunk: 8192 positions
+constexpr int kMaxChunks = 256;                    // rows up to 2^21 positions
+constexpr int kMaxCand = kTopkThreads * kPer;      // stage-2 candidates held in registers
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kMaxChunkElems = 32768;     // stage-1 LDS staging: 128 KB of keys
-constexpr int kTargetChunks = 8;
 
+// ---- LDS-resident select (the rare re-select over a row's scores) ----
+
+template <int NT>
 struct TopkShared {
+  static_assert(NT % 64 == 0 && (1 << 11) % NT == 0, "whole waves; digits split evenly over threads");
   uint32_t hist[kBins];
-  int wave_tot[2 * kTopkWaves + 1];
-  uint32_t red[2 * kTopkWaves];
+  int wave_tot[2 * (NT / 64) + 1];
+  uint32_t red[2 * (NT / 64)];
   uint32_t sel_digit;
   int sel_above;
 };
 
 // block-wide exclusive scan of one int per thread; returns prefix, writes total
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -49,30 +60,31 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
   if (lane == 63) wave_tot[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int t = (lane < kTopkWaves) ? wave_tot[lane] : 0;
+    int t = (lane < NW) ? wave_tot[lane] : 0;
     int s = t;
 #pragma unroll
-    for (int o = 1; o < kTopkWaves; o <<= 1) {
+    for (int o = 1; o < NW; o <<= 1) {
       const int y = __shfl_up(s, o);
       if (lane >= o) s += y;
     }
-    if (lane < kTopkWaves) wave_tot[kTopkWaves + lane] = s - t;   // exclusive wave offsets
-    if (lane == kTopkWaves - 1) wave_tot[2 * kTopkWaves] = s;
+    if (lane < NW) wave_tot[NW + lane] = s - t;   // exclusive wave offsets
+    if (lane == NW - 1) wave_tot[2 * NW] = s;
   }
   __syncthreads();
-  const int res = wave_tot[kTopkWaves + wave] + x - v;
-  total = wave_tot[2 * kTopkWaves];
+  const int res = wave_tot[NW + wave] + x - v;
+  total = wave_tot[2 * NW];
   __syncthreads();
   return res;
 }
 
 // k-th largest key T among keys[0..n) (n > k) and how many keys == T are taken.
 // KEY(i) returns the i-th key; reads are repeated once per pass.
-template <typename KeyFn>
-__device__ void radix_select(KeyFn KEY, int n, int k, TopkShared& sh, uint32_t& T_out, int& need_out) {
+template <int NT, typename KeyFn>
+__device__ void radix_select(KeyFn KEY, int n, int k, TopkShared<NT>& sh, uint32_t& T_out, int& need_out) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xffffffffu, kmax = 0;
-  for (int i = tid; i < n; i += kTopkThreads) {
+  for (int i = tid; i < n; i += NT) {
     const uint32_t key = KEY(i);
     kmin = min(kmin, key);
     kmax = max(kmax, key);
@@ -84,14 +96,14 @@ __device__ void radix_select(KeyFn KEY, int n, int k, TopkShared& sh, uint32_t& 
   }
   if (lane == 0) {
     sh.red[wave] = kmin;
-    sh.red[kTopkWaves + wave] = kmax;
+    sh.red[NW + wave] = kmax;
   }
   __syncthreads();
   kmin = 0xffffffffu;
   kmax = 0;
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     kmin = min(kmin, sh.red[w]);
-    kmax = max(kmax, sh.red[kTopkWaves + w]);
+    kmax = max(kmax, sh.red[NW + w]);
   }
   uint32_t prefix;
   int remaining = k;
@@ -108,25 +120,33 @@ __device__ void radix_select(KeyFn KEY, int n, int k, TopkShared& sh, uint32_t& 
     const int nb = hi < kDigitBits ? hi : kDigitBits;
     const int sh_ = hi - nb;
     const uint32_t dmask = (1u << nb) - 1u;
-    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kTopkThreads) {
+    for (int i = tid; i < n; i += NT) {
       const uint32_t key = KEY(i);
       const bool match = (hi == 32) ? true : ((key >> hi) == (prefix >> hi));
       if (match) atomicAdd(&sh.hist[(key >> sh_) & dmask], 1u);
     }
     __syncthreads();
-    // suffix counts from the top digit down; thread i covers digits 2047-2i, 2046-2i
-    const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
-    const int c_hi = (int)sh.hist[d_hi], c_lo = (int)sh.hist[d_lo];
+    // suffix counts from the top digit down; thread i covers the BPT digits below
+    // kBins-1-BPT*i, highest first
+    constexpr int BPT = kBins / NT;
+    const int d0 = kBins - 1 - BPT * tid;
+    int cnt[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      cnt[j] = (int)sh.hist[d0 - j];
+      sum += cnt[j];
+    }
     int tot;
-    const int before = block_exclusive_scan(c_hi + c_lo, sh.wave_tot, tot);
-    if (before < remaining && remaining <= before + c_hi) {
-      sh.sel_digit = (uint32_t)d_hi;
-      sh.sel_above = before;
-    } else if (before + c_hi < remaining && remaining <= before + c_hi + c_lo) {
-      sh.sel_digit = (uint32_t)d_lo;
-      sh.sel_above = before + c_hi;
+    int before = block_exclusive_scan<NT>(sum, sh.wave_tot, tot);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (before < remaining && remaining <= before + cnt[j]) {
+        sh.sel_digit = (uint32_t)(d0 - j);
+        sh.sel_above = before;
+      }
+      before += cnt[j];
     }
     __syncthreads();
     prefix |= sh.sel_digit << sh_;
@@ -138,14 +158,14 @@ __device__ void radix_select(KeyFn KEY, int n, int k, TopkShared& sh, uint32_t& 
   need_out = remaining;
 }
 
-// Ordered compaction: for i ascending, take i if key > T, or key == T among the first
+// Ordered compaction (the re-select path): for i ascending, take i if key > T, or key == T among the first
 // `need` such; EMIT(slot, i, key) for each taken element.  Each thread owns PER
 // consecutive elements per round so the scan order is element order.
-template <int PER, typename KeyFn, typename EmitFn>
-__device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, TopkShared& sh, EmitFn EMIT) {
+template <int NT, int PER, typename KeyFn, typename EmitFn>
+__device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, TopkShared<NT>& sh, EmitFn EMIT) {
   const int tid = threadIdx.x;
   int sel_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < n && sel_base < k; c0 += kTopkThreads * PER) {
+  for (int c0 = 0; c0 < n && sel_base < k; c0 += NT * PER) {
     uint32_t key[PER];
     int n_gt = 0, n_eq = 0;
 #pragma unroll
@@ -156,12 +176,12 @@ __device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, Topk
       n_eq += (i < n && key[r] == T);
     }
     int eq_tot, gt_tot;
-    int eq_rank = eq_base + block_exclusive_scan(n_eq, sh.wave_tot, eq_tot);
+    int eq_rank = eq_base + block_exclusive_scan<NT>(n_eq, sh.wave_tot, eq_tot);
     // taken by this thread: all its > T, plus its == T while the rank is below need
     int take_eq = need - eq_rank;
     take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
     int sel_tot;
-    int pos = sel_base + block_exclusive_scan(n_gt + take_eq, sh.wave_tot, sel_tot);
+    int pos = sel_base + block_exclusive_scan<NT>(n_gt + take_eq, sh.wave_tot, sel_tot);
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       const int i = c0 + tid * PER + r;
@@ -182,23 +202,215 @@ __device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, Topk
   }
 }
 
+// ---- register-resident select (both stages' hot path) ----
+
+// Wave-wide inclusive scans through DPP lane moves (no LDS round trips): four row
+// shifts build each 16-lane row's prefix, then row broadcasts of lanes 15 and 31 carry
+// the rows' totals forward.  Lanes with no source lane take the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x, uint32_t identity, Op op) {
+  x = op(x, dpp_move<0x111, 0xf>(x, identity));   // row_shr:1
+  x = op(x, dpp_move<0x112, 0xf>(x, identity));   // row_shr:2
+  x = op(x, dpp_move<0x114, 0xf>(x, identity));   // row_shr:4
+  x = op(x, dpp_move<0x118, 0xf>(x, identity));   // row_shr:8
+  x = op(x, dpp_move<0x142, 0xa>(x, identity));   // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_move<0x143, 0xc>(x, identity));   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ int wave_sum_incl(int x) {
+  return (int)wave_scan_incl((uint32_t)x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = wave_scan_incl(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = wave_scan_incl(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+struct alignas(16) RadixShared {
+  uint32_t hist[2][kBins];                 // digit histograms, alternating per pass
+  uint32_t red[2 * kTopkWaves];            // per-wave min / max, then per-wave digit counts
+  int cnt[kPer * kTopkWaves];              // ordered take: packed counts per (slot q, wave)
+  uint32_t sel_digit;
+  int sel_above;
+  int sel_count;
+};
+
+// Sum of x over lanes below `upto` (a wave-uniform lane count <= 64), for x held by lane i
+// as the i-th value.
+__device__ __forceinline__ int wave_prefix_below(int x, int upto) {
+  const int incl = wave_sum_incl(x);
+  return upto == 0 ? 0 : __builtin_amdgcn_readlane(incl, upto - 1);
+}
+
+// Block min / max (each thread passes its own); also clears both histograms.  One barrier.
+__device__ __forceinline__ void block_minmax(uint32_t& kmin, uint32_t& kmax, RadixShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    sh.red[wave] = kmin;
+    sh.red[kTopkWaves + wave] = kmax;
+  }
+  for (int i = threadIdx.x; i < 2 * kBins; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+  __syncthreads();
+  kmin = wave_min(lane < kTopkWaves ? sh.red[lane] : 0xffffffffu);
+  kmax = wave_max(lane < kTopkWaves ? sh.red[kTopkWaves + lane] : 0u);
+}
+
+// Threshold of the k best keys of the work-group: every key > T is taken, and the first
+// `need` keys == T in position order.  Empty slots hold key 0, which no select takes:
+// float_key maps every non-NaN float above 2^23 - 2, the first digit pass skips 0, and
+// the later passes' prefix does not match it.
+// kmin / kmax are the block min / max of the real keys (block_minmax, which also clears
+// the histograms).  Per digit: histogram atomics, a block scan of the counts from the top
+// digit down, and the one thread whose digits hold the `remaining`-th key publishes it:
+// three barriers.  When a digit's keys are all taken before the last digit, T is one below
+// that digit's smallest key and need = 0.
+template <int PER>
+__device__ void radix_select_reg(const uint32_t (&key)[PER], int k, uint32_t kmin, uint32_t kmax,
+                                 RadixShared& sh, uint32_t& T_out, int& need_out) {
+  static_assert(kBins == 2 * kTopkThreads, "each thread owns two digits");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t prefix;
+  int hi;
+  if (kmin == kmax) {
+    prefix = kmin;
+    hi = 0;
+  } else {
+    hi = 32 - __builtin_clz(kmin ^ kmax);
+    prefix = (hi == 32) ? 0u : (kmin & ~((1u << hi) - 1u));
+  }
+  int remaining = k;
+  int p = 0;
+  while (hi > 0) {
+    const int nb = hi < kDigitBits ? hi : kDigitBits;
+    const int s = hi - nb;
+    uint32_t* h = sh.hist[p & 1];
+    if (p == 0) {                                  // every real key shares the prefix; empty slots skipped
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if (key[q] != 0u) atomicAdd(&h[__builtin_amdgcn_ubfe(key[q], s, nb)], 1u);
+    } else {
+      const uint32_t mhi = ~((1u << hi) - 1u);     // hi <= 21 here
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if ((key[q] & mhi) == prefix) atomicAdd(&h[__builtin_amdgcn_ubfe(key[q], s, nb)], 1u);
+    }
+    __syncthreads();
+    // thread t owns digits kBins-1-2t (c_hi) and kBins-2-2t (c_lo): thread order is
+    // descending digit order, so a block scan of c_hi + c_lo counts the keys above.
+    const uint2 pair = *reinterpret_cast<const uint2*>(h + kBins - 2 - 2 * threadIdx.x);
+    const int c_lo = (int)pair.x, c_hi = (int)pair.y, c2 = c_hi + c_lo;
+    const int incl = wave_sum_incl(c2);
+    if (lane == 63) sh.red[wave] = (uint32_t)incl;
+    // the other histogram was last read before the previous pass's last barrier
+    uint32_t* hz = sh.hist[(p + 1) & 1];
+    for (int i = threadIdx.x; i < kBins; i += kTopkThreads) hz[i] = 0;
+    __syncthreads();
+    const int before = wave_prefix_below(lane < kTopkWaves ? (int)sh.red[lane] : 0, wave) + incl - c2;
+    if (before < remaining && remaining <= before + c2) {   // exactly one thread
+      const bool top = remaining <= before + c_hi;
+      sh.sel_digit = (uint32_t)(kBins - 1 - 2 * (int)threadIdx.x - (top ? 0 : 1));
+      sh.sel_above = top ? before : before + c_hi;
+      sh.sel_count = top ? c_hi : c_lo;
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << s;
+    remaining -= sh.sel_above;
+    const int count = sh.sel_count;
+    hi = s;
+    ++p;
+    if (hi > 0 && count == remaining) {            // the whole digit is taken: keys >= prefix
+      T_out = prefix - 1u;
+      need_out = 0;
+      return;
+    }
+  }
+  T_out = prefix;
+  need_out = remaining;
+}
+
+// number of set bits of m below this lane, plus acc
+__device__ __forceinline__ int lanes_below(uint64_t m, int acc) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)acc));
+}
+
+// Ordered take of the keys chosen by (T, need): slot q of thread t is the work-group's
+// element q * kTopkThreads + t, so element order is (q, wave, lane); per (q, wave) ballots
+// give each kept key its rank.  EMIT(slot, q) for each kept key.  Two barriers.
+template <int PER, typename EmitFn>
+__device__ void take_reg(const uint32_t (&key)[PER], uint32_t T, int need, RadixShared& sh, EmitFn EMIT) {
+  static_assert(PER * kTopkWaves % 64 == 0, "whole lanes of counts");
+  static_assert(PER <= 64, "lane q publishes slot q's counts");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t gtm[PER], eqm[PER];
+  int mine = 0;                                    // lane q: packed (eq, gt) counts of slot q
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    gtm[q] = __builtin_amdgcn_ballot_w64(key[q] > T);
+    eqm[q] = need > 0 ? __builtin_amdgcn_ballot_w64(key[q] == T) : 0ull;
+    const int packed = (__builtin_popcountll(eqm[q]) << 16) | __builtin_popcountll(gtm[q]);
+    mine = lane == q ? packed : mine;
+  }
+  if (lane < PER) sh.cnt[lane * kTopkWaves + wave] = mine;
+  __syncthreads();
+  if (wave == 0) {                                 // exclusive scan of the packed counts
+    constexpr int E = PER * kTopkWaves / 64;
+    int c[E], sum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      c[e] = sh.cnt[lane * E + e];
+      sum += c[e];
+    }
+    int run = wave_sum_incl(sum) - sum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sh.cnt[lane * E + e] = run;
+      run += c[e];
+    }
+  }
+  __syncthreads();
+  int slot[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {                  // slot of each kept key, -1 if not kept
+    const int base = __builtin_amdgcn_readfirstlane(sh.cnt[q * kTopkWaves + wave]);
+    const int gb = lanes_below(gtm[q], base & 0xffff);
+    if (eqm[q] == 0) {                             // no key == T in this wave's slot q
+      slot[q] = key[q] > T ? gb + min(need, base >> 16) : -1;
+    } else {
+      const int eb = lanes_below(eqm[q], base >> 16);
+      slot[q] = key[q] > T ? gb + min(need, eb) : ((key[q] == T && eb < need) ? gb + eb : -1);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if (slot[q] >= 0) EMIT(slot[q], q);
+}
+
 struct TopkArgs {
   const float* scores;
   int64_t stride;
   const int32_t* seq_lens;
   int Sq, k;
-  int chunk;          // C: positions per stage-1 chunk
-  int max_chunks;     // chunk slots per row in the workspace
-  int cap;            // candidate slots per chunk: min(C, 2k)
+  int max_chunks;     // chunk slots per row
+  int cand_stride;    // candidate slots per row (>= the sum of the r_c)
   uint32_t* xc;       // [rows, max_chunks] cut key of each chunk
-  uint2* cand;        // [rows, max_chunks, cap] (key, position) candidates
+  uint2* cand;        // [rows, cand_stride] (key, position) candidates, position order
   int32_t* idx;
 };
 
+// visible positions of the row, clamped to [0, stride]
 __device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
   const int b = row / a.Sq, t = row % a.Sq;
-  const int n = a.seq_lens[b] - a.Sq + 1 + t;
-  return n < 0 ? 0 : n;
+  const int64_t n = (int64_t)a.seq_lens[b] - a.Sq + 1 + t;
+  return n < 0 ? 0 : (int)(n < a.stride ? n : a.stride);
 }
 
 // candidates kept by a chunk of `len` of the row's `n` positions: twice its share
@@ -208,81 +420,111 @@ __device__ __forceinline__ int chunk_keep(int k, int len, int n) {
   return min(len, 2 * share);
 }
 
-// stage 1, grid (max_chunks, rows): chunk c keeps its r_c best keys (r_c = chunk_keep) as
-// (key, position) candidates in position order; X_c = its r_c-th largest key, so every key
-// it left out is < X_c, or == X_c at a later position.
+// stage 1, grid (max_chunks, rows).  Chunk c's candidates start at c * r_full in the row's
+// list (r_full: the keep of a full chunk; only the last chunk can be shorter).
 __global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
-  extern __shared__ uint32_t skeys[];
-  __shared__ TopkShared sh;
+  __shared__ RadixShared sh;
   const int row = blockIdx.y, c = blockIdx.x;
+  const int lo = c * kChunk;
+  if (lo >= a.stride) return;
+  // the loads are clamped to the row's stride, not its length, so they issue before the
+  // length arrives; positions past the length are masked below
+  const float* src = a.scores + (int64_t)row * a.stride;
+  float v[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) v[q] = src[min((int64_t)(lo + q * kTopkThreads + (int)threadIdx.x), a.stride - 1)];
   const int n = row_len(a, row);
   if (n <= a.k) return;                       // stage 2 writes 0..n-1 directly
-  const int lo = c * a.chunk;
   if (lo >= n) return;
-  const int len = min(a.chunk, n - lo);
+  const int len = min(kChunk, n - lo);
   const int r = chunk_keep(a.k, len, n);
-  const float* src = a.scores + (int64_t)row * a.stride + lo;
-  uint2* out = a.cand + ((int64_t)row * a.max_chunks + c) * a.cap;
-  uint32_t kmin = 0xffffffffu;
-  for (int i0 = 0; i0 < len; i0 += 8 * kTopkThreads) {      // 8 independent loads in flight
-    float v[8];
+  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kChunk, n);
+  uint32_t key[kPer], kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {                 // unconditional (clamped) loads stay in flight together
-      const int i = i0 + q * kTopkThreads + threadIdx.x;
-      v[q] = src[min(i, len - 1)];
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = i0 + q * kTopkThreads + threadIdx.x;
-      if (i < len) {
-        const uint32_t key = float_key(v[q]);
-        skeys[i] = key;
-        kmin = min(kmin, key);
-      }
-    }
+  for (int q = 0; q < kPer; ++q) {                 // empty slots: key 0
+    const bool in = q * kTopkThreads + (int)threadIdx.x < len;
+    key[q] = in ? float_key(v[q]) : 0u;
+    kmin = min(kmin, in ? key[q] : 0xffffffffu);
+    kmax = max(kmax, key[q]);
   }
-  __syncthreads();
+  block_minmax(kmin, kmax, sh);
   uint32_t T;
   if (r >= len) {                              // the whole chunk is kept; X_c = its smallest key
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = kmin;
-    __syncthreads();
-    T = 0xffffffffu;
-    for (int w = 0; w < kTopkWaves; ++w) T = min(T, sh.red[w]);
-    for (int i = threadIdx.x; i < len; i += kTopkThreads) out[i] = make_uint2(skeys[i], (uint32_t)(lo + i));
+    for (int q = 0; q < kPer; ++q) {
+      const int i = q * kTopkThreads + threadIdx.x;
+      if (i < len) out[i] = make_uint2(key[q], (uint32_t)(lo + i));
+    }
+    T = kmin;
   } else {
     int need;
-    radix_select([&](int i) { return skeys[i]; }, len, r, sh, T, need);
-    ordered_take<8>([&](int i) { return skeys[i]; }, len, T, need, r, sh,
-                    [&](int slot, int i, uint32_t key) { out[slot] = make_uint2(key, (uint32_t)(lo + i)); });
+    radix_select_reg<kPer>(key, r, kmin, kmax, sh, T, need);
+    take_reg<kPer>(key, T, need, sh, [&](int slot, int q) {
+      if (slot < r) out[slot] = make_uint2(key[q], (uint32_t)(lo + q * kTopkThreads + (int)threadIdx.x));
+    });
   }
   if (threadIdx.x == 0) a.xc[(int64_t)row * a.max_chunks + c] = T;
 }
 
-// stage 2: one work-group per row.  The chunks' candidates (about 2k, concatenated in
-// chunk order, so in position order) are staged in LDS and the exact select runs there,
-// giving the k-th key T.  The answer is exact if every chunk that left keys out has
-// X_c < T: all keys it left out are then below T.  Otherwise (ties at a chunk's cut, or
-// more than twice a chunk's share in the answer) the row is selected again from its
-// scores: the bound M is the largest X_c such that the chunks whose X is >= X_c hold at
-// least k keys >= it, which makes M a lower bound of the row's k-th key; the row's keys
-// >= M are compacted in position order into LDS and selected exactly; if ties at the
-// bound leave more keys than LDS holds, the select runs over the whole row.
+// Exact select of the k best of the row's n_cand candidates, PER per thread (candidate j =
+// q * kTopkThreads + t in slot q of thread t).  Writes the row's answer and returns true
+// unless a chunk that left keys out (cut_t, cut key x_t, one chunk per thread) could hold
+// part of it: then it returns false, having written nothing.
+template <int PER>
+__device__ bool select_candidates(const uint2 (&cv)[kPer], int n_cand, int k, bool cut_t, uint32_t x_t,
+                                  RadixShared& rs, int32_t* out) {
+  uint32_t key[PER], pos[PER], kmin = 0xffffffffu, kmax = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {                  // empty slots: key 0
+    const bool in = q * kTopkThreads + (int)threadIdx.x < n_cand;
+    key[q] = in ? cv[q].x : 0u;
+    pos[q] = cv[q].y;
+    kmin = min(kmin, in ? key[q] : 0xffffffffu);
+    kmax = max(kmax, key[q]);
+  }
+  block_minmax(kmin, kmax, rs);
+  uint32_t T;
+  int need;
+  radix_select_reg<PER>(key, k, kmin, kmax, rs, T, need);
+  const uint32_t V = need > 0 ? T : T + 1u;       // smallest key the answer may take
+  if (__syncthreads_or(cut_t && !(x_t < V))) return false;
+  take_reg<PER>(key, T, need, rs, [&](int slot, int q) {
+    if (slot < k) out[slot] = (int32_t)pos[q];
+  });
+  return true;
+}
+
+// stage 2: one work-group per row.  The candidates (about 2k, in position order) are held
+// in registers and the exact select over them gives the threshold (T, need); the smallest
+// key the answer may take is V = T, or T + 1 when need = 0.  The answer is exact if every
+// chunk that left keys out has X_c < V: all keys it left out are then below V.  Otherwise
+// (ties at a chunk's cut, or more than twice a chunk's share in the answer) the row is
+// selected again from its scores: the bound M is the largest X_c such that the chunks
+// whose X is >= X_c hold at least k candidates (all of them >= their chunk's X), which
+// makes M a lower bound of the row's k-th key; the row's keys >= M are compacted in
+// position order into LDS and selected exactly; if ties at the bound leave more keys than
+// LDS holds, the select runs over the whole row.
 constexpr int kFiltPer = 16;                       // keys per thread per filter round
-constexpr int kFiltLds = 8192;                     // candidates / filtered keys kept in LDS
+constexpr int kFiltLds = 8192;                     // filtered keys kept in LDS
 static_assert(kFiltPer * kTopkWaves == 256, "the filter scan covers 4 counts per lane of one wave");
 constexpr int kSelectLds = kFiltLds * 2;           // 32-bit words of dynamic LDS: keys + positions
-constexpr int kMaxChunks = 64;                     // chunks one wave combines
 __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   extern __shared__ uint32_t fl[];                 // [kFiltLds] keys, then [kFiltLds] positions
-  __shared__ TopkShared sh;
+  __shared__ RadixShared rs;
+  __shared__ TopkShared<kTopkThreads> sh;
+  __shared__ uint32_t xs[kMaxChunks];
+  __shared__ int rsz[kMaxChunks];
   __shared__ uint32_t m_sh;
-  __shared__ int ok_sh;
-  __shared__ int coff[kMaxChunks + 1];
   __shared__ int fcnt[kFiltPer * kTopkWaves];
   __shared__ int ftot;
   const int row = blockIdx.x;
+  // the row's candidate slots and cut keys are loaded before its length arrives (clamped
+  // to the row's workspace; slots past the row's count are masked below)
+  const uint2* cr = a.cand + (int64_t)row * a.cand_stride;
+  uint2 cv[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) cv[q] = cr[min(q * kTopkThreads + (int)threadIdx.x, a.cand_stride - 1)];
+  const uint32_t x_ld = a.xc[(int64_t)row * a.max_chunks + min((int)threadIdx.x, a.max_chunks - 1)];
   const int n = row_len(a, row);
   int32_t* out = a.idx + (int64_t)row * a.k;
   if (n <= a.k) {
@@ -290,82 +532,40 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
     return;
   }
   const float* src = a.scores + (int64_t)row * a.stride;
-  const int nch = (n + a.chunk - 1) / a.chunk;
+  const int nch = (n + kChunk - 1) / kChunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r_full = chunk_keep(a.k, kChunk, n);
+  const int n_cand = (nch - 1) * r_full + chunk_keep(a.k, n - (nch - 1) * kChunk, n);
+  // thread t < nch: chunk t's cut key, keep, and whether it left keys out
+  uint32_t x_t = 0;
+  int r_t = 0;
+  bool cut_t = false;
+  if ((int)threadIdx.x < nch) {
+    const int len_t = min(kChunk, n - (int)threadIdx.x * kChunk);
+    x_t = x_ld;
+    r_t = chunk_keep(a.k, len_t, n);
+    cut_t = r_t < len_t;
+    xs[threadIdx.x] = x_t;
+    rsz[threadIdx.x] = r_t;
+  }
   uint32_t* fkey = fl;
   uint32_t* fpos = fl + kFiltLds;
-  uint32_t xj = 0;                                 // wave 0, lane j < nch: X_j
-  int rj = 0, lenj = 0;
-  if (wave == 0) {
-    if (lane < nch) {
-      xj = a.xc[(int64_t)row * a.max_chunks + lane];
-      lenj = min(a.chunk, n - lane * a.chunk);
-      rj = chunk_keep(a.k, lenj, n);
-    }
-    int incl = rj;                                 // candidate offsets of the chunks
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane < nch) coff[lane] = incl - rj;
-    if (lane == nch - 1) coff[nch] = incl;
-  }
-  __syncthreads();
-  const int n_cand = coff[nch];
   uint32_t T;
   int need;
-  if (n_cand <= kFiltLds) {
-    // stage the candidates: slot j belongs to the last chunk whose offset is <= j
-    for (int j0 = 0; j0 < n_cand; j0 += 4 * kTopkThreads) {
-      uint2 v[4];
-      int jj[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = min(j0 + q * kTopkThreads + (int)threadIdx.x, n_cand - 1);
-        int lo = 0, hi = nch - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (coff[mid] <= j) lo = mid; else hi = mid - 1;
-        }
-        jj[q] = j;
-        v[q] = a.cand[((int64_t)row * a.max_chunks + lo) * a.cap + (j - coff[lo])];
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (j0 + q * kTopkThreads + (int)threadIdx.x < n_cand) {
-          fkey[jj[q]] = v[q].x;
-          fpos[jj[q]] = v[q].y;
-        }
-      }
-    }
-    __syncthreads();
-    radix_select([&](int j) { return fkey[j]; }, n_cand, a.k, sh, T, need);
-    if (wave == 0) {
-      const bool bad = lane < nch && rj < lenj && !(xj < T);
-      const uint64_t any_bad = __builtin_amdgcn_ballot_w64(bad);
-      if (lane == 0) ok_sh = (any_bad == 0);
-    }
-    __syncthreads();
-    if (ok_sh) {
-      ordered_take<4>([&](int j) { return fkey[j]; }, n_cand, T, need, a.k, sh,
-                      [&](int slot, int j, uint32_t) { out[slot] = (int32_t)fpos[j]; });
-      return;
-    }
+  if (n_cand <= kTopkThreads * 4) {
+    if (select_candidates<4>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
+  } else if (n_cand <= kMaxCand) {
+    if (select_candidates<kPer>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
   }
   // ---- select again from the row's scores
-  if (wave == 0) {
-    // lane j tests X_j as the bound: keys guaranteed >= X_j = sum of r_c over X_c >= X_j
+  if (threadIdx.x == 0) m_sh = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < nch) {
+    // keys guaranteed >= X_t: the candidates of every chunk whose X is >= X_t
     int64_t guaranteed = 0;
-    for (int c = 0; c < nch; ++c) {
-      const uint32_t x = (uint32_t)__shfl((int)xj, c);
-      const int r = __shfl(rj, c);
-      if (x >= xj) guaranteed += r;
-    }
-    uint32_t m = (lane < nch && guaranteed >= a.k) ? xj : 0u;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    if (lane == 0) m_sh = m;
+    for (int c = 0; c < nch; ++c)
+      if (xs[c] >= x_t) guaranteed += rsz[c];
+    if (guaranteed >= a.k) atomicMax(&m_sh, x_t);
   }
   __syncthreads();
   const uint32_t M = m_sh;
@@ -429,33 +629,29 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
       for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < n_f) ? (int32_t)fpos[i] : -1;
       return;
     }
-    radix_select([&](int j) { return fkey[j]; }, n_f, a.k, sh, T, need);
-    ordered_take<4>([&](int j) { return fkey[j]; }, n_f, T, need, a.k, sh,
+    radix_select<kTopkThreads>([&](int j) { return fkey[j]; }, n_f, a.k, sh, T, need);
+    ordered_take<kTopkThreads, 4>([&](int j) { return fkey[j]; }, n_f, T, need, a.k, sh,
                     [&](int slot, int j, uint32_t) { out[slot] = (int32_t)fpos[j]; });
   } else {                                         // many keys tie at the bound: select over the whole row
-    radix_select([&](int i) { return float_key(src[i]); }, n, a.k, sh, T, need);
-    ordered_take<4>([&](int i) { return float_key(src[i]); }, n, T, need, a.k, sh,
+    radix_select<kTopkThreads>([&](int i) { return float_key(src[i]); }, n, a.k, sh, T, need);
+    ordered_take<kTopkThreads, 4>([&](int i) { return float_key(src[i]); }, n, T, need, a.k, sh,
                     [&](int slot, int i, uint32_t) { out[slot] = i; });
   }
 }
 
-static void topk_geometry(int64_t stride, int k, int& chunk, int& max_chunks, int& cap) {
-  // about kTargetChunks chunks of the longest row, at most 128 KB of keys each
-  int64_t c = (stride + kTargetChunks - 1) / kTargetChunks;
-  c = (c + 1023) / 1024 * 1024;
-  if (c > kMaxChunkElems) c = kMaxChunkElems;
-  chunk = (int)c;
-  max_chunks = (int)((stride + c - 1) / c);
-  cap = (int)std::min<int64_t>(c, 2 * (int64_t)k);
+static void topk_geometry(int64_t stride, int k, int& max_chunks, int& cand_stride) {
+  max_chunks = (int)((stride + kChunk - 1) / kChunk);
+  // sum over chunks of min(len_c, 2 ceil(k len_c / n)) <= min(n, 2k + 2 * chunks)
+  cand_stride = (int)std::min<int64_t>(stride, 2 * (int64_t)k + 2 * (int64_t)max_chunks);
 }
 
 }  // namespace dsa
 
 extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
   if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
-  int chunk, max_chunks, cap;
-  dsa::topk_geometry(score_stride, k, chunk, max_chunks, cap);
-  return (size_t)B * Sq * max_chunks * ((size_t)cap * sizeof(uint2) + sizeof(uint32_t));
+  int max_chunks, cand_stride;
+  dsa::topk_geometry(score_stride, k, max_chunks, cand_stride);
+  return (size_t)B * Sq * ((size_t)cand_stride * sizeof(uint2) + (size_t)max_chunks * sizeof(uint32_t));
 }
 
 extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int Sq,
@@ -467,14 +663,15 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   DSA_CHECK_ARG(score_stride >= 1 && score_stride < ((int64_t)1 << 31), "dsa_topk: bad score_stride");
   DSA_CHECK_SUPPORTED(k <= 8192, "dsa_topk: k > 8192");
   DSA_CHECK_ARG((int64_t)B * Sq <= 65535, "dsa_topk: more than 65535 rows");
+  DSA_CHECK_SUPPORTED(score_stride <= (int64_t)kMaxChunks * kChunk, "dsa_topk: score_stride above %d",
+                      kMaxChunks * kChunk);
   TopkArgs a{};
   a.scores = scores;
   a.stride = score_stride;
   a.seq_lens = seq_lens;
   a.Sq = Sq;
   a.k = k;
-  topk_geometry(score_stride, k, a.chunk, a.max_chunks, a.cap);
-  DSA_CHECK_SUPPORTED(a.max_chunks <= kMaxChunks, "dsa_topk: score_stride above %d", kMaxChunks * kMaxChunkElems);
+  topk_geometry(score_stride, k, a.max_chunks, a.cand_stride);
   const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
   if (ws == nullptr || ws_bytes < need) {
     set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
@@ -483,18 +680,15 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   DSA_CHECK_ARG(((uintptr_t)ws & 7) == 0, "dsa_topk: workspace not 8-byte aligned");
   const size_t rows = (size_t)B * Sq;
   a.cand = static_cast<uint2*>(ws);
-  a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.max_chunks * a.cap);
+  a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.cand_stride);
   a.idx = idx;
-  const size_t lds = (size_t)a.chunk * sizeof(uint32_t);
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)(kMaxChunkElems * sizeof(uint32_t)));
     hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)(kSelectLds * sizeof(uint32_t)));
     attr = true;
   }
-  DSA_LAUNCH(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), lds, stream, a);
+  DSA_LAUNCH(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
   dsa_status_t st = launch_status("dsa_topk(chunk)");
   if (st != DSA_OK) return st;
   DSA_LAUNCH(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);

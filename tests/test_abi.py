@@ -42,7 +42,7 @@ def test_invalid_arguments_rejected_without_device():
                       None) == _lib.DSA_ERR_UNSUPPORTED
     assert L.dsa_topk(ctypes.c_void_p(16), 100000, ctypes.c_void_p(16), 2, 1, 2048, ctypes.c_void_p(16), None, 0,
                       None) == _lib.DSA_ERR_WORKSPACE
-    assert L.dsa_topk_workspace_size(32, 1, 2048, 65536) == 32 * 8 * (4096 * 8 + 4)
+    assert L.dsa_topk_workspace_size(32, 1, 2048, 65536) == 32 * (4112 * 8 + 8 * 4)
     assert L.dsa_page_translate(None, 10, 0, 4, None, None, None, None) == _lib.DSA_ERR_INVALID_ARG
     assert L.dsa_plan(None, 1, 1, 8, None, None, None, 4, 2, 10, None, None, None, None, None, 1, None,
                       None) == _lib.DSA_ERR_INVALID_ARG

@@ -154,10 +154,16 @@ def _topk_cases():
     cases.append((x, 2048))
     cases.append((-np.abs(rng.standard_normal(40000)).astype(np.float32), 1))
     cases.append((rng.standard_normal(33000).astype(np.float32) * np.float32(1e30), 8192))
+    # ascending scores: the whole answer sits in the last chunk, far above its share
+    cases.append((np.sort(rng.standard_normal(65536)).astype(np.float32), 2048))
+    # one position past a chunk boundary; a large k near the register capacity
+    cases.append((rng.standard_normal(8193).astype(np.float32), 4000))
+    # more candidates than one work-group holds: the re-select over the row
+    cases.append((rng.standard_normal(300000).astype(np.float32), 8192))
     return cases
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(13))
 def test_topk_standalone_bit_exact(case):
     s, k = _topk_cases()[case]
     n = len(s)
@@ -169,8 +175,8 @@ def test_topk_standalone_bit_exact(case):
 
 def test_topk_batched_mtp_rows():
     rng = np.random.default_rng(3)
-    B, Sq, Lmax, k = 3, 4, 5000, 512
-    lens = np.array([5000, 600, 515], dtype=np.int32)
+    B, Sq, Lmax, k = 5, 4, 16390, 512
+    lens = np.array([5000, 600, 515, 8195, 16390], dtype=np.int32)
     s = rng.integers(0, 200, (B, Sq, Lmax)).astype(np.float32)
     idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
     dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
