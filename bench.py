@@ -66,8 +66,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.j
 # entry point -> (kernel name prefixes in rocprofv3 output, sources the kernels are built from)
 ENTRY_KERNELS = {
     "indexer": (["void dsa::indexer_mfma_kernel<false, 2, 1, 1>"], ["indexer.hip"]),
-    "topk": (["dsa::topk_bound_kernel", "dsa::topk_select_kernel"], ["topk.hip"]),
-    "mla": (["void dsa::mla_decode_kernel<2>", "dsa::mla_merge_kernel"], ["mla.hip"]),
+    "topk": (["dsa::topk_chunk_kernel", "dsa::topk_select_kernel"], ["topk.hip"]),
+    "mla": (["void dsa::mla_decode_kernel<", "dsa::mla_merge_kernel"], ["mla.hip"]),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0   # counter KiB -> bytes/1024, from a 256 MiB device copy
 

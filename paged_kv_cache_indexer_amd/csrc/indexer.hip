@@ -90,13 +90,14 @@ struct MfmaArgs {
 // token tile (each covers NQ of the Sq queries).  MT_W = HMT * NQ M tiles per wave.
 //
 // Work is cut into units of up to `ut` tiles inside one request.  A wave loads the
-// request's queries once per unit, then streams the unit's tiles through three fixed
-// register slots (two tiles in flight behind the one being computed).  Every fetch is
+// request's queries once per unit, then streams the unit's tiles through kSlots fixed
+// register slots (kSlots - 1 tiles in flight behind the one being computed).  Every fetch is
 // issued unconditionally (past the unit's end it re-reads the last tile, an L2 hit), and
 // the page lookup is a scalar load, so the steady-state loop never waits on more than
 // the tile it is about to use.  The unit size is derived on the device from the total
 // tile count so that the units fill the grid's wave slots in one round.
 constexpr int kPrefixPerThread = (kMaxB + 255) / 256;
+constexpr int kSlots = 3;      // register slots per wave: kSlots - 1 tiles in flight behind the one computed
 
 // unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; returns ut
 __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int* unit_off, int* wsum) {
@@ -132,8 +133,8 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   int total_tiles = 0;
   block_scan(mine, total_tiles);
   int ut = (total_tiles + wave_slots - 1) / wave_slots;
-  ut = ((ut + 2) / 3) * 3;                        // whole passes over the three slots
-  if (ut < 3) ut = 3;
+  ut = ((ut + kSlots - 1) / kSlots) * kSlots;     // whole passes over the register slots
+  if (ut < kSlots) ut = kSlots;
   int units[kPrefixPerThread];
   int my_units = 0;
 #pragma unroll
@@ -250,10 +251,9 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
     }
     // tile prefetches go out after the query loads, so the loop below is entered with the
     // same outstanding-load order as its back edge (no full drain at the loop header)
-    Slot A, Bs, C;
-    fetch(A, t_begin);
-    fetch(Bs, t_begin + 1);
-    fetch(C, t_begin + 2);
+    Slot sl[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) fetch(sl[k], t_begin + k);
 #pragma unroll
     for (int r = 0; r < (MT_W * 32 + 63) / 64; ++r) {
       const int i = lane + 64 * r;
@@ -319,15 +319,14 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
       if (live && !cur.valid && lane == 0 && rg == 0) count_error(a.err);
     };
 
-    // fixed-shape body: no exit between the three fetches (tiles past the unit's end are
-    // computed from the clamped tile and not stored)
-    for (int t = t_begin; t < t_end; t += 3) {
-      compute(A, t, true);
-      fetch(A, t + 3);
-      compute(Bs, t + 1, t + 1 < t_end);
-      fetch(Bs, t + 4);
-      compute(C, t + 2, t + 2 < t_end);
-      fetch(C, t + 5);
+    // fixed-shape body: no exit between the fetches (tiles past the unit's end are computed
+    // from the clamped tile and not stored)
+    for (int t = t_begin; t < t_end; t += kSlots) {
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        compute(sl[k], t + k, k == 0 || t + k < t_end);
+        fetch(sl[k], t + k + kSlots);
+      }
     }
   }
 }
