@@ -93,11 +93,12 @@ struct MfmaArgs {
 // request's queries once per unit, then streams the unit's tiles through kSlots fixed
 // register slots (kSlots - 1 tiles in flight behind the one being computed).  Every fetch is
 // issued unconditionally (past the unit's end it re-reads the last tile, an L2 hit), and
-// the page lookup is a scalar load, so the steady-state loop never waits on more than
-// the tile it is about to use.  The unit size is derived on the device from the total
+// the unit's page lookups are done once, one tile per lane, so the steady-state loop never
+// waits on more than the tile it is about to use.  The unit size is derived on the device from the total
 // tile count so that the units fill the grid's wave slots in one round.
 constexpr int kPrefixPerThread = (kMaxB + 255) / 256;
 constexpr int kSlots = 3;      // register slots per wave: kSlots - 1 tiles in flight behind the one computed
+constexpr int kMaxUnit = (64 / kSlots) * kSlots;   // tiles per unit: at most one per lane
 
 // unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; returns ut
 __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int* unit_off, int* wsum) {
@@ -135,6 +136,7 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   int ut = (total_tiles + wave_slots - 1) / wave_slots;
   ut = ((ut + kSlots - 1) / kSlots) * kSlots;     // whole passes over the register slots
   if (ut < kSlots) ut = kSlots;
+  if (ut > kMaxUnit) ut = kMaxUnit;               // a unit's tile rows fit one per lane
   int units[kPrefixPerThread];
   int my_units = 0;
 #pragma unroll
@@ -155,6 +157,13 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   return ut;
 }
 
+// max(x, 0) as a signed-integer max of the bits: a float with the sign bit set (including
+// -0.0) is a negative integer and becomes +0.0; one instruction, where fmaxf would first
+// quiet its NaN operand
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 template <bool QFP8, int HMT, int NQ, int RG>
 __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   constexpr int MT_W = HMT * NQ;
@@ -171,6 +180,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   const int n = lane & 31;                         // token within tile / row within M tile
   const int g = lane >> 5;                         // lane group
   const int ps = a.keys.page_size;
+  const int tpp = ps / kTile;                       // tiles per page (ps % 32 == 0 on this path)
+  const int tpp_shift = (tpp > 0 && (tpp & (tpp - 1)) == 0) ? __builtin_ctz(tpp) : -1;
 
   __shared__ int scan_wsum[4];
   const int ut = __builtin_amdgcn_readfirstlane(indexer_units(a.seq_lens, a.B, gridDim.x * WPU, unit_off, scan_wsum));
@@ -201,20 +212,34 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
     const int t_begin = (u - __builtin_amdgcn_readfirstlane(unit_off[b])) * ut;
     const int t_end = min(t_begin + ut, n_tiles_b);
 
+    // first key row of each tile of the unit, one tile per lane (-1: its page is missing or
+    // out of range); a fetch reads its tile's row back with readlane, so no memory wait sits
+    // between a tile's LDS re-layout and the refill of its slot
+    int64_t my_row = -1;
+    {
+      const int t = t_begin + lane;
+      if (t < t_end) {
+        const int s0 = t * kTile;                  // positions fit in 31 bits
+        int64_t r0 = -1;
+        if (a.keys.page_table) {
+          const int lp = tpp_shift >= 0 ? (t >> tpp_shift) : t / tpp;
+          if (lp < a.keys.pt_stride) {
+            const int32_t pg = a.keys.page_table[(int64_t)b * a.keys.pt_stride + lp];
+            if (pg >= 0) r0 = (int64_t)pg * ps + (s0 - lp * ps);
+          }
+        } else if (a.keys.req_stride <= 0 || s0 < a.keys.req_stride) {
+          r0 = (int64_t)b * a.keys.req_stride + s0;
+        }
+        my_row = (r0 >= 0 && r0 + kTile <= a.keys.num_rows) ? r0 : -1;
+      }
+    }
+    const int row_lo = (int)(uint32_t)my_row, row_hi = (int)(my_row >> 32);
     auto fetch = [&](Slot& sl, int t) {
       t = min(t, t_end - 1);
-      const int64_t s0 = (int64_t)t * kTile;
-      int64_t r0 = -1;
-      if (a.keys.page_table) {
-        const int64_t lp = s0 / ps;
-        if (lp < a.keys.pt_stride) {
-          const int32_t pg = scalar_load(a.keys.page_table + (int64_t)b * a.keys.pt_stride + lp);
-          if (pg >= 0) r0 = (int64_t)pg * ps + (s0 - lp * ps);
-        }
-      } else if (a.keys.req_stride <= 0 || s0 < a.keys.req_stride) {
-        r0 = (int64_t)b * a.keys.req_stride + s0;
-      }
-      sl.valid = r0 >= 0 && r0 + kTile <= a.keys.num_rows;
+      const int i = t - t_begin;                   // < kMaxUnit <= 64
+      const int64_t r0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, i) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane(row_lo, i));
+      sl.valid = r0 >= 0;
       const int64_t r = (sl.valid ? r0 : 0) + n;
       const char* kp = a.keys.base + (sl.valid ? r0 : 0) * 128 + lane * 16;
 #pragma unroll
@@ -260,12 +285,17 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
       if (i < MT_W * 32) wsm[wave][i] = wreg[r];
     }
 
-    auto compute = [&](const Slot& cur, int t, bool live) {
+    // compute tile t from slot `cur`; once its bytes are in the LDS re-layout buffer the
+    // slot is refilled with tile t_next, so that load is in flight during this tile's MFMAs
+    auto compute = [&](Slot& cur, int t, bool live, int t_next) {
       // re-lay the tile: load c of lane i holds row 8c + i/8, bytes 16*(i%8) .. +16
       char* st = kstage[wave];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<u32x4*>(st + (c * 8 + (lane >> 3)) * kStageStride + (lane & 7) * 16) = cur.kb[c];
+      const float sig = cur.sig;
+      const bool valid = cur.valid;
+      fetch(cur, t_next);
       u32x4 kb[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const u32x4*>(st + n * kStageStride + g * 64 + c * 16);
@@ -303,30 +333,27 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const f32x4 wv = *reinterpret_cast<const f32x4*>(&wsm[wave][mt * 32 + i4 * 8 + g * 4]);
-            part = fmaf(wv.x, fmaxf(acc[mt][i4 * 4 + 0], 0.0f), part);
-            part = fmaf(wv.y, fmaxf(acc[mt][i4 * 4 + 1], 0.0f), part);
-            part = fmaf(wv.z, fmaxf(acc[mt][i4 * 4 + 2], 0.0f), part);
-            part = fmaf(wv.w, fmaxf(acc[mt][i4 * 4 + 3], 0.0f), part);
+            part = fmaf(wv.x, relu(acc[mt][i4 * 4 + 0]), part);
+            part = fmaf(wv.y, relu(acc[mt][i4 * 4 + 1]), part);
+            part = fmaf(wv.z, relu(acc[mt][i4 * 4 + 2]), part);
+            part = fmaf(wv.w, relu(acc[mt][i4 * 4 + 3]), part);
           }
         }
         part += __shfl_xor(part, 32);
         const int tq = rg * NQ + qq;
         const int vis = L - a.Sq + 1 + tq;
-        float v = a.k_scale ? part * cur.sig : part;
-        if (!cur.valid || s >= vis) v = -INFINITY;
+        float v = a.k_scale ? part * sig : part;
+        if (!valid || s >= vis) v = -INFINITY;
         if (live && g == 0 && s < L) a.scores[((int64_t)b * a.Sq + tq) * a.score_stride + s] = v;
       }
-      if (live && !cur.valid && lane == 0 && rg == 0) count_error(a.err);
+      if (live && !valid && lane == 0 && rg == 0) count_error(a.err);
     };
 
     // fixed-shape body: no exit between the fetches (tiles past the unit's end are computed
     // from the clamped tile and not stored)
     for (int t = t_begin; t < t_end; t += kSlots) {
 #pragma unroll
-      for (int k = 0; k < kSlots; ++k) {
-        compute(sl[k], t + k, k == 0 || t + k < t_end);
-        fetch(sl[k], t + k + kSlots);
-      }
+      for (int k = 0; k < kSlots; ++k) compute(sl[k], t + k, k == 0 || t + k < t_end, t + k + kSlots);
     }
   }
 }
