@@ -1,9 +1,10 @@
-"""Storage-format decoding for the oracle (test infrastructure only).
+"""Storage-format decoding and encoding for the oracle (test infrastructure only).
 
 bf16 is the upper half of an IEEE binary32; OCP FP8 E4M3FN has 1 sign bit, 4
 exponent bits (bias 7) and 3 mantissa bits, no infinities, and the all-ones
 exponent+mantissa pattern as NaN (largest finite value 448).  Both decoders are
-written from those definitions by bit manipulation.
+written from those definitions by bit manipulation; the e4m3 encoder picks the
+nearest finite value from the decoded code table.
 """
 import numpy as np
 
@@ -38,3 +39,24 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     r = np.rint(m * 256.0) / 256.0           # 8 significant bits, ties to even
     y = np.ldexp(r, e).astype(np.float32)    # exact: 8 bits fit in binary32
     return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# the 127 non-negative finite e4m3 values, ascending with their codes 0x00..0x7E
+_E4M3_POS = None
+
+
+def f64_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float64 -> OCP E4M3FN codes: the nearest finite e4m3 value, ties to the even code
+    (even mantissa), magnitudes above 448 saturated to 448.  -0.0 encodes as 0x80."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    x = np.asarray(x, dtype=np.float64)
+    assert np.isfinite(x).all()
+    a = np.minimum(np.abs(x), _E4M3_POS[-1])
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
