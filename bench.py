@@ -130,6 +130,9 @@ def main():
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter files and exit")
+    ap.add_argument("--entry", choices=["step", "kv_write"], default="step",
+                    help="kv_write: time dsa_kv_write alone (the new tokens of a decode step) and print "
+                         "its own line instead of the step's")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
@@ -144,6 +147,9 @@ def main():
     from tests.dsa_dev import DevWorkload, DecodeStep, HipMark
 
     torch.cuda.set_device(0)
+    if args.entry == "kv_write":
+        bench_kv_write(args)
+        return
     wl = synth.make_workload(2)
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
@@ -235,6 +241,46 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_kv_write(args):
+    """dsa_kv_write for the decode batch (B=32, one new token) and an MTP batch (B=8, four
+    new tokens): 64-token pages spread over a 64K-position cache, bf16 latent rows and keys."""
+    import torch
+    import paged_kv_cache_indexer_amd as dsa
+    from tests.dsa_dev import HipMark
+    res = []
+    for B, Sq in ((32, 1), (8, 4)):
+        ps, L, D = 64, 65536, 128
+        P = L // ps
+        g = torch.Generator(device="cpu").manual_seed(7)
+        pt = torch.randperm(B * P, generator=g).to(torch.int32).view(B, P).cuda()
+        kv = torch.zeros(B * L, 576, dtype=torch.bfloat16, device="cuda")
+        ic = torch.zeros(B * L, D, dtype=torch.uint8, device="cuda")
+        isc = torch.zeros(B * L, dtype=torch.float32, device="cuda")
+        lat = torch.randn(B, Sq, 576, generator=g).to(torch.bfloat16).cuda()
+        keys = torch.randn(B, Sq, D, generator=g).to(torch.bfloat16).cuda()
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        kvr, icr = dsa.Rows(kv, 1152, pt, ps), dsa.Rows(ic, D, pt, ps)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream)
+            torch.cuda.synchronize()
+            e0, e1 = HipMark(), HipMark()
+            e0.record(stream)
+            for _ in range(args.steps):
+                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        us = e0.elapsed_ms(e1) / args.steps * 1e3
+        by = B * Sq * (1152 + 2 * D + 1152 + D + 4)     # read latent + key, write row + codes + scale
+        res.append({"batch": B, "new_tokens": Sq, "us_per_call": us, "algo_bytes": by, "GBps": by / us / 1e3})
+    print(json.dumps({"metric": "dsa_kv_write us per call (back-to-back launches, HIP events)",
+                      "entry": "dsa_kv_write", "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "runs": res, "bound": "launch latency (a few KB per call)"}), flush=True)
 
 
 if __name__ == "__main__":

@@ -13,6 +13,8 @@
  *   dsa_gather_kv          per-layer serve (pool / paged / host rows) and install  [GLM52] §4.4, §5
  *   dsa_sparse_mla_decode  MLA latent attention over the selected rows only        [TSA] "MLA", [GLM52] §2.1
  *   dsa_page_translate     page-sharded ownership closed form                      [HCCP] §1.1
+ *   dsa_kv_write           new tokens' latent rows and e4m3 indexer keys into the
+ *                          paged caches (fused quantise + scatter)                 [TSA] "KV host tiering"
  *
  * Conventions shared by every call
  *   - Pointers are device pointers owned by the caller, unless stated otherwise.  The
@@ -248,6 +250,34 @@ dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_
 dsa_status_t dsa_page_translate(const int64_t* x, int64_t n, int page_size, int n_ranks,
                                 int32_t* rank, int64_t* local_row, int32_t* err_count,
                                 hipStream_t stream);
+
+/*
+ * dsa_kv_write — the KV write path of a decode step: quantise and scatter the new tokens
+ * into the paged caches in one launch ([TSA] "Attention integration / KV host tiering":
+ * the fused KV-pack kernel; [TSA] "MLA": one 576-wide latent row per token; [GLM52] §2.1:
+ * fp8 indexer keys).  The Sq new tokens of request b sit at its last Sq positions,
+ * p = seq_lens[b] - Sq + t (seq_lens counts them already).  For each:
+ *     kv row of (b, p)        = latent[b, t, :]                  (bf16, copied bit for bit)
+ *     sigma                   = max_d |idx_k[b, t, d]| / 448      (float32 division)
+ *     idx_cache row of (b, p) = e4m3(idx_k[b, t, d] / sigma)     (float32 division, nearest
+ *                               OCP E4M3FN value, ties to even, saturating at 448)
+ *     idx_scale[that row]     = sigma
+ * A zero key stores sigma = 0 and zero codes (it dequantises to 0).  The pages do not fix
+ * the key quantisation; this is the per-token-scale layout dsa_indexer_scores reads.
+ *
+ *   latent      [B, Sq, 576] bf16, 16-byte aligned
+ *   idx_k       [B, Sq, D] bf16 or float32 (idx_k_dtype), 8-byte aligned; D even, <= 128
+ *   kv          rows of the latent cache (row_bytes 1152, base 16-byte aligned), written
+ *   idx_cache   rows of the indexer cache (row_bytes D, base 2-byte aligned), written; it may
+ *               use its own page table
+ *   idx_scale   [idx_cache rows] float32, written at each written row
+ * A token whose position or page is out of range in either cache is skipped and counted
+ * in err_count.  Two tokens mapping to the same row race (the caller's pages are distinct).
+ */
+dsa_status_t dsa_kv_write(const void* latent, const void* idx_k, dsa_dtype_t idx_k_dtype,
+                          const int32_t* seq_lens, int B, int Sq, int D, const dsa_rows_t* kv,
+                          const dsa_rows_t* idx_cache, float* idx_scale, int32_t* err_count,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

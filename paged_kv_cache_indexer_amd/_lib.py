@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED
 
 EXPORTED = ["dsa_version", "dsa_last_error", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
             "dsa_plan", "dsa_gather_kv", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_page_translate"]
+            "dsa_page_translate", "dsa_kv_write"]
 
 
 class dsa_rows_t(ctypes.Structure):
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
                                                  ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, sz, vp,
                                                  vp]),
         "dsa_page_translate": (ctypes.c_int, [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]),
+        "dsa_kv_write": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, prow,
+                                        prow, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -141,3 +141,12 @@ def dsa_page_translate(x: torch.Tensor, page_size: int, n_ranks: int, rank: torc
                        err: Optional[torch.Tensor] = None, stream=None):
     _check(_lib.load().dsa_page_translate(_ptr(x), x.numel(), page_size, n_ranks, _ptr(rank), _ptr(local_row),
                                           _ptr(err), _stream(stream)), "dsa_page_translate")
+
+
+def dsa_kv_write(latent: torch.Tensor, idx_k: torch.Tensor, seq_lens: torch.Tensor, kv: Rows, idx_cache: Rows,
+                 idx_scale: torch.Tensor, err: Optional[torch.Tensor] = None, stream=None):
+    """Quantise and scatter the new tokens ([B, Sq, 576] latent, [B, Sq, D] keys) into the caches."""
+    B, Sq, D = idx_k.shape
+    _check(_lib.load().dsa_kv_write(_ptr(latent), _ptr(idx_k), _dtype_code(idx_k), _ptr(seq_lens), B, Sq, D,
+                                    kv.ref(), idx_cache.ref(), _ptr(idx_scale), _ptr(err), _stream(stream)),
+           "dsa_kv_write")

@@ -55,5 +55,15 @@ def test_invalid_arguments_rejected_without_device():
                                    None, 0, None, None) == _lib.DSA_ERR_INVALID_ARG
     assert L.dsa_gather_kv(ctypes.c_void_p(16), None, None, 1, 1, 4, None, None, 0, 100, ctypes.c_void_p(16), 0,
                            None, None) == _lib.DSA_ERR_INVALID_ARG
+    kv, ic = _lib.dsa_rows_t(), _lib.dsa_rows_t()
+    kv.base, kv.row_bytes, ic.base, ic.row_bytes = 16, 1152, 16, 128
+    p = ctypes.c_void_p(16)
+    assert L.dsa_kv_write(p, p, _lib.DSA_E4M3, p, 1, 1, 128, ctypes.byref(kv), ctypes.byref(ic), p, None,
+                          None) == _lib.DSA_ERR_INVALID_ARG          # keys must be bf16 or fp32
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 130, ctypes.byref(kv), ctypes.byref(ic), p, None,
+                          None) == _lib.DSA_ERR_UNSUPPORTED          # D > 128
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 64, ctypes.byref(kv), ctypes.byref(ic), p, None,
+                          None) == _lib.DSA_ERR_INVALID_ARG          # indexer rows must be D bytes
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 0, 1, 128, None, None, None, None, None) == _lib.DSA_OK
     # empty batches are valid no-ops
     assert L.dsa_topk(None, 1, None, 0, 1, 8, None, None, 0, None) == _lib.DSA_OK
