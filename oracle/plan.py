@@ -100,3 +100,54 @@ def plan_step(topk: np.ndarray, pool_ids: np.ndarray, id_to_slot: np.ndarray, pt
 def empty_state(n_sets: int, ways: int, id_range: int):
     return (np.full(n_sets * ways, -1, np.int32), np.full(id_range, -1, np.int32),
             np.zeros(n_sets, np.int32))
+
+
+# --------------------------------------------------------------------------------------
+# Replacement-policy comparison ([GLM52] §3: an 8192-entry device pool under LRU raises the
+# average hit rate on the same top-k trajectory from keeping only the previous step's set;
+# §4.3: the set-associative FIFO pool adopted instead).  These run on the CPU only; they
+# measure policies on a trajectory and are not part of the device path.
+
+def lru_hits(trajectory: np.ndarray, capacity: int) -> np.ndarray:
+    """Hits per step of a fully associative LRU pool of `capacity` ids over one request's
+    trajectory [steps, k] (each row ascending, -1 padded).
+
+    Reading, in the plan's two phases: the step's de-duplicated set U is looked up
+    against the pool before anything is installed (u is a hit iff pooled before the step);
+    the hits are then touched in ascending position, and the misses installed after them in
+    ascending position, so they are the most recently used.  The pool keeps the `capacity`
+    most recently used ids (|U| <= capacity, so nothing of the current step is evicted).
+    """
+    last_use = {}
+    hits = []
+    for s, row in enumerate(np.asarray(trajectory)):
+        U = np.unique(row[row >= 0])
+        assert len(U) <= capacity
+        is_hit = [u in last_use for u in U.tolist()]
+        hits.append(sum(is_hit))
+        for r, (u, h) in enumerate(zip(U.tolist(), is_hit)):
+            last_use[u] = (s, 0 if h else 1, r)
+        if len(last_use) > capacity:
+            keep = sorted(last_use.items(), key=lambda kv: kv[1])[-capacity:]
+            last_use = dict(keep)
+    return np.array(hits, dtype=np.int64)
+
+
+def previous_set_hits(trajectory: np.ndarray) -> np.ndarray:
+    """Hits per step when only the previous step's set is kept on the device."""
+    prev, hits = set(), []
+    for row in np.asarray(trajectory):
+        U = set(np.unique(row[row >= 0]).tolist())
+        hits.append(len(U & prev))
+        prev = U
+    return np.array(hits, dtype=np.int64)
+
+
+def fifo_hits(trajectory: np.ndarray, n_sets: int, ways: int, id_range: int) -> np.ndarray:
+    """Hits per step of the set-associative FIFO pool (plan_step) over one request."""
+    state = empty_state(n_sets, ways, id_range)
+    hits = []
+    for row in np.asarray(trajectory):
+        out, state = plan_step(row[None, :], *state, n_sets, ways)
+        hits.append(out["n_hit"])
+    return np.array(hits, dtype=np.int64)

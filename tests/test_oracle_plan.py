@@ -147,3 +147,49 @@ def test_multi_query_union_and_padding():
     assert out["n_unique"] == 5 and list(out["miss_pos"]) == [1, 5, 9, 13, 17]
     assert out["slot"][0, 3] == -1 and out["is_hit"][0, 3] == 0
     assert out["slot"][0, 1] == out["slot"][1, 0]                # same id -> same decision
+
+
+# ---------------------------------------------------------------- replacement-policy comparison
+def _textbook_lru(traj, capacity):
+    """A recency list: per step, look every id up first; move each hit to the back
+    (ascending), then append each miss (ascending), dropping the front when over capacity."""
+    from collections import OrderedDict
+    cache, hits = OrderedDict(), []
+    for row in traj:
+        U = np.unique(row[row >= 0]).tolist()
+        hit = [u for u in U if u in cache]
+        for u in hit:
+            cache.move_to_end(u)
+        for u in U:
+            if u not in cache:
+                cache[u] = True
+                if len(cache) > capacity:
+                    cache.popitem(last=False)
+        hits.append(len(hit))
+    return np.array(hits)
+
+
+def _random_traj(rng, steps, k, id_range):
+    return np.stack([np.sort(rng.choice(id_range, size=k, replace=False)) for _ in range(steps)]).astype(np.int32)
+
+
+def test_lru_matches_textbook_lru():
+    rng = np.random.default_rng(4)
+    for cap in (16, 20, 37, 64):
+        t = _random_traj(rng, 40, 16, 64)
+        assert np.array_equal(plan.lru_hits(t, cap), _textbook_lru(t, cap)), cap
+
+
+def test_lru_special_cases():
+    rng = np.random.default_rng(6)
+    t = _random_traj(rng, 25, 12, 50)
+    # a pool of exactly k ids holds the previous step's set
+    assert np.array_equal(plan.lru_hits(t, 12), plan.previous_set_hits(t))
+    # a pool larger than every id hits whatever was seen before
+    seen, want = set(), []
+    for row in t:
+        want.append(len(set(row.tolist()) & seen))
+        seen |= set(row.tolist())
+    assert np.array_equal(plan.lru_hits(t, 1000), want)
+    # one set of enough ways never evicts either
+    assert np.array_equal(plan.fifo_hits(t, 1, 64, 64), want)
