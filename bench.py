@@ -130,9 +130,10 @@ def main():
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter files and exit")
-    ap.add_argument("--entry", choices=["step", "kv_write"], default="step",
-                    help="kv_write: time dsa_kv_write alone (the new tokens of a decode step) and print "
-                         "its own line instead of the step's")
+    ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
+                    help="kv_write: time dsa_kv_write alone (the new tokens of a decode step); pool_group: "
+                         "time the device-pool workload with serial and auxiliary-stream installs; each "
+                         "prints its own line instead of the step's")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
@@ -149,6 +150,9 @@ def main():
     torch.cuda.set_device(0)
     if args.entry == "kv_write":
         bench_kv_write(args)
+        return
+    if args.entry == "pool_group":
+        bench_pool_group(args)
         return
     wl = synth.make_workload(2)
     dw = DevWorkload(wl)
@@ -281,6 +285,56 @@ def bench_kv_write(args):
     print(json.dumps({"metric": "dsa_kv_write us per call (back-to-back launches, HIP events)",
                       "entry": "dsa_kv_write", "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
                       "runs": res, "bound": "launch latency (a few KB per call)"}), flush=True)
+
+
+def bench_pool_group(args):
+    """The pool workload at full size (16 requests, 128K context, 4 layers of one shared
+    group, 2048 selected rows per request): the 8-step top-k trajectory from an empty pool,
+    per step one plan and per layer serve (hits from the device pool, misses from pinned
+    host rows over the host link) -> attention -> install, with installs serial or on an
+    auxiliary stream overlapped with attention.  Host rows are zero (only time is measured)."""
+    import torch
+    import synth
+    from synth import gen as sgen
+    import paged_kv_cache_indexer_amd as dsa
+    from tests.dsa_dev import HipMark, PoolGroupStep, host_device_ptr
+    cfg = synth.spec(4)
+    traj = sgen.topk_trajectory(cfg)
+    hosts = []
+    for _ in range(cfg.layers):
+        h = torch.zeros((cfg.B * cfg.L, 576), dtype=torch.int16, pin_memory=True)
+        hosts.append((h, dsa.Rows(h, 1152, req_stride=cfg.L, base_ptr=host_device_ptr(h))))
+    rows = [r for _, r in hosts]
+    H = cfg.mla_heads
+    q = [torch.randn(cfg.B, 1, H, 576, device="cuda").to(torch.bfloat16) for _ in range(cfg.layers)]
+    tks = [torch.from_numpy(np.ascontiguousarray(traj[s][:, None, :])).cuda() for s in range(cfg.steps)]
+    res = []
+    for n_sets, ways in ((1024, 8), (1024, 16)):
+        for aux in (False, True):
+            best = None
+            for rep in range(3):
+                pg = PoolGroupStep(cfg.B, cfg.topk, H, n_sets, ways, cfg.id_range, rows, cfg.scale, aux_install=aux)
+                stream = torch.cuda.Stream()
+                torch.cuda.synchronize()
+                e0, e1 = HipMark(), HipMark()
+                e0.record(stream)
+                for s in range(cfg.steps):
+                    pg.run(stream, tks[s], q)
+                if aux:
+                    stream.wait_event(pg.plan_free[(pg.step_no - 1) % 2])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_ms(e1) / cfg.steps
+                assert int(pg.err) == 0
+                best = ms if best is None else min(best, ms)
+                hit = float(sum(pg.plan_out[(cfg.steps - 1) % 2]["is_hit"].sum().item() for _ in [0])) / (cfg.B * cfg.topk)
+                del pg
+            res.append({"pool": f"{n_sets}x{ways}", "install": "aux stream" if aux else "serial",
+                        "ms_per_step": best, "ms_per_layer": best / cfg.layers, "last_step_hit_rate": hit})
+    print(json.dumps({"metric": "pool-group decode ms per step (plan + 4 x (serve, attention, install))",
+                      "entry": "pool_group", "data": "synthetic trajectory; zero host rows (timing only)",
+                      "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk, "runs": res}),
+          flush=True)
 
 
 if __name__ == "__main__":

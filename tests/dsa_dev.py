@@ -164,3 +164,71 @@ class DecodeStep:
                                   err=dw.err, stream=stream)
         if marks:
             marks[3].record(stream)
+
+
+class PoolGroupStep:
+    """One decode step of the device-pool workload for the layers of one shared group:
+    one plan (committed at plan time), then per layer serve -> attention -> install.
+
+    With `aux_install`, each layer's install runs on a second stream: it waits for that
+    layer's serve (it reads the served rows) and overlaps the layer's attention, and the
+    next step's serve of the layer waits for it (it reads pool rows the install writes and
+    overwrites the served rows the install reads).  The plan outputs alternate between two
+    buffers, so the next step's plan never overwrites what a pending install still reads.
+
+    host  : list (one per layer) of Rows over the request-major host rows [B*L, 576]
+    """
+
+    def __init__(self, B, k, H, n_sets, ways, id_range, host, scale, aux_install=False):
+        self.B, self.k, self.H, self.S, self.W, self.idr = B, k, H, n_sets, ways, id_range
+        self.host, self.scale, self.aux = host, scale, aux_install
+        self.layers = len(host)
+        dev = DEV
+        self.pool = [torch.zeros((B, n_sets * ways, 576), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.sel = [torch.empty((B, 1, k, 576), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.o = [torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.lse = [torch.empty((B, 1, H), dtype=torch.float32, device=dev) for _ in host]
+        self.pids = torch.full((B, n_sets * ways), -1, dtype=torch.int32, device=dev)
+        self.its = torch.full((B, id_range), -1, dtype=torch.int32, device=dev)
+        self.ptr = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+        self.plan_out = [dict(is_hit=torch.empty((B, 1, k), dtype=torch.uint8, device=dev),
+                              slot=torch.empty((B, 1, k), dtype=torch.int32, device=dev),
+                              mp=torch.empty((B, k), dtype=torch.int32, device=dev),
+                              ms=torch.empty((B, k), dtype=torch.int32, device=dev),
+                              mc=torch.empty(B, dtype=torch.int32, device=dev)) for _ in range(2)]
+        self.ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, 1, H, k)), dtype=torch.uint8, device=dev)
+        self.ident = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).view(B, 1, k)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.aux_stream = torch.cuda.Stream() if aux_install else None
+        self.installed = [torch.cuda.Event() for _ in host]          # layer l's last install
+        self.plan_free = [torch.cuda.Event() for _ in range(2)]      # installs of the buffer's last step
+        self.step_no = 0
+
+    def run(self, stream, topk, q):
+        """topk [B, 1, k] int32 (device); q: list of [B, 1, H, 576] bf16 per layer."""
+        po = self.plan_out[self.step_no % 2]
+        if self.aux:
+            stream.wait_event(self.plan_free[self.step_no % 2])
+        with torch.cuda.stream(stream):
+            dsa.dsa_plan(topk, self.pids, self.its, self.ptr, self.S, self.W, po["is_hit"], po["slot"], po["mp"],
+                         po["ms"], po["mc"], commit=True, err=self.err, stream=stream)
+        for l in range(self.layers):
+            if self.aux:
+                stream.wait_event(self.installed[l])
+            dsa.dsa_gather_kv(topk, po["is_hit"], po["slot"], self.host[l], self.pool[l], self.sel[l],
+                              dsa.DSA_GATHER_SERVE, err=self.err, stream=stream)
+            if self.aux:
+                served = torch.cuda.Event()
+                served.record(stream)
+                self.aux_stream.wait_event(served)
+                dsa.dsa_gather_kv(topk, po["is_hit"], po["slot"], None, self.pool[l], self.sel[l],
+                                  dsa.DSA_GATHER_INSTALL, err=self.err, stream=self.aux_stream)
+                self.installed[l].record(self.aux_stream)
+            dsa.dsa_sparse_mla_decode(q[l], self.ident, dsa.Rows(self.sel[l], 1152, req_stride=self.k), self.scale,
+                                      self.o[l], self.lse[l], ws=self.ws, err=self.err, stream=stream)
+            if not self.aux:
+                dsa.dsa_gather_kv(topk, po["is_hit"], po["slot"], None, self.pool[l], self.sel[l],
+                                  dsa.DSA_GATHER_INSTALL, err=self.err, stream=stream)
+        if self.aux:
+            self.plan_free[self.step_no % 2].record(self.aux_stream)
+        self.step_no += 1
