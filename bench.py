@@ -331,9 +331,34 @@ def bench_pool_group(args):
                 del pg
             res.append({"pool": f"{n_sets}x{ways}", "install": "aux stream" if aux else "serial",
                         "ms_per_step": best, "ms_per_layer": best / cfg.layers, "last_step_hit_rate": hit})
+    # MTP draft steps over a frozen selection (next_n = 4 attention passes per verify step):
+    # serve once and reuse the selection buffer, or serve again before every draft step
+    from tests.dsa_dev import MtpDraftSteps
+    next_n = 4
+    qd = [q for _ in range(next_n)]
+    mtp = []
+    for reuse in (False, True):
+        best = None
+        for rep in range(3):
+            pg = PoolGroupStep(cfg.B, cfg.topk, H, 1024, 8, cfg.id_range, rows, cfg.scale)
+            stream = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            e0, e1 = HipMark(), HipMark()
+            e0.record(stream)
+            for s in range(cfg.steps):
+                MtpDraftSteps(pg, reuse).run(stream, tks[s], qd)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            assert int(pg.err) == 0
+            ms = e0.elapsed_ms(e1) / cfg.steps
+            best = ms if best is None else min(best, ms)
+            del pg
+        mtp.append({"selection": "reused" if reuse else "served per draft step", "draft_steps": next_n,
+                    "ms_per_verify_step": best})
     print(json.dumps({"metric": "pool-group decode ms per step (plan + 4 x (serve, attention, install))",
                       "entry": "pool_group", "data": "synthetic trajectory; zero host rows (timing only)",
-                      "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk, "runs": res}),
+                      "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk, "runs": res,
+                      "mtp_draft": mtp}),
           flush=True)
 
 

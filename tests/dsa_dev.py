@@ -206,6 +206,12 @@ class PoolGroupStep:
 
     def run(self, stream, topk, q):
         """topk [B, 1, k] int32 (device); q: list of [B, 1, H, 576] bf16 per layer."""
+        # the caller's tensors are read by work queued on other streams: keep the caching
+        # allocator from reusing their memory before that work is done
+        for t in [topk] + list(q):
+            t.record_stream(stream)
+            if self.aux:
+                t.record_stream(self.aux_stream)
         po = self.plan_out[self.step_no % 2]
         if self.aux:
             stream.wait_event(self.plan_free[self.step_no % 2])
@@ -232,3 +238,40 @@ class PoolGroupStep:
         if self.aux:
             self.plan_free[self.step_no % 2].record(self.aux_stream)
         self.step_no += 1
+
+
+class MtpDraftSteps:
+    """MTP draft steps over one frozen selection (the first step's top-k): one plan, one
+    serve of the selected rows (hits from the device pool, misses from the host rows), an
+    attention per draft step with that step's queries, and the installs after the last
+    draft step (the frozen selection needs nothing new from the pool meanwhile).  With
+    `reuse`, every draft step reads the first serve's selection buffer; without it, each
+    draft step serves the same rows again (history rows are immutable and the pool rows are
+    unchanged until the installs, so both give the same bytes)."""
+
+    def __init__(self, pg: "PoolGroupStep", reuse: bool):
+        self.pg, self.reuse = pg, reuse
+
+    def run(self, stream, topk, q_steps):
+        """topk [B, 1, k]; q_steps: per draft step, a list of per-layer queries.  Returns
+        the per-step list of per-layer (o, lse) copies."""
+        pg = self.pg
+        po = pg.plan_out[0]
+        outs = []
+        for t in [topk] + [x for q in q_steps for x in q]:
+            t.record_stream(stream)
+        with torch.cuda.stream(stream):
+            dsa.dsa_plan(topk, pg.pids, pg.its, pg.ptr, pg.S, pg.W, po["is_hit"], po["slot"], po["mp"], po["ms"],
+                         po["mc"], commit=True, err=pg.err, stream=stream)
+            for d, q in enumerate(q_steps):
+                for l in range(pg.layers):
+                    if d == 0 or not self.reuse:
+                        dsa.dsa_gather_kv(topk, po["is_hit"], po["slot"], pg.host[l], pg.pool[l], pg.sel[l],
+                                          dsa.DSA_GATHER_SERVE, err=pg.err, stream=stream)
+                    dsa.dsa_sparse_mla_decode(q[l], pg.ident, dsa.Rows(pg.sel[l], 1152, req_stride=pg.k), pg.scale,
+                                              pg.o[l], pg.lse[l], ws=pg.ws, err=pg.err, stream=stream)
+                outs.append([(o.clone(), lse.clone()) for o, lse in zip(pg.o, pg.lse)])
+            for l in range(pg.layers):
+                dsa.dsa_gather_kv(topk, po["is_hit"], po["slot"], None, pg.pool[l], pg.sel[l],
+                                  dsa.DSA_GATHER_INSTALL, err=pg.err, stream=stream)
+        return outs

@@ -62,3 +62,36 @@ def test_aux_stream_install_matches_serial(n_sets, ways):
         for b in range(cfg.B):
             live = np.nonzero(pid[b] >= 0)[0]
             assert np.array_equal(pool[b, live], hn[b * cfg.L + pid[b, live]])
+
+
+def test_mtp_draft_steps_reuse_the_first_selection():
+    """Draft steps that reuse the first step's selection buffer attend exactly like draft
+    steps that serve the frozen top-k again, and leave the same pool."""
+    from tests.dsa_dev import MtpDraftSteps
+    cfg = synth.spec(4).scaled(B=4, L=16384, steps=3, layers=2, id_range=16384)
+    traj = sgen.topk_trajectory(cfg)
+    hosts = _host_rows(cfg, cfg.layers)
+    rows = [r for _, r in hosts]
+    H, next_n = 32, 4
+    g = torch.Generator(device="cpu").manual_seed(2)
+    stream = torch.cuda.Stream()
+    results = {}
+    for reuse in (False, True):
+        pg = PoolGroupStep(cfg.B, cfg.topk, H, cfg.n_sets, cfg.ways, cfg.id_range, rows, cfg.scale)
+        g.manual_seed(2)
+        outs_all = []
+        for s in range(cfg.steps):                       # a few verify steps, each with next_n draft steps
+            q_steps = [[torch.randn(cfg.B, 1, H, 576, generator=g).to(torch.bfloat16).to(DEV)
+                        for _ in range(cfg.layers)] for _ in range(next_n)]
+            tk = t_i32(traj[s][:, None, :])
+            outs_all.append(MtpDraftSteps(pg, reuse).run(stream, tk, q_steps))
+            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        assert int(pg.err) == 0
+        results[reuse] = (outs_all, [p.clone() for p in pg.pool], pg.pids.clone())
+    (o0, p0, i0), (o1, p1, i1) = results[False], results[True]
+    for s in range(cfg.steps):
+        for d in range(next_n):
+            for l in range(cfg.layers):
+                assert torch.equal(o0[s][d][l][0], o1[s][d][l][0]) and torch.equal(o0[s][d][l][1], o1[s][d][l][1])
+    assert all(torch.equal(a, b) for a, b in zip(p0, p1)) and torch.equal(i0, i1)
