@@ -60,3 +60,51 @@ def f64_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- MXFP4
+# OCP Microscaling (MX) v1.0: an MXFP4 block is 32 FP4 E2M1 elements sharing one E8M0
+# scale.  E2M1 has 1 sign bit, 2 exponent bits (bias 1) and 1 mantissa bit, no
+# infinities or NaN; its magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  E8M0 is an unsigned
+# power of two 2^(c - 127), with code 0xFF as NaN.  Packing (a reading; the format fixes
+# the element encoding, not the byte layout): element 2i sits in the low nibble of byte i
+# and element 2i+1 in the high nibble.
+
+MX_BLOCK = 32
+
+
+def e2m1_to_f64(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (the low 4 bits of each uint8) -> float64, exactly."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    normal = (1.0 + m / 2.0) * np.ldexp(1.0, (e - 1).astype(np.int64))
+    subnormal = m / 2.0                       # m * 2^(1 - bias) * 2^-1
+    return np.where(e == 0, subnormal, normal) * sign
+
+
+def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale codes (uint8) -> float64 2^(c - 127); 0xFF decodes to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 0xFF, np.nan, np.ldexp(1.0, c - 127))
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """[..., n] bytes -> [..., 2n] E2M1 codes, element 2i from the low nibble of byte i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mxfp4_to_f64(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 rows -> float64 [..., D]: packed [..., D/2] bytes, scales [..., D/32] E8M0.
+
+    Element d is e2m1(code d) * 2^(scale[d // 32] - 127), exact in float64.
+    """
+    vals = e2m1_to_f64(unpack_fp4(packed))
+    s = e8m0_to_f64(scales)
+    assert vals.shape[-1] == MX_BLOCK * s.shape[-1], (vals.shape, s.shape)
+    return vals * np.repeat(s, MX_BLOCK, axis=-1)

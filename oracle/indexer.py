@@ -8,13 +8,16 @@ dot product
     score[b,t,s] = sum_h  w[b,t,h] * max(0, sigma_s * sum_d q[b,t,h,d] * c[b,s,d])
 
 where c is the stored key (fp32, or an e4m3 code with per-token scale sigma_s;
-sigma = 1 when absent).  Query t of a request with cache length L and Sq query
+sigma = 1 when absent).  The FP4 indexer cache that the TokenSpeed audit page lists
+as an option of the DSA backend ("DSA": optional FP4 indexer cache) is not defined
+there; it is read here as OCP MXFP4 keys: each block of 32 dimensions is E2M1 codes
+times its own E8M0 power of two, decoded exactly, with sigma = 1.  Query t of a request with cache length L and Sq query
 tokens sees positions [0, L - Sq + t]; other positions score -inf.  Evaluated in
 float64 and rounded once to float32.
 """
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_to_f64
+from .formats import bf16_to_f64, e4m3_to_f64, mxfp4_to_f64
 from .paging import paged_rows
 
 
@@ -32,6 +35,8 @@ def request_keys(wl, b: int, positions) -> np.ndarray:
     """Dequantised keys [n, D] (float64) of request b at the given positions."""
     rows = paged_rows(wl.page_table[b], positions, wl.page_size)
     flat = wl.idx_k.reshape(-1, wl.idx_k.shape[-1])[rows]
+    if wl.idx_k_dtype == "mxfp4":
+        return mxfp4_to_f64(flat, wl.idx_k_scale.reshape(-1, wl.idx_k_scale.shape[-1])[rows])
     k = np.asarray(flat, dtype=np.float32).astype(np.float64) if wl.idx_k_dtype == "f32" else e4m3_to_f64(flat)
     if wl.idx_k_scale is not None:
         k = k * wl.idx_k_scale.reshape(-1)[rows].astype(np.float64)[:, None]

@@ -30,7 +30,7 @@ class WorkloadSpec:
     idx_heads: int = 64
     idx_dim: int = 128
     idx_q_kind: str = "bf16"    # "grid_f32" | "bf16" | "e4m3"
-    idx_k_kind: str = "e4m3_scaled"  # "grid_f32" | "e4m3_scaled"
+    idx_k_kind: str = "e4m3_scaled"  # "grid_f32" | "e4m3_scaled" | "mxfp4"
     w_kind: str = "u01_div64"   # "quarters" | "u01_div64"
     topk: int = 2048
     # MLA

@@ -7,6 +7,8 @@ materialised.  Results are raw storage arrays:
 
 * bf16  -> ``uint16`` bit patterns (fp32 draw, cast by torch, round-to-nearest-even)
 * e4m3  -> ``uint8``  OCP FP8 E4M3FN codes (cast by torch, round-to-nearest-even)
+* mxfp4 -> ``uint8``  packed E2M1 codes (two per byte) plus one E8M0 code per 32
+  elements, both drawn directly as codes
 * fp32 / int32 / int64 as themselves
 
 Paged caches are stored in *physical* page order: one seeded permutation of all
@@ -96,6 +98,30 @@ def scaled_e4m3_rows(key, n_rows: int, width: int):
     return codes, sig
 
 
+MXFP4_SCALE_CODES = (124, 128)     # E8M0 block codes drawn uniformly in this range (2^-3 .. 2^1)
+
+
+def mxfp4_rows(key, n_rows: int, width: int):
+    """MXFP4 keys drawn as codes: uniform random bytes (every E2M1 code equally likely in
+    each nibble) and E8M0 block-scale codes uniform in MXFP4_SCALE_CODES.
+
+    Returns (packed uint8 [n_rows, width/2], scales uint8 [n_rows, width/32]).
+    """
+    assert width % 32 == 0
+    packed = np.empty((n_rows, width // 2), dtype=np.uint8)
+    scales = np.empty((n_rows, width // 32), dtype=np.uint8)
+    lo, hi = MXFP4_SCALE_CODES
+
+    def work(args):
+        c, a, b = args
+        g = _rng(*key, c)
+        packed[a:b] = g.integers(0, 256, (b - a, width // 2), dtype=np.uint8)
+        scales[a:b] = g.integers(lo, hi + 1, (b - a, width // 32), dtype=np.uint8)
+
+    list(_POOL.map(work, list(_chunks(n_rows))))
+    return packed, scales
+
+
 @dataclass
 class Workload:
     spec: WorkloadSpec
@@ -110,9 +136,9 @@ class Workload:
     idx_q: Optional[np.ndarray] = None   # [B,Sq,H,D] f32 | uint16(bf16) | uint8(e4m3)
     idx_q_dtype: str = ""
     idx_w: Optional[np.ndarray] = None   # f32 [B,Sq,H]
-    idx_k: Optional[np.ndarray] = None   # [num_pages, ps, D] f32 | uint8(e4m3)
+    idx_k: Optional[np.ndarray] = None   # [num_pages, ps, D] f32 | uint8(e4m3); [num_pages, ps, D/2] uint8(mxfp4)
     idx_k_dtype: str = ""
-    idx_k_scale: Optional[np.ndarray] = None  # f32 [num_pages, ps] or None
+    idx_k_scale: Optional[np.ndarray] = None  # f32 [num_pages, ps]; uint8 [num_pages, ps, D/32] (mxfp4); or None
     mla_q: Optional[np.ndarray] = None   # uint16(bf16) [B,Sq,Hm,576]
     kv: Optional[np.ndarray] = None      # uint16(bf16) [num_pages, ps, 576]
     extra: Dict[str, object] = field(default_factory=dict)
@@ -160,7 +186,7 @@ def _indexer_query(cfg: WorkloadSpec, B: int):
 
 
 def _indexer_keys(cfg: WorkloadSpec, num_pages: int, key_extra=()):
-    """Paged indexer keys [num_pages, ps, D] (+ per-token scale for e4m3)."""
+    """Paged indexer keys [num_pages, ps, D] (+ per-token scale for e4m3, block scales for mxfp4)."""
     D, ps = cfg.idx_dim, cfg.page_size
     s, c = cfg.seed, cfg.cid
     out = {}
@@ -169,6 +195,11 @@ def _indexer_keys(cfg: WorkloadSpec, num_pages: int, key_extra=()):
         out["idx_k"] = _rng(s, c, T_IDXK, *key_extra).integers(-4, 5, size=(num_pages, ps, D)).astype(np.float32)
         out["idx_k_dtype"] = "f32"
         out["idx_k_scale"] = None
+    elif cfg.idx_k_kind == "mxfp4":
+        packed, sc = mxfp4_rows((s, c, T_IDXK) + tuple(key_extra), rows, D)
+        out["idx_k"] = packed.reshape(num_pages, ps, D // 2)
+        out["idx_k_dtype"] = "mxfp4"
+        out["idx_k_scale"] = sc.reshape(num_pages, ps, D // 32)
     else:
         codes, sig = scaled_e4m3_rows((s, c, T_IDXK) + tuple(key_extra), rows, D)
         out["idx_k"] = codes.reshape(num_pages, ps, D)

@@ -4,6 +4,7 @@ Each case reduces the score to something fixed independently of the oracle's cod
 a library dot product, an exact identity of ReLU, or an invariance of paging.
 """
 import dataclasses
+import os
 
 import numpy as np
 import torch
@@ -94,3 +95,51 @@ def test_visibility_of_draft_queries():
         n = 300 - 4 + 1 + t                       # history 296 tokens + drafts 0..t
         assert np.isfinite(sc[t, :n]).all()
         assert np.isneginf(sc[t, n:]).all()
+
+
+def mxfp4_workload(L=200, H=8, seed=0):
+    return synth.make_workload(synth.spec(2).scaled(B=1, L=L, idx_heads=H, idx_k_kind="mxfp4", seed=seed),
+                               with_kv=False)
+
+
+def _golden_e2m1():
+    path = os.path.join(os.path.dirname(__file__), "golden", "ocp_e2m1_codes.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    return {int(c, 16): float(v) for c, v in rows}
+
+
+def test_mxfp4_scores_equal_fp32_scores_of_the_decoded_keys():
+    # decode every key by hand (nibble loop over the OCP E2M1 table, torch's E8M0 decode),
+    # store the values as fp32 keys, and score them on the plain fp32 path
+    wl = mxfp4_workload(L=150)
+    table = _golden_e2m1()
+    packed = wl.idx_k.reshape(-1, 64)
+    sc = torch.from_numpy(wl.idx_k_scale.reshape(-1, 4).copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    dec = np.empty((packed.shape[0], 128), dtype=np.float32)
+    for r in range(packed.shape[0]):
+        for i in range(64):
+            byte = int(packed[r, i])
+            for half, code in ((0, byte & 0xF), (1, byte >> 4)):
+                d = 2 * i + half
+                dec[r, d] = table[code] * sc[r, d // 32]
+    f32 = dataclasses.replace(wl, idx_k=dec.reshape(wl.num_pages, wl.page_size, 128), idx_k_dtype="f32",
+                              idx_k_scale=None)
+    assert np.array_equal(indexer.scores(wl, 0), indexer.scores(f32, 0))
+
+
+def test_mxfp4_block_scale_acts_on_its_own_32_dimensions():
+    wl = mxfp4_workload(L=100, H=1)
+    wl.idx_w = np.ones_like(wl.idx_w)
+    for j in range(4):
+        # query: +1 on block j's dimensions only (bf16 1.0 = 0x3F80), so the score is
+        # max(0, 2^(e_j - 127) * sum of that block's codes' values)
+        q = np.zeros_like(wl.idx_q)
+        q[0, 0, 0, 32 * j:32 * j + 32] = 0x3F80
+        base = dataclasses.replace(wl, idx_q=q)
+        s0 = indexer.scores(base, 0)[0]
+        for k in range(4):
+            sc = wl.idx_k_scale.copy()
+            sc[..., k] += 1
+            s1 = indexer.scores(dataclasses.replace(base, idx_k_scale=sc), 0)[0]
+            assert np.array_equal(s1, s0 * (2 if k == j else 1)), (j, k)
+    assert (s0 > 0).any()

@@ -44,3 +44,16 @@ def test_trajectory_reuse_fraction():
             assert len(np.unique(tr[s, b])) == cfg.topk and (np.diff(tr[s, b]) > 0).all()
             if s:
                 assert len(np.intersect1d(tr[s, b], tr[s - 1, b])) == 1229
+
+
+def test_mxfp4_keys_shapes_and_code_ranges():
+    a = synth.make_workload(synth.spec(2).scaled(B=2, L=1000, idx_k_kind="mxfp4"), with_kv=False)
+    b = synth.make_workload(synth.spec(2).scaled(B=2, L=1000, idx_k_kind="mxfp4"), with_kv=False)
+    assert a.idx_k_dtype == "mxfp4"
+    assert a.idx_k.shape == (a.num_pages, 64, 64) and a.idx_k.dtype == np.uint8
+    assert a.idx_k_scale.shape == (a.num_pages, 64, 4) and a.idx_k_scale.dtype == np.uint8
+    assert np.array_equal(a.idx_k, b.idx_k) and np.array_equal(a.idx_k_scale, b.idx_k_scale)
+    lo, hi = gen.MXFP4_SCALE_CODES
+    assert a.idx_k_scale.min() == lo and a.idx_k_scale.max() == hi
+    nib = np.concatenate([a.idx_k.reshape(-1) & 0xF, a.idx_k.reshape(-1) >> 4])
+    assert np.bincount(nib, minlength=16).min() > 0.9 * nib.size / 16
