@@ -8,7 +8,10 @@ inputs, resident in HBM before timing starts.
 One step = indexer scan -> top-k -> sparse MLA decode (gather fused into attention through
 the page table) for the whole batch.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--keys mxfp4]
+
+--keys mxfp4 runs the same step over the FP4 indexer cache (MXFP4 keys: 64 bytes of E2M1
+codes and 4 E8M0 block scales per token) instead of e4m3 keys with a float32 scale.
 """
 import argparse
 import json
@@ -25,10 +28,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
-def algorithmic_work(B, L, H_idx, D, k, H_mla, ps):
+KEY_BYTES = {"e4m3": lambda D: D + 4,          # e4m3 codes + float32 per-token scale
+             "mxfp4": lambda D: D // 2 + D // 32}  # E2M1 codes + E8M0 block scales
+
+
+def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3"):
     """Bytes / flops each kernel must move or compute for one layer-step (no re-reads)."""
-    idx_bytes = (B * L * D            # e4m3 keys
-                 + B * L * 4          # per-token key scale
+    idx_bytes = (B * L * KEY_BYTES[keys](D)  # keys and their scales
                  + B * H_idx * D * 2  # bf16 queries
                  + B * H_idx * 4      # head weights
                  + B * (L // ps) * 4  # page table
@@ -65,7 +71,8 @@ def cpu_baseline(wl, budget_s=15.0):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.json")
 # entry point -> (kernel name prefixes in rocprofv3 output, sources the kernels are built from)
 ENTRY_KERNELS = {
-    "indexer": (["void dsa::indexer_mfma_kernel<false, 2, 1, 1>"], ["indexer.hip"]),
+    "indexer": (["void dsa::indexer_mfma_kernel<false, false, 2, 1, 1>"], ["indexer.hip"]),
+    "indexer_mxfp4": (["void dsa::indexer_mfma_kernel<false, true, 2, 1, 1>"], ["indexer.hip"]),
     "topk": (["dsa::topk_chunk_kernel", "dsa::topk_select_kernel"], ["topk.hip"]),
     "mla": (["void dsa::mla_decode_kernel<", "dsa::mla_merge_kernel"], ["mla.hip"]),
 }
@@ -87,9 +94,15 @@ def source_digest(entry):
 
 def record_traffic(fetch_csv, write_csv):
     """Average FETCH_SIZE / WRITE_SIZE per launch of each entry point (sum over its kernels),
-    from two rocprofv3 --pmc passes, written with the sources' digest."""
+    from two rocprofv3 --pmc passes, written with the sources' digest.  Entry points whose
+    kernels did not run in the profiled command keep their earlier record."""
     import csv
     out = {"factors": {"FETCH_SIZE": FETCH_FACTOR, "WRITE_SIZE": WRITE_FACTOR}, "entries": {}}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            out["entries"] = json.load(fh).get("entries", {})
+    except (OSError, ValueError):
+        pass
     vals = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         with open(path) as fh:
@@ -101,6 +114,8 @@ def record_traffic(fetch_csv, write_csv):
                         if r["Kernel_Name"].startswith(pfx):
                             vals.setdefault((entry, pfx, counter), []).append(float(r["Counter_Value"]))
     for entry, (prefixes, _) in ENTRY_KERNELS.items():
+        if not all((entry, p, c) in vals for p in prefixes for c in ("FETCH_SIZE", "WRITE_SIZE")):
+            continue
         kib = {c: sum(float(np.mean(vals[(entry, p, c)])) for p in prefixes) for c in ("FETCH_SIZE", "WRITE_SIZE")}
         out["entries"][entry] = {"fetch_kib": kib["FETCH_SIZE"], "write_kib": kib["WRITE_SIZE"],
                                  "bytes": (kib["FETCH_SIZE"] * FETCH_FACTOR + kib["WRITE_SIZE"] * WRITE_FACTOR) * 1024,
@@ -130,6 +145,8 @@ def main():
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter files and exit")
+    ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
     ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
                     help="kv_write: time dsa_kv_write alone (the new tokens of a decode step); pool_group: "
                          "time the device-pool workload with serial and auxiliary-stream installs; each "
@@ -154,7 +171,7 @@ def main():
     if args.entry == "pool_group":
         bench_pool_group(args)
         return
-    wl = synth.make_workload(2)
+    wl = synth.make_workload(synth.spec(2).scaled(idx_k_kind="mxfp4") if args.keys == "mxfp4" else 2)
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
@@ -208,7 +225,7 @@ def main():
 
     per = {n: float(np.mean([evs[i][j].elapsed_ms(evs[i][j + 1]) for i in range(args.steps)])) * 1e-3
            for j, n in enumerate(names)}                        # seconds per launch
-    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size)
+    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys)
     kernels = {}
     for n in names:
         by, fl = work[n]
@@ -218,7 +235,9 @@ def main():
     dom = max(names, key=lambda n: per[n])
     by = work[dom][0]
     roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom}
+                "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS,
+                "traffic": measured_traffic(dom + ("_mxfp4" if dom == "indexer" and args.keys == "mxfp4" else "")),
+                "kernel": dom}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     ms = wall / args.steps * 1e3
@@ -234,12 +253,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)",
+        "data": ("synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)" if args.keys == "e4m3" else
+                 "synthetic (seeded N(0,1); MXFP4 keys drawn as uniform codes, E8M0 in 124..128; random page "
+                 "permutation)"),
         "launch": mode,
         "kernel_timing": "HIP events on the launch stream around eager launches of the same K steps",
         "config": {"workload": "decode_b32_ctx65536_top2048", "batch": B, "context": L, "query_tokens": Sq,
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
-                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "keys": "e4m3 + fp32 scale"},
+                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16",
+                   "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

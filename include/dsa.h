@@ -55,7 +55,10 @@ typedef enum {
 typedef enum {
   DSA_F32 = 0,   /* IEEE binary32                                            */
   DSA_BF16 = 1,  /* bfloat16 (upper half of binary32)                        */
-  DSA_E4M3 = 2   /* OCP FP8 E4M3FN (bias 7, max 448, no infinities)          */
+  DSA_E4M3 = 2,  /* OCP FP8 E4M3FN (bias 7, max 448, no infinities)          */
+  DSA_MXFP4 = 3  /* OCP MX FP4: E2M1 codes two per byte (element 2i in the    *
+                  * low nibble of byte i) with one E8M0 scale byte 2^(c-127)  *
+                  * per 32 elements, held in a separate scale array           */
 } dsa_dtype_t;
 
 /*
@@ -104,8 +107,14 @@ const char* dsa_last_error(void);
  *
  *   q        [B, Sq, H, D]  dtype q_dtype (F32, BF16 or E4M3)
  *   w        [B, Sq, H]     float32 head weights
- *   keys     row store of keys: row_bytes = D * sizeof(k_dtype); k_dtype F32 or E4M3
- *   k_scale  float32 per key row (same row index as `keys`, sigma_s > 0), or NULL (1.0)
+ *   keys     row store of keys: row_bytes = D * sizeof(k_dtype) for F32 and E4M3, D / 2
+ *            for MXFP4
+ *   k_scale  F32 / E4M3 keys: float32 sigma_s per key row (same row index as `keys`,
+ *            sigma_s > 0), or NULL (1.0).
+ *            MXFP4 keys (the optional FP4 indexer cache of the TokenSpeed audit page,
+ *            "DSA"; read as OCP MXFP4): required; uint8 [num_rows, D/32] E8M0 block
+ *            scales, 4-byte aligned, key dimension d scaled by byte d/32 of its row.
+ *            The score then has no sigma_s (sigma_s = 1).
  *   seq_lens [B] int32 cache length per request (history + Sq query tokens), >= Sq
  *   scores   [B, Sq, score_stride] float32, score_stride >= max(seq_lens)
  *   ready    if not NULL, the stream waits on this event before the scan starts: the
@@ -113,12 +122,15 @@ const char* dsa_last_error(void);
  *            read keys that are not yet resident ([GLM5R] "BugFix#2": the indexer must
  *            sync with the load stream before it launches; [HCCP] §1.3 ordering).
  *
- * Supported: (q F32, k F32): any H*D <= 4096; (q BF16, k E4M3) and (q E4M3, k E4M3):
+ * Supported: (q F32, k F32): any H*D <= 4096; q BF16 or E4M3 with k E4M3 or MXFP4:
  * D = 128, H a multiple of 32, Sq*H <= 256.  Page size (paged keys) a multiple of 32.
+ * MXFP4 block-scale codes: 0x00..0xFE with E4M3 queries (the scaled MFMA applies them);
+ * 0x00..0xFE with BF16 queries as long as every scaled key element is a finite bf16
+ * (|element| * 2^(c-127) < 2^128).  Code 0xFF (NaN) gives an unspecified score.
  * Out-of-range page ids: the affected tokens score -inf and count in err_count.
  */
 dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
-                                const dsa_rows_t* keys, dsa_dtype_t k_dtype, const float* k_scale,
+                                const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,
                                 const int32_t* seq_lens, int B, int Sq, int H, int D,
                                 int64_t score_stride, float* scores, int32_t* err_count,
                                 hipEvent_t ready, hipStream_t stream);

@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_HIP, DSA_ERR_WORKSPACE = 0, -1, -2, -3, -4
-DSA_F32, DSA_BF16, DSA_E4M3 = 0, 1, 2
+DSA_F32, DSA_BF16, DSA_E4M3, DSA_MXFP4 = 0, 1, 2, 3
 DSA_GATHER_SERVE, DSA_GATHER_INSTALL = 0, 1
 
 STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED", -3: "DSA_ERR_HIP",

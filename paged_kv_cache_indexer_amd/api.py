@@ -10,7 +10,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import dsa_rows_t, DSA_F32, DSA_BF16, DSA_E4M3, DSA_GATHER_SERVE, DSA_GATHER_INSTALL  # noqa: F401
+from ._lib import dsa_rows_t, DSA_F32, DSA_BF16, DSA_E4M3, DSA_MXFP4, DSA_GATHER_SERVE, DSA_GATHER_INSTALL  # noqa: F401
 
 
 class DsaError(RuntimeError):

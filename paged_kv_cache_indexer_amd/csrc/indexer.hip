@@ -5,19 +5,26 @@
 //
 // Three kernels on one entry point:
 //   * indexer_f32_kernel   fp32 q and keys on the VALU (one thread per token).
-//   * indexer_mfma_kernel  D = 128 e4m3 keys streamed from the paged cache, heads on the
+//   * indexer_mfma_kernel  D = 128 keys streamed from the paged cache, heads on the
 //     MFMA M axis and 32 tokens on N, so the ReLU-weighted head sum is an in-lane
 //     reduction plus one cross-half add.  bf16 queries use v_mfma_f32_32x32x16_bf16 with
-//     the keys widened e4m3 -> bf16 in registers (exact); e4m3 queries use the fp8
+//     the keys widened to bf16 in registers (exact); e4m3 queries use the scaled
 //     v_mfma_scale_f32_32x32x64_f8f6f4 directly on the key bytes.
+//     Keys are e4m3 (128 B per token, optional per-token fp32 scale) or MXFP4 (64 B of
+//     E2M1 codes plus four E8M0 block scales per token: the FP4 indexer cache, read as
+//     OCP MXFP4).  MXFP4 keys are widened with v_cvt_scalef32_pk_bf16_fp4, which applies
+//     the block scale while converting (exact: every scaled E2M1 value is a bf16), or fed
+//     to the scaled MFMA as its fp4 B operand with the E8M0 byte as the B scale.
 //
-// Key loads: a 32-token tile (4 KB, contiguous inside its page) is read with four 16-byte
-// loads per lane where each instruction covers 1 KB contiguously (lane i, load c: bytes
-// 1024c + 16i), the streaming shape that reaches full HBM bandwidth.  The tile is then
-// re-laid through a per-wave LDS buffer so that lane (n = lane%32, g = lane/32) holds
-// bytes [64g, 64g+64) of token n's key for the MFMA B operand.  The contraction order over
-// d is the same permutation for the A (query) and B (key) operands, so any
-// d -> (lane group, register slot) assignment is valid.
+// Key loads: a 32-token tile (4 KB for e4m3, 2 KB for MXFP4; contiguous inside its page)
+// is read with 16-byte loads per lane where each instruction covers 1 KB contiguously
+// (lane i, load c: bytes 1024c + 16i), the streaming shape that reaches full HBM
+// bandwidth.  The tile is then re-laid through a per-wave LDS buffer so that lane
+// (n = lane%32, g = lane/32) holds the second half (g = 1) or first half (g = 0) of token
+// n's key bytes for the MFMA B operand.  The contraction order over d is the same
+// permutation for the A (query) and B (key) operands, so any d -> (lane group, register
+// slot) assignment is valid, provided (MXFP4) that each scaled-MFMA lane operand stays
+// inside one 32-element block.
 #include <type_traits>
 
 #include "common.h"
@@ -77,8 +84,8 @@ constexpr int kMaxB = 1024;    // requests per launch on this path
 struct MfmaArgs {
   const void* q;               // [B, Sq, H, 128] bf16 or e4m3
   const float* w;              // [B, Sq, H]
-  RowStore keys;               // 128-byte e4m3 rows
-  const float* k_scale;        // per row, or null
+  RowStore keys;               // 128-byte e4m3 rows or 64-byte MXFP4 rows
+  const void* k_scale;         // e4m3: float per row, or null; MXFP4: 4 E8M0 bytes per row
   const int32_t* seq_lens;     // [B]
   int B, Sq, H;
   int64_t score_stride;
@@ -157,6 +164,23 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   return ut;
 }
 
+// E8M0 code (low 8 bits of c) -> the float 2^(c - 127); code 0 is the subnormal 2^-127
+__device__ __forceinline__ float e8m0_to_float(uint32_t c) {
+  c &= 0xFFu;
+  return __uint_as_float(c ? (c << 23) : 0x00400000u);
+}
+
+// 8 E2M1 codes (one dword, element i in nibble i) times a power-of-two scale -> bf16x8
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+  const u32x4 r = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // max(x, 0) as a signed-integer max of the bits: a float with the sign bit set (including
 // -0.0) is a negative integer and becomes +0.0; one instruction, where fmaxf would first
 // quiet its NaN operand
@@ -164,14 +188,17 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-template <bool QFP8, int HMT, int NQ, int RG>
+template <bool QFP8, bool KFP4, int HMT, int NQ, int RG>
 __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   constexpr int MT_W = HMT * NQ;
   constexpr int WPU = 4 / RG;                      // units processed side by side per work-group
   constexpr int KSTEPS = QFP8 ? 2 : 8;
+  constexpr int kRowBytes = KFP4 ? 64 : 128;       // key bytes per token
+  constexpr int kLoads = kRowBytes * kTile / 1024; // 16-byte loads per lane per tile
+  constexpr int kHalf = kRowBytes / 2;             // key bytes per lane group after the re-layout
   __shared__ int unit_off[kMaxB + 1];              // prefix of units per request
   __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
-  constexpr int kStageStride = 144;                                   // 128-byte key rows, padded
+  constexpr int kStageStride = kRowBytes + 16;                        // key rows, padded
   __shared__ __attribute__((aligned(16))) char kstage[4][kTile * kStageStride];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,8 +219,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   qop_t qa[MT_W][KSTEPS];
 
   struct Slot {
-    u32x4 kb[4];
-    float sig;
+    u32x4 kb[kLoads];
+    uint32_t sig;                                  // e4m3: fp32 scale bits; MXFP4: 4 E8M0 codes
     bool valid;
   };
 
@@ -241,20 +268,34 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
                                    (uint32_t)__builtin_amdgcn_readlane(row_lo, i));
       sl.valid = r0 >= 0;
       const int64_t r = (sl.valid ? r0 : 0) + n;
-      const char* kp = a.keys.base + (sl.valid ? r0 : 0) * 128 + lane * 16;
+      const char* kp = a.keys.base + (sl.valid ? r0 : 0) * kRowBytes + lane * 16;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sl.kb[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + c * 1024));
+      for (int c = 0; c < kLoads; ++c)
+        sl.kb[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + c * 1024));
       // always issue the scale load (a dummy in-bounds read when there is no scale), so
-      // every fetch adds the same number of outstanding loads; the value is only looked
-      // at in the epilogue, so nothing waits for it here
-      sl.sig = a.k_scale ? a.k_scale[r] : *reinterpret_cast<const float*>(a.keys.base);
+      // every fetch adds the same number of outstanding loads; an e4m3 scale is only looked
+      // at in the epilogue, so nothing waits for it here (MXFP4 is required to pass one)
+      sl.sig = a.k_scale ? static_cast<const uint32_t*>(a.k_scale)[r]
+                         : *reinterpret_cast<const uint32_t*>(a.keys.base);
     };
 
     // queries and weights of request b for this wave's rows
 #pragma unroll
     for (int mt = 0; mt < MT_W; ++mt) {
       const int64_t qoff = ((int64_t)b * a.Sq * a.H + row0 + mt * 32 + n) * 128;
-      if constexpr (QFP8) {
+      if constexpr (QFP8 && KFP4) {
+        // The scaled MFMA takes an 8-bit A lane (row, half g) as K = 16g + [0, 16) and
+        // 32 + 16g + [0, 16), but an fp4 B lane (column, half g) as K = 32g + [0, 32).  Step
+        // j's key lane (n, g) holds dimensions 64g + 32j + [0, 32), so the query lane (row, g)
+        // takes dimensions 32j + 16g + [0, 16) and 64 + 32j + 16g + [0, 16).
+        const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qoff + g * 16;
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(qp + j * 32);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(qp + 64 + j * 32);
+          qa[mt][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+      } else if constexpr (QFP8) {
         const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qoff + g * 64;
 #pragma unroll
         for (int j = 0; j < KSTEPS; ++j) {
@@ -288,21 +329,53 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
     // compute tile t from slot `cur`; once its bytes are in the LDS re-layout buffer the
     // slot is refilled with tile t_next, so that load is in flight during this tile's MFMAs
     auto compute = [&](Slot& cur, int t, bool live, int t_next) {
-      // re-lay the tile: load c of lane i holds row 8c + i/8, bytes 16*(i%8) .. +16
+      // re-lay the tile: load c of lane i holds token (1024c + 16i) / kRowBytes, bytes
+      // (16i) % kRowBytes .. +16
+      constexpr int kLanesPerRow = kRowBytes / 16;
       char* st = kstage[wave];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<u32x4*>(st + (c * 8 + (lane >> 3)) * kStageStride + (lane & 7) * 16) = cur.kb[c];
-      const float sig = cur.sig;
+      for (int c = 0; c < kLoads; ++c)
+        *reinterpret_cast<u32x4*>(st + (c * (64 / kLanesPerRow) + lane / kLanesPerRow) * kStageStride +
+                                  (lane % kLanesPerRow) * 16) = cur.kb[c];
+      const uint32_t sig = cur.sig;
       const bool valid = cur.valid;
       fetch(cur, t_next);
-      u32x4 kb[4];
+      u32x4 kb[kLoads];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const u32x4*>(st + n * kStageStride + g * 64 + c * 16);
+      for (int c = 0; c < kLoads; ++c)
+        kb[c] = *reinterpret_cast<const u32x4*>(st + n * kStageStride + g * kHalf + c * 16);
       f32x16 acc[MT_W];
 #pragma unroll
       for (int mt = 0; mt < MT_W; ++mt) acc[mt] = f32x16{};
-      if constexpr (QFP8) {
+      if constexpr (KFP4) {
+        // lane group g holds key dimensions [64g, 64g+64) = blocks 2g and 2g+1; their E8M0
+        // codes are bytes 0 and 1 of sg
+        const uint32_t sg = sig >> (16 * g);
+        if constexpr (QFP8) {
+          // step j: this lane's 32 dimensions [64g + 32j, +32) are MFMA K = 32g + [0, 32), key
+          // block 2g + j; the MFMA takes the scale of K-block g of column n from lane n + 32g,
+          // which is this lane, so its B scale is byte j of sg
+          const i32x8 b0 = i32x8{(int)kb[0].x, (int)kb[0].y, (int)kb[0].z, (int)kb[0].w, 0, 0, 0, 0};
+          const i32x8 b1 = i32x8{(int)kb[1].x, (int)kb[1].y, (int)kb[1].z, (int)kb[1].w, 0, 0, 0, 0};
+#pragma unroll
+          for (int mt = 0; mt < MT_W; ++mt) {
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][0], b0, acc[mt], 0, 4, 0, 127, 0, (int)sg);
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][1], b1, acc[mt], 0, 4, 0, 127, 1, (int)sg);
+          }
+        } else {
+          // step j: dimensions [64g + 8j, +8), in block 2g + j/4
+          const float s0 = e8m0_to_float(sg), s1 = e8m0_to_float(sg >> 8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const u32x4 kc = kb[j >> 2];
+            const uint32_t v = (j & 3) == 0 ? kc.x : (j & 3) == 1 ? kc.y : (j & 3) == 2 ? kc.z : kc.w;
+            const bf16x8 bop = fp4x8_to_bf16x8(v, j < 4 ? s0 : s1);
+#pragma unroll
+            for (int mt = 0; mt < MT_W; ++mt)
+              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][j], bop, acc[mt], 0, 0, 0);
+          }
+        }
+      } else if constexpr (QFP8) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const u32x4 k0 = kb[2 * j], k1 = kb[2 * j + 1];
@@ -342,7 +415,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
         part += __shfl_xor(part, 32);
         const int tq = rg * NQ + qq;
         const int vis = L - a.Sq + 1 + tq;
-        float v = a.k_scale ? part * sig : part;
+        float v = (!KFP4 && a.k_scale) ? part * __uint_as_float(sig) : part;
         if (!valid || s >= vis) v = -INFINITY;
         if (live && g == 0 && s < L) a.scores[((int64_t)b * a.Sq + tq) * a.score_stride + s] = v;
       }
@@ -358,27 +431,27 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   }
 }
 
-template <bool QFP8, int HMT, int NQ, int RG>
+template <bool QFP8, bool KFP4, int HMT, int NQ, int RG>
 static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
   static int grid = 0;
   if (grid == 0) {
     int dev = 0, cus = 256, per_cu = 1;
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, HMT, NQ, RG>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>, 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     grid = cus * per_cu;
   }
-  DSA_LAUNCH((indexer_mfma_kernel<QFP8, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
+  DSA_LAUNCH((indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
   return launch_status("dsa_indexer_scores");
 }
 
 }  // namespace dsa
 
 extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
-                                           const dsa_rows_t* keys, dsa_dtype_t k_dtype, const float* k_scale,
+                                           const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,
                                            const int32_t* seq_lens, int B, int Sq, int H, int D,
                                            int64_t score_stride, float* scores, int32_t* err_count,
                                            hipEvent_t ready, hipStream_t stream) {
@@ -405,23 +478,35 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
     DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
     const int64_t gx = (score_stride + 255) / 256;
     DSA_LAUNCH(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
-                       static_cast<const float*>(q), w, ks, k_scale, seq_lens, Sq, H, D, score_stride, scores,
+                       static_cast<const float*>(q), w, ks, static_cast<const float*>(k_scale), seq_lens, Sq, H, D, score_stride, scores,
                        err_count);
     return launch_status("dsa_indexer_scores");
   }
-  DSA_CHECK_SUPPORTED(k_dtype == DSA_E4M3 && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
-                      "dsa_indexer_scores: supported dtypes are (f32,f32), (bf16,e4m3), (e4m3,e4m3)");
+  DSA_CHECK_SUPPORTED((k_dtype == DSA_E4M3 || k_dtype == DSA_MXFP4) && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
+                      "dsa_indexer_scores: supported dtypes are (f32,f32) and q bf16/e4m3 with k e4m3/mxfp4");
   DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && Sq * H <= 256 && B <= kMaxB,
                       "dsa_indexer_scores: MFMA path needs D == 128, H %% 32 == 0, Sq*H <= 256, B <= 1024");
-  DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
+  const bool fp4 = k_dtype == DSA_MXFP4;
+  if (fp4) {
+    DSA_CHECK_ARG(keys->row_bytes == 64, "dsa_indexer_scores: MXFP4 row_bytes != 64");
+    DSA_CHECK_ARG(k_scale && ((uintptr_t)k_scale & 3) == 0,
+                  "dsa_indexer_scores: MXFP4 keys need 4-byte aligned E8M0 block scales");
+  } else {
+    DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
+  }
   if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "dsa_indexer_scores: page_size %% 32 != 0");
   MfmaArgs a{q, w, ks, k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count};
   const int HMT = H / 32;
   const bool f8 = q_dtype == DSA_E4M3;
   // one wave covers up to 4 M tiles; queries beyond that go to a second wave on the same tile
 #define DSA_CASE(HM, NQ_, RG_)                                                                  \
-  if (HMT == HM && Sq == NQ_ * RG_)                                                              \
-    return f8 ? launch_mfma<true, HM, NQ_, RG_>(a, stream) : launch_mfma<false, HM, NQ_, RG_>(a, stream);
+  if (HMT == HM && Sq == NQ_ * RG_) {                                                            \
+    if (fp4)                                                                                     \
+      return f8 ? launch_mfma<true, true, HM, NQ_, RG_>(a, stream)                               \
+                : launch_mfma<false, true, HM, NQ_, RG_>(a, stream);                             \
+    return f8 ? launch_mfma<true, false, HM, NQ_, RG_>(a, stream)                                \
+              : launch_mfma<false, false, HM, NQ_, RG_>(a, stream);                              \
+  }
   DSA_CASE(1, 1, 1) DSA_CASE(1, 2, 1) DSA_CASE(1, 4, 1) DSA_CASE(1, 4, 2)
   DSA_CASE(2, 1, 1) DSA_CASE(2, 2, 1) DSA_CASE(2, 2, 2)
   DSA_CASE(4, 1, 1) DSA_CASE(4, 1, 2)

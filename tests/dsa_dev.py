@@ -50,7 +50,11 @@ class DevWorkload:
             self.k_dtype = dsa.DSA_F32
             row_bytes = wl.idx_k.shape[-1] * 4
         self.q_dtype = {"f32": dsa.DSA_F32, "bf16": dsa.DSA_BF16, "e4m3": dsa.DSA_E4M3}[wl.idx_q_dtype]
-        self.k_scale = t_f32(wl.idx_k_scale) if wl.idx_k_scale is not None else None
+        if wl.idx_k_dtype == "mxfp4":                  # packed E2M1 rows + E8M0 block scales
+            self.k_dtype = dsa.DSA_MXFP4
+            self.k_scale = t_u8(wl.idx_k_scale)
+        else:
+            self.k_scale = t_f32(wl.idx_k_scale) if wl.idx_k_scale is not None else None
         self.idx_w = t_f32(wl.idx_w)
         self.keys = dsa.Rows(self.idx_k, row_bytes, self.page_table, wl.page_size)
         self.mla_q = t_u16_as_bf16(wl.mla_q)

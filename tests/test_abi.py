@@ -65,5 +65,17 @@ def test_invalid_arguments_rejected_without_device():
     assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 64, ctypes.byref(kv), ctypes.byref(ic), p, None,
                           None) == _lib.DSA_ERR_INVALID_ARG          # indexer rows must be D bytes
     assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 0, 1, 128, None, None, None, None, None) == _lib.DSA_OK
+    # MXFP4 keys: 64-byte rows and a 4-byte aligned block-scale array are required
+    k4 = _lib.dsa_rows_t()
+    k4.base, k4.row_bytes, k4.num_rows = 16, 64, 64
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(k4), _lib.DSA_MXFP4, None, p, 1, 1, 64, 128,
+                                64, p, None, None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(k4), _lib.DSA_MXFP4, ctypes.c_void_p(18), p, 1,
+                                1, 64, 128, 64, p, None, None, None) == _lib.DSA_ERR_INVALID_ARG
+    k4.row_bytes = 128
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(k4), _lib.DSA_MXFP4, p, p, 1, 1, 64, 128, 64, p,
+                                None, None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_scores(p, _lib.DSA_F32, p, ctypes.byref(k4), _lib.DSA_MXFP4, p, p, 1, 1, 64, 128, 64, p,
+                                None, None, None) == _lib.DSA_ERR_UNSUPPORTED
     # empty batches are valid no-ops
     assert L.dsa_topk(None, 1, None, 0, 1, 8, None, None, 0, None) == _lib.DSA_OK

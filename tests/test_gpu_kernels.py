@@ -108,6 +108,36 @@ def test_indexer_e4m3_queries_mtp_within_bound():
     check_scores(wl, DevWorkload(wl, with_kv=False).scores())
 
 
+@pytest.mark.parametrize("L", [[1000, 777, 33], [4096, 64, 4095]])
+def test_indexer_mxfp4_keys_bf16_queries_within_bound(L):
+    wl = synth.make_workload(synth.spec(2).scaled(B=3, L=max(L), idx_k_kind="mxfp4"), with_kv=False)
+    wl.seq_lens = np.array(L, dtype=np.int32)
+    dw = DevWorkload(wl, with_kv=False)
+    assert dw.keys.c.row_bytes == 64 and dw.k_dtype == dsa.DSA_MXFP4
+    check_scores(wl, dw.scores())
+    assert int(dw.err) == 0
+
+
+def test_indexer_mxfp4_keys_e4m3_queries_mtp_within_bound():
+    wl = synth.make_workload(synth.spec(3).scaled(B=2, L=1500, idx_k_kind="mxfp4"), with_kv=False)
+    wl.seq_lens = np.array([1500, 1031], dtype=np.int32)
+    dw = DevWorkload(wl, with_kv=False)
+    check_scores(wl, dw.scores())
+    assert int(dw.err) == 0
+
+
+@pytest.mark.parametrize("qkind,H,Sq", [("bf16", 32, 1), ("e4m3", 64, 1), ("bf16", 128, 2)])
+def test_indexer_mxfp4_wide_block_scales(qkind, H, Sq):
+    # block scales spread over 2^-27 .. 2^27 and differing inside each token, so a wrong
+    # block -> scale mapping or nibble order cannot stay inside the bound
+    wl = synth.make_workload(synth.spec(2).scaled(B=2, L=2100, idx_heads=H, Sq=Sq, idx_q_kind=qkind,
+                                                  idx_k_kind="mxfp4"), with_kv=False)
+    wl.seq_lens = np.array([2100, 1333], dtype=np.int32)
+    rng = np.random.default_rng(11)
+    wl.idx_k_scale = rng.integers(100, 155, wl.idx_k_scale.shape).astype(np.uint8)
+    check_scores(wl, DevWorkload(wl, with_kv=False).scores())
+
+
 def test_indexer_ready_event_orders_load_before_scan():
     """The scan waits on the load stream's event; without the wait it reads stale keys."""
     wl = synth.make_workload(synth.spec(1).scaled(L=2048), with_kv=False)
