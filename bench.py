@@ -145,6 +145,10 @@ def main():
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter files and exit")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="distinct per-layer caches the steps rotate through (a model's successive layers "
+                         "read different caches; rotating keeps a step from hitting the previous step's "
+                         "bytes in the 256 MB last-level cache)")
     ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
     ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
@@ -175,7 +179,7 @@ def main():
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
-    step = DecodeStep(dw)
+    step = DecodeStep(dw, layers=args.layers)
     names = ["indexer", "topk", "mla"]
     stream = torch.cuda.Stream()            # non-default stream: the step is captured and replayed
 
@@ -186,8 +190,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step.run(stream)
+        for i in range(args.warmup):
+            step.run(stream, layer=i)
     torch.cuda.synchronize()
 
     # The K timed steps are one HIP graph (launch overhead of the five kernels removed, as
@@ -200,7 +204,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(args.steps):
-                step.run(stream)
+                step.run(stream, layer=i)
         graph.replay()
         torch.cuda.synchronize()
         run_timed = graph.replay
@@ -211,7 +215,7 @@ def main():
 
         def run_timed():
             for i in range(args.steps):
-                step.run(stream)
+                step.run(stream, layer=i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_timed()
@@ -219,7 +223,7 @@ def main():
     wall = time.perf_counter() - t0
     evs = [[HipMark() for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step.run(stream, evs[i])
+        step.run(stream, evs[i], layer=i)
     torch.cuda.synchronize()
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
 
@@ -260,7 +264,7 @@ def main():
         "kernel_timing": "HIP events on the launch stream around eager launches of the same K steps",
         "config": {"workload": "decode_b32_ctx65536_top2048", "batch": B, "context": L, "query_tokens": Sq,
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
-                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16",
+                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "layers_rotated": args.layers,
                    "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},
         "roofline": roofline,
         "kernels": kernels,

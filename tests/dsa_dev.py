@@ -140,9 +140,21 @@ class DecodeStep:
     recorded before, between and after the stages.
     """
 
-    def __init__(self, dw: DevWorkload):
+    def __init__(self, dw: DevWorkload, layers: int = 1):
+        """layers > 1: that many distinct device copies of the per-layer caches (indexer keys,
+        their scales, latent rows); `run(..., layer=i)` uses copy i % layers.  Successive
+        layers of a model read different caches, so rotating keeps a step from finding the
+        previous step's cache bytes in the last-level cache."""
         wl = dw.wl
         self.dw = dw
+        self.caches = [(dw.keys, dw.k_scale, dw.rows)]
+        for _ in range(layers - 1):
+            k = dw.idx_k.clone()
+            ks = dw.k_scale.clone() if dw.k_scale is not None else None
+            kv = dw.kv.clone()
+            keys = dsa.Rows(k, dw.keys.c.row_bytes, dw.page_table, wl.page_size)
+            rows = dsa.Rows(kv, 1152, dw.page_table, wl.page_size)
+            self.caches.append((keys, ks, rows))
         B, Sq, L, k = dw.B, dw.Sq, dw.Lmax, wl.topk
         H = wl.mla_q.shape[2]
         self.scores = torch.empty((B, Sq, L), dtype=torch.float32, device=DEV)
@@ -153,18 +165,19 @@ class DecodeStep:
                                   device=DEV)
         self.ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, k, L)), dtype=torch.uint8, device=DEV)
 
-    def run(self, stream, marks=None):
+    def run(self, stream, marks=None, layer=0):
         dw = self.dw
+        keys, k_scale, rows = self.caches[layer % len(self.caches)]
         if marks:
             marks[0].record(stream)
-        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, dw.k_scale, dw.seq_lens, self.scores,
+        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, keys, k_scale, dw.seq_lens, self.scores,
                                k_dtype=dw.k_dtype, err=dw.err, q_dtype=dw.q_dtype, stream=stream)
         if marks:
             marks[1].record(stream)
         dsa.dsa_topk(self.scores, dw.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
         if marks:
             marks[2].record(stream)
-        dsa.dsa_sparse_mla_decode(dw.mla_q, self.idx, dw.rows, dw.wl.scale, self.o, self.lse, ws=self.ws_mla,
+        dsa.dsa_sparse_mla_decode(dw.mla_q, self.idx, rows, dw.wl.scale, self.o, self.lse, ws=self.ws_mla,
                                   err=dw.err, stream=stream)
         if marks:
             marks[3].record(stream)
