@@ -110,7 +110,8 @@ constexpr int kSlots = 2;
 constexpr int kMaxUnit = (64 / kSlots) * kSlots;   // tiles per unit: at most one per lane
 
 // unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; returns ut
-__device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int* unit_off, int* wsum) {
+__device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int max_unit, int* unit_off,
+                              int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tiles[kPrefixPerThread];
   int mine = 0;
@@ -145,7 +146,7 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   int ut = (total_tiles + wave_slots - 1) / wave_slots;
   ut = ((ut + kSlots - 1) / kSlots) * kSlots;     // whole passes over the register slots
   if (ut < kSlots) ut = kSlots;
-  if (ut > kMaxUnit) ut = kMaxUnit;               // a unit's tile rows fit one per lane
+  if (ut > max_unit) ut = max_unit;               // tile rows one per lane; scores fit the LDS buffer
   int units[kPrefixPerThread];
   int my_units = 0;
 #pragma unroll
@@ -202,6 +203,13 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
   constexpr int kStageStride = kRowBytes + 16;                        // key rows, padded
   __shared__ __attribute__((aligned(16))) char kstage[4][kTile * kStageStride];
+  // A unit's scores are staged here and written after its last tile.  Stores share the
+  // vector-memory counter with loads, so a score store issued inside the tile loop made every
+  // later wait for key data also wait for that store's write acknowledgement (measured:
+  // 55.8 us with per-tile stores, 49.2 us without stores).
+  constexpr int kUnitCap = kMaxUnit / NQ;          // tiles per unit: NQ * kUnitCap * 32 scores per wave
+  static_assert(kUnitCap % kSlots == 0, "a unit is whole passes over the register slots");
+  __shared__ __attribute__((aligned(16))) float sbuf[4][kMaxUnit * kTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = wave % RG;
@@ -213,7 +221,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   const int tpp_shift = (tpp > 0 && (tpp & (tpp - 1)) == 0) ? __builtin_ctz(tpp) : -1;
 
   __shared__ int scan_wsum[4];
-  const int ut = __builtin_amdgcn_readfirstlane(indexer_units(a.seq_lens, a.B, gridDim.x * WPU, unit_off, scan_wsum));
+  const int ut = __builtin_amdgcn_readfirstlane(
+      indexer_units(a.seq_lens, a.B, gridDim.x * WPU, kUnitCap, unit_off, scan_wsum));
   const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
   const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
@@ -421,7 +430,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
         const int vis = L - a.Sq + 1 + tq;
         float v = (!KFP4 && a.k_scale) ? part * __uint_as_float(sig) : part;
         if (!valid || s >= vis) v = -INFINITY;
-        if (live && g == 0 && s < L) a.scores[((int64_t)b * a.Sq + tq) * a.score_stride + s] = v;
+        if (live && g == 0) sbuf[wave][(qq * kUnitCap + (t - t_begin)) * kTile + n] = v;
       }
       if (live && !valid && lane == 0 && rg == 0) count_error(a.err);
     };
@@ -431,6 +440,23 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
     for (int t = t_begin; t < t_end; t += kSlots) {
 #pragma unroll
       for (int k = 0; k < kSlots; ++k) compute(sl[k], t + k, k == 0 || t + k < t_end, t + k + kSlots);
+    }
+
+    // write the unit's scores: positions [t_begin * 32, min(t_end * 32, L)) of each query
+    const int s0 = t_begin * kTile;
+    const int ntok = min(t_end * kTile, L) - s0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int tq = rg * NQ + qq;
+      float* dst = a.scores + ((int64_t)b * a.Sq + tq) * a.score_stride + s0;
+      const float* src = &sbuf[wave][qq * kUnitCap * kTile];
+      int i0 = 0;
+      if (((uintptr_t)dst & 15) == 0) {
+        for (int i = lane * 4; i + 4 <= ntok; i += 256)
+          *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(src + i);
+        i0 = ntok & ~3;
+      }
+      for (int i = i0 + lane; i < ntok; i += 64) dst[i] = src[i];
     }
   }
 }
