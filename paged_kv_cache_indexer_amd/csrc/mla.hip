@@ -401,9 +401,38 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   }
 }
 
-// merge of split partials: 64 threads per (query row, head), 8 value dims per thread
+// merge of split partials: 64 threads per (query row, head), 8 value dims per thread.  With
+// SMAX > 0 (splits <= SMAX) every lse and partial load is issued before any is used, so a
+// thread waits for memory once; SMAX == 0 handles any split count.  F32: o and the partials
+// are float32, else bf16.
 constexpr int kMergeHeads = 4;   // heads per 256-thread work-group
+constexpr int kMergeUnrolled = 8;
 
+template <bool F32>
+__device__ __forceinline__ void merge_load(const void* part_o, int64_t pb, u32x4& v0, u32x4& v1) {
+  if constexpr (F32) {
+    v0 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(part_o) + pb);
+    v1 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(part_o) + pb + 4);
+  } else {
+    v0 = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(part_o) + pb);
+  }
+}
+
+template <bool F32>
+__device__ __forceinline__ void merge_add(float w, const u32x4& v0, const u32x4& v1, float* acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (F32) {
+      acc[i] += w * __uint_as_float(v0[i]);
+      acc[4 + i] += w * __uint_as_float(v1[i]);
+    } else {
+      acc[2 * i] += w * __uint_as_float(v0[i] << 16);
+      acc[2 * i + 1] += w * __uint_as_float(v0[i] & 0xffff0000u);
+    }
+  }
+}
+
+template <int SMAX, bool F32>
 __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) {
   const int qr = blockIdx.y;
   const int head = blockIdx.x * kMergeHeads + (threadIdx.x >> 6);
@@ -411,36 +440,53 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
   const int S = a.splits;
   const int d = (threadIdx.x & 63) * 8;
   const float* pl = a.part_lse + (int64_t)qr * S * a.H + head;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * a.H]);
-  float wsum = 0.0f;
+  const int64_t pbase = ((int64_t)qr * S * a.H + head) * kVDim + d;   // split s adds s * H * 512
+  const int64_t pstep = (int64_t)a.H * kVDim;
+  float mx = -INFINITY, wsum = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (mx > -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float l = pl[(int64_t)s * a.H];
-      const float w = (l == -INFINITY) ? 0.0f : __expf(l - mx);
-      wsum += w;
-      const int64_t pb = (((int64_t)qr * S + s) * a.H + head) * kVDim + d;
-      if (a.o_f32) {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + pb);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + pb + 4);
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += w * v0[i];
-          acc[4 + i] += w * v1[i];
-        }
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + pb);
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += w * __uint_as_float(v[i] << 16);
-          acc[2 * i + 1] += w * __uint_as_float(v[i] & 0xffff0000u);
-        }
+  if constexpr (SMAX > 0) {
+    float lv[SMAX];
+    u32x4 v0[SMAX], v1[SMAX];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      lv[s] = -INFINITY;
+      v0[s] = u32x4{};
+      v1[s] = u32x4{};
+      if (s < S) {
+        lv[s] = pl[(int64_t)s * a.H];
+        merge_load<F32>(a.part_o, pbase + s * pstep, v0[s], v1[s]);
       }
     }
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) mx = fmaxf(mx, lv[s]);
+    if (mx > -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        const float w = (lv[s] == -INFINITY) ? 0.0f : __expf(lv[s] - mx);
+        wsum += w;
+        merge_add<F32>(w, v0[s], v1[s], acc);
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * a.H]);
+    if (mx > -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float l = pl[(int64_t)s * a.H];
+        const float w = (l == -INFINITY) ? 0.0f : __expf(l - mx);
+        wsum += w;
+        u32x4 v0 = u32x4{}, v1 = u32x4{};
+        merge_load<F32>(a.part_o, pbase + s * pstep, v0, v1);
+        merge_add<F32>(w, v0, v1, acc);
+      }
+    }
+  }
+  if (mx > -INFINITY) {
     const float inv = 1.0f / wsum;
+#pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= inv;
   }
   const int64_t ob = ((int64_t)qr * a.H + head) * kVDim + d;
-  if (a.o_f32) {
+  if constexpr (F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ob) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ob + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   } else {
@@ -540,7 +586,14 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
     DSA_LAUNCH((mla_decode_kernel<1, 2>), grid, dim3(128), 0, stream, a);
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
-  DSA_LAUNCH(mla_merge_kernel, dim3((H + kMergeHeads - 1) / kMergeHeads, QR), dim3(64 * kMergeHeads), 0,
-                     stream, a);
+  const dim3 mgrid((H + kMergeHeads - 1) / kMergeHeads, QR);
+  const dim3 mblock(64 * kMergeHeads);
+  // (the unrolled fp32 variant needs four times the registers, so fp32 keeps the loop)
+  if (a.o_f32)
+    DSA_LAUNCH((mla_merge_kernel<0, true>), mgrid, mblock, 0, stream, a);
+  else if (splits <= kMergeUnrolled)
+    DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false>), mgrid, mblock, 0, stream, a);
+  else
+    DSA_LAUNCH((mla_merge_kernel<0, false>), mgrid, mblock, 0, stream, a);
   return launch_status("dsa_sparse_mla_decode(merge)");
 }
