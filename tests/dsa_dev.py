@@ -165,20 +165,26 @@ class DecodeStep:
                                   device=DEV)
         self.ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, k, L)), dtype=torch.uint8, device=DEV)
 
-    def run(self, stream, marks=None, layer=0):
+    def stage(self, name, stream, layer=0):
+        """Enqueue one stage ("indexer", "topk" or "mla") of the step on `stream`."""
         dw = self.dw
         keys, k_scale, rows = self.caches[layer % len(self.caches)]
-        if marks:
-            marks[0].record(stream)
-        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, keys, k_scale, dw.seq_lens, self.scores,
-                               k_dtype=dw.k_dtype, err=dw.err, q_dtype=dw.q_dtype, stream=stream)
-        if marks:
-            marks[1].record(stream)
-        dsa.dsa_topk(self.scores, dw.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
-        if marks:
-            marks[2].record(stream)
-        dsa.dsa_sparse_mla_decode(dw.mla_q, self.idx, rows, dw.wl.scale, self.o, self.lse, ws=self.ws_mla,
-                                  err=dw.err, stream=stream)
+        if name == "indexer":
+            dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, keys, k_scale, dw.seq_lens, self.scores,
+                                   k_dtype=dw.k_dtype, err=dw.err, q_dtype=dw.q_dtype, stream=stream)
+        elif name == "topk":
+            dsa.dsa_topk(self.scores, dw.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
+        elif name == "mla":
+            dsa.dsa_sparse_mla_decode(dw.mla_q, self.idx, rows, dw.wl.scale, self.o, self.lse, ws=self.ws_mla,
+                                      err=dw.err, stream=stream)
+        else:
+            raise ValueError(name)
+
+    def run(self, stream, marks=None, layer=0):
+        for j, name in enumerate(("indexer", "topk", "mla")):
+            if marks:
+                marks[j].record(stream)
+            self.stage(name, stream, layer)
         if marks:
             marks[3].record(stream)
 
