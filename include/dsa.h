@@ -127,7 +127,7 @@ const char* dsa_last_error(void);
  * MXFP4 block-scale codes: 0x00..0xFE with E4M3 queries (the scaled MFMA applies them);
  * 0x00..0xFE with BF16 queries as long as every scaled key element is a finite bf16
  * (|element| * 2^(c-127) < 2^128).  Code 0xFF (NaN) gives an unspecified score.
- * Out-of-range page ids: the affected tokens score -inf and count in err_count.
+ * Out-of-range page ids: the affected tokens score -inf, and each adds one to err_count.
  */
 dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
                                 const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,

@@ -49,8 +49,8 @@ dsa_status_t launch_status(const char* what);
   } while (0)
 
 // ---------------------------------------------------------------- device helpers
-__device__ __forceinline__ void count_error(int32_t* err) {
-  if (err) atomicAdd(err, 1);
+__device__ __forceinline__ void count_error(int32_t* err, int32_t n = 1) {
+  if (err) atomicAdd(err, n);
 }
 
 // Row address in a dsa_rows_t (paged or dense).  Returns nullptr if the page id or

@@ -432,7 +432,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
         if (!valid || s >= vis) v = -INFINITY;
         if (live && g == 0) sbuf[wave][(qq * kUnitCap + (t - t_begin)) * kTile + n] = v;
       }
-      if (live && !valid && lane == 0 && rg == 0) count_error(a.err);
+      // one error per unresolvable token (the tile's positions below L), as the fp32 path counts
+      if (live && !valid && lane == 0 && rg == 0) count_error(a.err, min(kTile, L - t * kTile));
     };
 
     // fixed-shape body: no exit between the fetches (tiles past the unit's end are computed

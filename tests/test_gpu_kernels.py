@@ -386,3 +386,36 @@ def test_decode_step_graph_replay_matches_eager():
         for got, want in zip((step.scores, step.idx, step.o, step.lse), ref):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}"
     assert int(dw.err) == 0
+
+
+@pytest.mark.parametrize("kind", ["grid_f32", "e4m3_scaled", "mxfp4"])
+def test_indexer_unresolvable_pages_score_neg_inf_and_count(kind):
+    """Page ids past the cache or negative: those tokens score -inf and each counts one
+    error; every other score is the oracle's."""
+    qk = "grid_f32" if kind == "grid_f32" else "bf16"
+    H = 4 if kind == "grid_f32" else 64
+    D = 64 if kind == "grid_f32" else 128
+    wk = "quarters" if kind == "grid_f32" else "u01_div64"      # quarters keep the fp32 grid exact
+    wl = synth.make_workload(synth.spec(2).scaled(B=2, L=1000, idx_heads=H, idx_dim=D, idx_q_kind=qk,
+                                                  idx_k_kind=kind, w_kind=wk), with_kv=False)
+    wl.seq_lens = np.array([1000, 700], dtype=np.int32)
+    ref = [o_idx.scores(wl, b) for b in range(wl.B)]          # oracle on the intact table
+    dw = DevWorkload(wl, with_kv=False)
+    pt = dw.page_table.clone()
+    pt[0, 3] = wl.num_pages + 7                               # past the cache
+    pt[1, 10] = -5                                            # negative (page 10 holds 700 - 640 = 60 tokens)
+    dw.page_table.copy_(pt)
+    got = dw.scores().cpu().numpy()
+    bad = {0: range(192, 256), 1: range(640, 700)}
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        want = ref[b].copy()
+        want[:, list(bad[b])] = -np.inf
+        g = got[b, :, :L]
+        assert np.array_equal(np.isneginf(g), np.isneginf(want)), b
+        fin = np.isfinite(want)
+        if kind == "grid_f32":
+            assert np.array_equal(g[fin], want[fin])
+        else:
+            assert np.allclose(g[fin], want[fin], rtol=1e-4, atol=1e-3 * np.abs(want[fin]).max())
+    assert int(dw.err) == 64 + 60
