@@ -281,39 +281,45 @@ def main():
 
 def bench_kv_write(args):
     """dsa_kv_write for the decode batch (B=32, one new token) and an MTP batch (B=8, four
-    new tokens): 64-token pages spread over a 64K-position cache, bf16 latent rows and keys."""
+    new tokens): 64-token pages spread over a 64K-position cache, bf16 latent rows and keys,
+    into an e4m3 and into an MXFP4 indexer cache."""
     import torch
     import paged_kv_cache_indexer_amd as dsa
     from tests.dsa_dev import HipMark
     res = []
-    for B, Sq in ((32, 1), (8, 4)):
+    for (B, Sq), cache in ((b_sq, c) for c in ("e4m3", "mxfp4") for b_sq in ((32, 1), (8, 4))):
         ps, L, D = 64, 65536, 128
+        fp4 = cache == "mxfp4"
         P = L // ps
         g = torch.Generator(device="cpu").manual_seed(7)
         pt = torch.randperm(B * P, generator=g).to(torch.int32).view(B, P).cuda()
         kv = torch.zeros(B * L, 576, dtype=torch.bfloat16, device="cuda")
-        ic = torch.zeros(B * L, D, dtype=torch.uint8, device="cuda")
-        isc = torch.zeros(B * L, dtype=torch.float32, device="cuda")
+        ic = torch.zeros(B * L, D // 2 if fp4 else D, dtype=torch.uint8, device="cuda")
+        isc = (torch.zeros(B * L, D // 32, dtype=torch.uint8, device="cuda") if fp4 else
+               torch.zeros(B * L, dtype=torch.float32, device="cuda"))
+        cd = dsa.DSA_MXFP4 if fp4 else dsa.DSA_E4M3
         lat = torch.randn(B, Sq, 576, generator=g).to(torch.bfloat16).cuda()
         keys = torch.randn(B, Sq, D, generator=g).to(torch.bfloat16).cuda()
         lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
-        kvr, icr = dsa.Rows(kv, 1152, pt, ps), dsa.Rows(ic, D, pt, ps)
+        kvr, icr = dsa.Rows(kv, 1152, pt, ps), dsa.Rows(ic, D // 2 if fp4 else D, pt, ps)
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
             for _ in range(args.warmup):
-                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream)
+                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream, cache_dtype=cd)
             torch.cuda.synchronize()
             e0, e1 = HipMark(), HipMark()
             e0.record(stream)
             for _ in range(args.steps):
-                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream)
+                dsa.dsa_kv_write(lat, keys, lens, kvr, icr, isc, err, stream=stream, cache_dtype=cd)
             e1.record(stream)
         torch.cuda.synchronize()
         assert int(err.item()) == 0
         us = e0.elapsed_ms(e1) / args.steps * 1e3
-        by = B * Sq * (1152 + 2 * D + 1152 + D + 4)     # read latent + key, write row + codes + scale
-        res.append({"batch": B, "new_tokens": Sq, "us_per_call": us, "algo_bytes": by, "GBps": by / us / 1e3})
+        # read latent + key, write row + codes + scales
+        by = B * Sq * (1152 + 2 * D + 1152 + (D // 2 + D // 32 if fp4 else D + 4))
+        res.append({"indexer_cache": cache, "batch": B, "new_tokens": Sq, "us_per_call": us, "algo_bytes": by,
+                    "GBps": by / us / 1e3})
     print(json.dumps({"metric": "dsa_kv_write us per call (back-to-back launches, HIP events)",
                       "entry": "dsa_kv_write", "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
                       "runs": res, "bound": "launch latency (a few KB per call)"}), flush=True)

@@ -13,7 +13,7 @@
  *   dsa_gather_kv          per-layer serve (pool / paged / host rows) and install  [GLM52] §4.4, §5
  *   dsa_sparse_mla_decode  MLA latent attention over the selected rows only        [TSA] "MLA", [GLM52] §2.1
  *   dsa_page_translate     page-sharded ownership closed form                      [HCCP] §1.1
- *   dsa_kv_write           new tokens' latent rows and e4m3 indexer keys into the
+ *   dsa_kv_write           new tokens' latent rows and e4m3 or MXFP4 indexer keys into the
  *                          paged caches (fused quantise + scatter)                 [TSA] "KV host tiering"
  *
  * Conventions shared by every call
@@ -276,20 +276,30 @@ dsa_status_t dsa_page_translate(const int64_t* x, int64_t n, int page_size, int 
  *     idx_scale[that row]     = sigma
  * A zero key stores sigma = 0 and zero codes (it dequantises to 0).  The pages do not fix
  * the key quantisation; this is the per-token-scale layout dsa_indexer_scores reads.
+ * With idx_cache_dtype = DSA_MXFP4 (the FP4 indexer cache, [TSA] "DSA", read as OCP MXFP4)
+ * the key is quantised per block j of 32 dimensions instead (OCP MX conversion):
+ *     code_j                  = clamp(floor(log2 max_{d in j} |idx_k[b,t,d]|) - 2 + 127, 0, 254)
+ *                               (0 for an all-zero block); X_j = 2^(code_j - 127)
+ *     element d               = nearest E2M1 value of idx_k[b,t,d] / X_j, ties to the even
+ *                               mantissa, magnitudes above 6 saturating to 6
+ *     idx_cache row of (b, p) = the D codes, element 2i in the low nibble of byte i
+ *     idx_scale[row][j]       = code_j
  *
  *   latent      [B, Sq, 576] bf16, 16-byte aligned
  *   idx_k       [B, Sq, D] bf16 or float32 (idx_k_dtype), 8-byte aligned; D even, <= 128
  *   kv          rows of the latent cache (row_bytes 1152, base 16-byte aligned), written
- *   idx_cache   rows of the indexer cache (row_bytes D, base 2-byte aligned), written; it may
- *               use its own page table
- *   idx_scale   [idx_cache rows] float32, written at each written row
+ *   idx_cache   rows of the indexer cache, written; it may use its own page table.
+ *               E4M3: row_bytes D, base 2-byte aligned.  MXFP4: row_bytes D / 2, D a
+ *               multiple of 32.
+ *   idx_scale   E4M3: [idx_cache rows] float32 (4-byte aligned); MXFP4: [idx_cache rows,
+ *               D / 32] uint8 E8M0 codes; written at each written row
  * A token whose position or page is out of range in either cache is skipped and counted
  * in err_count.  Two tokens mapping to the same row race (the caller's pages are distinct).
  */
 dsa_status_t dsa_kv_write(const void* latent, const void* idx_k, dsa_dtype_t idx_k_dtype,
                           const int32_t* seq_lens, int B, int Sq, int D, const dsa_rows_t* kv,
-                          const dsa_rows_t* idx_cache, float* idx_scale, int32_t* err_count,
-                          hipStream_t stream);
+                          const dsa_rows_t* idx_cache, dsa_dtype_t idx_cache_dtype, void* idx_scale,
+                          int32_t* err_count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

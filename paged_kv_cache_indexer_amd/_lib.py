@@ -61,7 +61,7 @@ def load() -> ctypes.CDLL:
                                                  vp]),
         "dsa_page_translate": (ctypes.c_int, [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]),
         "dsa_kv_write": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, prow,
-                                        prow, vp, vp, vp]),
+                                        prow, ctypes.c_int, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

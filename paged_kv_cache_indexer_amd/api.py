@@ -144,9 +144,12 @@ def dsa_page_translate(x: torch.Tensor, page_size: int, n_ranks: int, rank: torc
 
 
 def dsa_kv_write(latent: torch.Tensor, idx_k: torch.Tensor, seq_lens: torch.Tensor, kv: Rows, idx_cache: Rows,
-                 idx_scale: torch.Tensor, err: Optional[torch.Tensor] = None, stream=None):
-    """Quantise and scatter the new tokens ([B, Sq, 576] latent, [B, Sq, D] keys) into the caches."""
+                 idx_scale: torch.Tensor, err: Optional[torch.Tensor] = None, stream=None,
+                 cache_dtype: int = DSA_E4M3):
+    """Quantise and scatter the new tokens ([B, Sq, 576] latent, [B, Sq, D] keys) into the caches.
+    cache_dtype DSA_E4M3: float32 idx_scale per row; DSA_MXFP4: uint8 [rows, D/32] E8M0 scales."""
     B, Sq, D = idx_k.shape
     _check(_lib.load().dsa_kv_write(_ptr(latent), _ptr(idx_k), _dtype_code(idx_k), _ptr(seq_lens), B, Sq, D,
-                                    kv.ref(), idx_cache.ref(), _ptr(idx_scale), _ptr(err), _stream(stream)),
+                                    kv.ref(), idx_cache.ref(), cache_dtype, _ptr(idx_scale), _ptr(err),
+                                    _stream(stream)),
            "dsa_kv_write")

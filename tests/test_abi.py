@@ -58,13 +58,20 @@ def test_invalid_arguments_rejected_without_device():
     kv, ic = _lib.dsa_rows_t(), _lib.dsa_rows_t()
     kv.base, kv.row_bytes, ic.base, ic.row_bytes = 16, 1152, 16, 128
     p = ctypes.c_void_p(16)
-    assert L.dsa_kv_write(p, p, _lib.DSA_E4M3, p, 1, 1, 128, ctypes.byref(kv), ctypes.byref(ic), p, None,
+    E4, F4 = _lib.DSA_E4M3, _lib.DSA_MXFP4
+    assert L.dsa_kv_write(p, p, _lib.DSA_E4M3, p, 1, 1, 128, ctypes.byref(kv), ctypes.byref(ic), E4, p, None,
                           None) == _lib.DSA_ERR_INVALID_ARG          # keys must be bf16 or fp32
-    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 130, ctypes.byref(kv), ctypes.byref(ic), p, None,
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 130, ctypes.byref(kv), ctypes.byref(ic), E4, p, None,
                           None) == _lib.DSA_ERR_UNSUPPORTED          # D > 128
-    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 64, ctypes.byref(kv), ctypes.byref(ic), p, None,
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 64, ctypes.byref(kv), ctypes.byref(ic), E4, p, None,
                           None) == _lib.DSA_ERR_INVALID_ARG          # indexer rows must be D bytes
-    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 0, 1, 128, None, None, None, None, None) == _lib.DSA_OK
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 128, ctypes.byref(kv), ctypes.byref(ic), _lib.DSA_BF16, p,
+                          None, None) == _lib.DSA_ERR_INVALID_ARG    # the cache is e4m3 or mxfp4
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 128, ctypes.byref(kv), ctypes.byref(ic), F4, p, None,
+                          None) == _lib.DSA_ERR_INVALID_ARG          # mxfp4 rows must be D/2 bytes
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 1, 1, 48, ctypes.byref(kv), ctypes.byref(ic), F4, p, None,
+                          None) == _lib.DSA_ERR_UNSUPPORTED          # mxfp4 needs D % 32 == 0
+    assert L.dsa_kv_write(p, p, _lib.DSA_BF16, p, 0, 1, 128, None, None, E4, None, None, None) == _lib.DSA_OK
     # MXFP4 keys: 64-byte rows and a 4-byte aligned block-scale array are required
     k4 = _lib.dsa_rows_t()
     k4.base, k4.row_bytes, k4.num_rows = 16, 64, 64
