@@ -81,6 +81,25 @@ def test_decode_b32_ctx65536_full_step():
     print(f"top-k swaps against the oracle's selection: {swaps}")
 
 
+@pytest.mark.parametrize("cid", [2, 3])
+def test_full_step_over_the_fp4_indexer_cache(cid):
+    """The decode (B=32, 64K, bf16 queries) and MTP-verify (B=8, 200K, fp8 queries) steps
+    with MXFP4 indexer keys instead of e4m3, full size, sampled requests against the oracle."""
+    wl = synth.make_workload(synth.spec(cid).scaled(idx_k_kind="mxfp4"), with_kv=True)
+    dw = DevWorkload(wl)
+    step = DecodeStep(dw)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step.run(stream)
+    torch.cuda.synchronize()
+    assert int(dw.err) == 0
+    sc, idx = step.scores.cpu().numpy(), step.idx.cpu().numpy()
+    check_all_rows(wl, idx)
+    assert torch.isfinite(step.lse).all()
+    swaps = sum(check_request(wl, b, sc, idx, step.o, step.lse) for b in ((0, 31) if cid == 2 else (3,)))
+    print(f"top-k swaps against the oracle's selection: {swaps}")
+
+
 def test_mtp_verify_b8_ctx200k_full_step():
     """Four draft queries per request (fp8 queries, causal visibility), full size."""
     wl = synth.make_workload(3)
