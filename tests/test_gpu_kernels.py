@@ -419,3 +419,20 @@ def test_indexer_unresolvable_pages_score_neg_inf_and_count(kind):
         else:
             assert np.allclose(g[fin], want[fin], rtol=1e-4, atol=1e-3 * np.abs(want[fin]).max())
     assert int(dw.err) == 64 + 60
+
+
+# every MFMA instantiation: (heads, query tokens) x query dtype x key layout
+_SHAPES = [(32, 1), (32, 2), (32, 4), (32, 8), (64, 1), (64, 2), (64, 4), (128, 1), (128, 2)]
+
+
+@pytest.mark.parametrize("H,Sq", _SHAPES)
+@pytest.mark.parametrize("qk", ["bf16", "e4m3"])
+@pytest.mark.parametrize("keys", ["e4m3_scaled", "mxfp4"])
+def test_indexer_every_mfma_instantiation(H, Sq, qk, keys):
+    ps = {1: 64, 2: 32, 4: 128, 8: 32}[Sq]
+    wl = synth.make_workload(synth.spec(2).scaled(B=2, L=1300, Sq=Sq, idx_heads=H, idx_q_kind=qk,
+                                                  idx_k_kind=keys, page_size=ps, seed=H + Sq), with_kv=False)
+    wl.seq_lens = np.array([1300, 97 + Sq], dtype=np.int32)
+    dw = DevWorkload(wl, with_kv=False)
+    check_scores(wl, dw.scores())
+    assert int(dw.err) == 0
