@@ -218,7 +218,8 @@ def test_topk_batched_mtp_rows():
 
 
 # ------------------------------------------------------------------ sparse MLA
-@pytest.mark.parametrize("H,k,L", [(128, 2048, 3000), (16, 256, 4096), (64, 300, 700), (128, 100, 100)])
+@pytest.mark.parametrize("H,k,L", [(128, 2048, 3000), (16, 256, 4096), (64, 300, 700), (128, 100, 100),
+                                   (32, 512, 2000), (48, 300, 1000)])
 def test_mla_against_oracle(H, k, L):
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=L, mla_heads=H, topk=k))
     rng = np.random.default_rng(H + k)
