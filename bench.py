@@ -26,27 +26,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 KEY_BYTES = {"e4m3": lambda D: D + 4,          # e4m3 codes + float32 per-token scale
              "mxfp4": lambda D: D // 2 + D // 32}  # E2M1 codes + E8M0 block scales
 
 
-def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3"):
-    """Bytes / flops each kernel must move or compute for one layer-step (no re-reads)."""
-    idx_bytes = (B * L * KEY_BYTES[keys](D)  # keys and their scales
-                 + B * H_idx * D * 2  # bf16 queries
-                 + B * H_idx * 4      # head weights
+def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2):
+    """Bytes / flops each kernel must move or compute for one layer-step (no re-reads); Sq
+    query tokens per request, each scoring the whole cache and attending its own top-k."""
+    Q = B * Sq
+    idx_bytes = (B * L * KEY_BYTES[keys](D)  # keys and their scales, read once for all Sq queries
+                 + Q * H_idx * D * q_bytes  # queries
+                 + Q * H_idx * 4      # head weights
                  + B * (L // ps) * 4  # page table
-                 + B * L * 4)         # scores out
-    idx_flops = 2 * B * H_idx * D * L
-    topk_bytes = B * L * 4 + B * k * 4
-    mla_bytes = (B * k * 1152         # selected latent rows
-                 + B * H_mla * 576 * 2  # q
-                 + B * k * 4          # indices
-                 + B * H_mla * 512 * 2  # o (bf16)
-                 + B * H_mla * 4)     # lse
-    mla_flops = 2 * B * H_mla * k * (576 + 512)
+                 + Q * L * 4)         # scores out
+    idx_flops = 2 * Q * H_idx * D * L
+    topk_bytes = Q * L * 4 + Q * k * 4
+    mla_bytes = (Q * k * 1152         # selected latent rows
+                 + Q * H_mla * 576 * 2  # q
+                 + Q * k * 4          # indices
+                 + Q * H_mla * 512 * 2  # o (bf16)
+                 + Q * H_mla * 4)     # lse
+    mla_flops = 2 * Q * H_mla * k * (576 + 512)
     return {"indexer": (idx_bytes, idx_flops), "topk": (topk_bytes, 0), "mla": (mla_bytes, mla_flops)}
 
 
@@ -174,6 +177,9 @@ def main():
                     help="distinct per-layer caches the steps rotate through (a model's successive layers "
                          "read different caches; rotating keeps a step from hitting the previous step's "
                          "bytes in the 256 MB last-level cache)")
+    ap.add_argument("--config", type=int, choices=[2, 3], default=2,
+                    help="2: the decode workload (B=32, 64K context, one query token); 3: MTP verify (B=8, "
+                         "200K context, 4 query tokens with fp8 queries), printed as its own line")
     ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
     ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
@@ -201,7 +207,8 @@ def main():
         torch.cuda.set_device(0)
         bench_pool_group(args)
         return
-    wl = synth.make_workload(synth.spec(2).scaled(idx_k_kind="mxfp4") if args.keys == "mxfp4" else 2)
+    cfg = synth.spec(args.config)
+    wl = synth.make_workload(cfg.scaled(idx_k_kind="mxfp4") if args.keys == "mxfp4" else cfg)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)     # forks: before any GPU call
     torch.cuda.set_device(0)
     dw = DevWorkload(wl)
@@ -263,26 +270,33 @@ def main():
         per[n] = m0.elapsed_ms(m1) * 1e-3 / args.steps             # seconds per launch
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
 
-    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys)
+    fp8_q = wl.idx_q_dtype == "e4m3"                 # the indexer then runs on the fp8 MFMA
+    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys, Sq=Sq,
+                            q_bytes=1 if fp8_q else 2)
+    peak = {"indexer": FP8_PEAK_TFLOPS if fp8_q else BF16_PEAK_TFLOPS, "topk": BF16_PEAK_TFLOPS,
+            "mla": BF16_PEAK_TFLOPS}
     kernels = {}
     for n in names:
         by, fl = work[n]
         kernels[n] = {"avg_us": per[n] * 1e6, "algo_bytes": by, "algo_flops": fl,
                       "GBps": by / per[n] / 1e9, "hbm_frac": by / per[n] / 1e9 / HBM_PEAK_GBS,
-                      "TFLOPs": fl / per[n] / 1e12, "bf16_mfma_frac": fl / per[n] / 1e12 / BF16_PEAK_TFLOPS}
-    # step roofline: sum over the kernels of their time at peak (bytes at 8 TB/s or bf16 flops
-    # at 2.5 PF/s, whichever is longer) over the measured step time
-    t_star = sum(max(work[n][0] / (HBM_PEAK_GBS * 1e9), work[n][1] / (BF16_PEAK_TFLOPS * 1e12)) for n in names)
+                      "TFLOPs": fl / per[n] / 1e12, "mfma_dtype": "fp8" if (n == "indexer" and fp8_q) else "bf16",
+                      "mfma_frac": fl / per[n] / 1e12 / peak[n]}
+    # step roofline: sum over the kernels of their time at peak (bytes at 8 TB/s or flops at
+    # the MFMA peak of their dtype, whichever is longer) over the measured step time
+    t_star = sum(max(work[n][0] / (HBM_PEAK_GBS * 1e9), work[n][1] / (peak[n] * 1e12)) for n in names)
     dom = max(names, key=lambda n: per[n])
     by = work[dom][0]
     roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS,
-                "traffic": measured_traffic(dom + ("_mxfp4" if dom == "indexer" and args.keys == "mxfp4" else "")),
+                "traffic": (measured_traffic(dom + ("_mxfp4" if dom == "indexer" and args.keys == "mxfp4" else ""))
+                            if args.config == 2 else None),
                 "kernel": dom}
 
     ms = wall / args.steps * 1e3
     out = {
-        "metric": "DSA decode layer-steps/s (B=32, 64K ctx, top-2048); % HBM/MFMA roofline",
+        "metric": ("DSA decode layer-steps/s (B=32, 64K ctx, top-2048); % HBM/MFMA roofline" if args.config == 2 else
+                   "DSA MTP-verify layer-steps/s (B=8, 200K ctx, 4 query tokens, top-2048); % HBM/MFMA roofline"),
         "value": args.steps / wall,
         "unit": "layer-steps/s",
         "n_gpus": 1,
@@ -292,13 +306,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not fp8_q else "fp8 indexer, bf16 attention",
         "data": ("synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)" if args.keys == "e4m3" else
                  "synthetic (seeded N(0,1); MXFP4 keys drawn as uniform codes, E8M0 in 124..128; random page "
                  "permutation)"),
         "launch": mode,
         "kernel_timing": "per stage: HIP events on the launch stream around K back-to-back launches of that stage",
-        "config": {"workload": "decode_b32_ctx65536_top2048", "batch": B, "context": L, "query_tokens": Sq,
+        "config": {"workload": ("decode_b32_ctx65536_top2048" if args.config == 2 else
+                                "mtp_verify_b8_ctx200004_sq4_top2048"), "batch": B, "context": L, "query_tokens": Sq,
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
                    "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "layers_rotated": args.layers,
                    "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},

@@ -203,12 +203,13 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
   constexpr int kStageStride = kRowBytes + 16;                        // key rows, padded
   __shared__ __attribute__((aligned(16))) char kstage[4][kTile * kStageStride];
-  // A unit's scores are staged here and written after its last tile.  Stores share the
-  // vector-memory counter with loads, so a score store issued inside the tile loop made every
-  // later wait for key data also wait for that store's write acknowledgement (measured:
-  // 55.8 us with per-tile stores, 49.2 us without stores).
-  constexpr int kUnitCap = kMaxUnit / NQ;          // tiles per unit: NQ * kUnitCap * 32 scores per wave
-  static_assert(kUnitCap % kSlots == 0, "a unit is whole passes over the register slots");
+  // Scores are staged here, kBufTiles tiles per query, and written when the buffer is full or
+  // the unit ends (with one query per wave, once per unit).  Stores share the vector-memory
+  // counter with loads, so a score store issued inside the tile loop made every later wait
+  // for key data also wait for that store's write acknowledgement (measured: 55.8 us with
+  // per-tile stores, 49.2 us without stores).
+  constexpr int kBufTiles = kMaxUnit / NQ;         // NQ * kBufTiles * 32 scores per wave
+  static_assert(kBufTiles % kSlots == 0, "a buffer is whole passes over the register slots");
   __shared__ __attribute__((aligned(16))) float sbuf[4][kMaxUnit * kTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -222,7 +223,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
 
   __shared__ int scan_wsum[4];
   const int ut = __builtin_amdgcn_readfirstlane(
-      indexer_units(a.seq_lens, a.B, gridDim.x * WPU, kUnitCap, unit_off, scan_wsum));
+      indexer_units(a.seq_lens, a.B, gridDim.x * WPU, kMaxUnit, unit_off, scan_wsum));
   const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
   const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
@@ -430,35 +431,44 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
         const int vis = L - a.Sq + 1 + tq;
         float v = (!KFP4 && a.k_scale) ? part * __uint_as_float(sig) : part;
         if (!valid || s >= vis) v = -INFINITY;
-        if (live && g == 0) sbuf[wave][(qq * kUnitCap + (t - t_begin)) * kTile + n] = v;
+        if (live && g == 0) sbuf[wave][(qq * kBufTiles + (t - t_begin) % kBufTiles) * kTile + n] = v;
       }
       // one error per unresolvable token (the tile's positions below L), as the fp32 path counts
       if (live && !valid && lane == 0 && rg == 0) count_error(a.err, min(kTile, L - t * kTile));
     };
 
+    // write the staged scores of tiles [t_lo, t_hi): positions [t_lo * 32, min(t_hi * 32, L))
+    // of each query; t_lo is the first tile of its buffer fill
+    auto flush = [&](int t_lo, int t_hi) {
+      const int s0 = t_lo * kTile;
+      const int ntok = min(t_hi * kTile, L) - s0;
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const int tq = rg * NQ + qq;
+        float* dst = a.scores + ((int64_t)b * a.Sq + tq) * a.score_stride + s0;
+        const float* src = &sbuf[wave][qq * kBufTiles * kTile];
+        int i0 = 0;
+        if (((uintptr_t)dst & 15) == 0) {
+          for (int i = lane * 4; i + 4 <= ntok; i += 256)
+            *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(src + i);
+          i0 = ntok & ~3;
+        }
+        for (int i = i0 + lane; i < ntok; i += 64) dst[i] = src[i];
+      }
+    };
+
     // fixed-shape body: no exit between the fetches (tiles past the unit's end are computed
     // from the clamped tile and not stored)
+    int t_flushed = t_begin;
     for (int t = t_begin; t < t_end; t += kSlots) {
 #pragma unroll
       for (int k = 0; k < kSlots; ++k) compute(sl[k], t + k, k == 0 || t + k < t_end, t + k + kSlots);
-    }
-
-    // write the unit's scores: positions [t_begin * 32, min(t_end * 32, L)) of each query
-    const int s0 = t_begin * kTile;
-    const int ntok = min(t_end * kTile, L) - s0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      const int tq = rg * NQ + qq;
-      float* dst = a.scores + ((int64_t)b * a.Sq + tq) * a.score_stride + s0;
-      const float* src = &sbuf[wave][qq * kUnitCap * kTile];
-      int i0 = 0;
-      if (((uintptr_t)dst & 15) == 0) {
-        for (int i = lane * 4; i + 4 <= ntok; i += 256)
-          *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(src + i);
-        i0 = ntok & ~3;
+      if (t + kSlots - t_flushed == kBufTiles && t + kSlots < t_end) {   // buffer full, unit goes on
+        flush(t_flushed, t + kSlots);
+        t_flushed = t + kSlots;
       }
-      for (int i = i0 + lane; i < ntok; i += 64) dst[i] = src[i];
     }
+    flush(t_flushed, t_end);
   }
 }
 

@@ -224,3 +224,20 @@ def test_pool_group_b16_ctx128k_full_trajectory():
         hits.append(int(hit_np.sum()))
     print("pool hits per step (of %d):" % (B * k), hits)
     assert hits[0] == 0 and min(hits[1:]) > 0
+
+
+def test_indexer_long_units_flush_scores_mid_unit():
+    """8 query tokens x 32 heads over 150K-token caches: units of about 38 tiles against a
+    score buffer of 16 tiles per query, so every wave writes its staged scores mid-unit."""
+    wl = synth.make_workload(synth.spec(3).scaled(L=150000, Sq=8, idx_heads=32), with_kv=False)
+    dw = DevWorkload(wl, with_kv=False)
+    sc = dw.scores().cpu().numpy()
+    assert int(dw.err) == 0
+    for b in (0, 5):
+        L = int(wl.seq_lens[b])
+        ref = o_idx.scores(wl, b)
+        for t in range(wl.Sq):
+            n = o_idx.visible_len(L, wl.Sq, t)
+            bound = indexer_bound(wl, b, t, n)
+            assert (np.abs(sc[b, t, :n].astype(np.float64) - ref[t, :n].astype(np.float64)) <= bound).all(), (b, t)
+            assert np.isneginf(sc[b, t, n:L]).all()
