@@ -326,7 +326,12 @@ extern "C" dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int3
                       "dsa_plan: needs Sq*k <= 8192, n_sets <= 4096, ways <= 64");
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan_smem());
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan_smem());
+    if (e != hipSuccess) {
+      set_last_error("dsa_plan: hipFuncSetAttribute: %s", hipGetErrorString(e));
+      return DSA_ERR_HIP;
+    }
     attr = true;
   }
   PlanArgs args{topk, Sq, k, pool_ids, id_to_slot, ptr, n_sets, ways, id_range, is_hit, slot,

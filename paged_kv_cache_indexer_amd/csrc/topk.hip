@@ -4,7 +4,8 @@
 // Order: score descending, then position ascending; -0.0 == +0.0.  Scores map to
 // order-preserving uint32 keys.
 //
-// Stage 1 (one work-group per chunk of kChunk positions of a row): chunk c (len_c
+// Stage 1 (one work-group per chunk of a row's positions, 8192 or, when the grid would
+// otherwise take more than one round of the chip's work-group slots, 16384): chunk c (len_c
 // positions) keeps its r_c = min(len_c, 2 ceil(k len_c / n)) best keys as candidates, in
 // position order, and records a cut key X_c: every key it left out is <= X_c, and one
 // equal to X_c sits after every kept key equal to it.  The chunks' candidates are written
@@ -29,7 +30,11 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kPer = 8;                            // keys per thread held in registers
 constexpr int kChunk = kTopkThreads * kPer;        // stage-1 chunk: 8192 positions
+constexpr int kLongPer = 16;                       // keys per thread of the long-row chunks
 constexpr int kMaxChunks = 256;                    // rows up to 2^21 positions
+// Stage-1 work-groups that run in one round: 256 CUs x 2 work-groups of 1024 threads (the
+// chunk kernel fits eight waves per SIMD).  A larger grid switches to 16384-position chunks.
+constexpr int64_t kChunkRound = 512;
 constexpr int kMaxCand = kTopkThreads * kPer;      // stage-2 candidates held in registers
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
@@ -236,7 +241,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 struct alignas(16) RadixShared {
   uint32_t hist[2][kBins];                 // digit histograms, alternating per pass
   uint32_t red[2 * kTopkWaves];            // per-wave min / max, then per-wave digit counts
-  int cnt[kPer * kTopkWaves];              // ordered take: packed counts per (slot q, wave)
+  int cnt[kLongPer * kTopkWaves];          // ordered take: packed counts per (slot q, wave)
   uint32_t sel_digit;
   int sel_above;
   int sel_count;
@@ -377,21 +382,32 @@ __device__ void take_reg(const uint32_t (&key)[PER], uint32_t T, int need, Radix
     }
   }
   __syncthreads();
-  int slot[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {                  // slot of each kept key, -1 if not kept
+  auto slot_of = [&](int q, uint64_t gt, uint64_t eq) {   // slot of a kept key, -1 if not kept
     const int base = __builtin_amdgcn_readfirstlane(sh.cnt[q * kTopkWaves + wave]);
-    const int gb = lanes_below(gtm[q], base & 0xffff);
-    if (eqm[q] == 0) {                             // no key == T in this wave's slot q
-      slot[q] = key[q] > T ? gb + min(need, base >> 16) : -1;
-    } else {
-      const int eb = lanes_below(eqm[q], base >> 16);
-      slot[q] = key[q] > T ? gb + min(need, eb) : ((key[q] == T && eb < need) ? gb + eb : -1);
+    const int gb = lanes_below(gt, base & 0xffff);
+    if (eq == 0)                                   // no key == T in this wave's slot q
+      return key[q] > T ? gb + min(need, base >> 16) : -1;
+    const int eb = lanes_below(eq, base >> 16);
+    return key[q] > T ? gb + min(need, eb) : ((key[q] == T && eb < need) ? gb + eb : -1);
+  };
+  if constexpr (PER <= kPer) {
+    int slot[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) slot[q] = slot_of(q, gtm[q], eqm[q]);
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (slot[q] >= 0) EMIT(slot[q], q);
+  } else {
+    // sixteen keys per thread: the ballots are taken again here rather than held across the
+    // scan, which keeps the kernel within the registers of eight waves per SIMD
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const uint64_t gt = __builtin_amdgcn_ballot_w64(key[q] > T);
+      const uint64_t eq = need > 0 ? __builtin_amdgcn_ballot_w64(key[q] == T) : 0ull;
+      const int s = slot_of(q, gt, eq);
+      if (s >= 0) EMIT(s, q);
     }
   }
-#pragma unroll
-  for (int q = 0; q < PER; ++q)
-    if (slot[q] >= 0) EMIT(slot[q], q);
 }
 
 struct TopkArgs {
@@ -399,6 +415,7 @@ struct TopkArgs {
   int64_t stride;
   const int32_t* seq_lens;
   int Sq, k;
+  int chunk;          // positions per stage-1 chunk: kTopkThreads * (kPer or kLongPer)
   int max_chunks;     // chunk slots per row
   int cand_stride;    // candidate slots per row (>= the sum of the r_c)
   uint32_t* xc;       // [rows, max_chunks] cut key of each chunk
@@ -420,28 +437,36 @@ __device__ __forceinline__ int chunk_keep(int k, int len, int n) {
   return min(len, 2 * share);
 }
 
-// stage 1, grid (max_chunks, rows).  Chunk c's candidates start at c * r_full in the row's
-// list (r_full: the keep of a full chunk; only the last chunk can be shorter).
-__global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
+// stage 1, grid (max_chunks, rows), PER keys per thread (a.chunk = kTopkThreads * PER).
+// Chunk c's candidates start at c * r_full in the row's list (r_full: the keep of a full
+// chunk; only the last chunk can be shorter).  Eight waves per SIMD (two work-groups per
+// CU) for either PER: with sixteen keys the compiler keeps a few scalars in VGPR lanes.
+template <int PER>
+__global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+topk_chunk_kernel(TopkArgs a) {
+  constexpr int kC = kTopkThreads * PER;
   __shared__ RadixShared sh;
   const int row = blockIdx.y, c = blockIdx.x;
-  const int lo = c * kChunk;
+  const int lo = c * kC;
   if (lo >= a.stride) return;
   // the loads are clamped to the row's stride, not its length, so they issue before the
   // length arrives; positions past the length are masked below
-  const float* src = a.scores + (int64_t)row * a.stride;
-  float v[kPer];
+  // 32-bit byte offsets from the row's base (the row holds < 2^21 positions): one VGPR per load
+  const char* src = reinterpret_cast<const char*>(a.scores + (int64_t)row * a.stride);
+  const int last = (int)a.stride - 1;
+  float v[PER];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) v[q] = src[min((int64_t)(lo + q * kTopkThreads + (int)threadIdx.x), a.stride - 1)];
+  for (int q = 0; q < PER; ++q)
+    v[q] = *reinterpret_cast<const float*>(src + (uint32_t)min(lo + q * kTopkThreads + (int)threadIdx.x, last) * 4u);
   const int n = row_len(a, row);
   if (n <= a.k) return;                       // stage 2 writes 0..n-1 directly
   if (lo >= n) return;
-  const int len = min(kChunk, n - lo);
+  const int len = min(kC, n - lo);
   const int r = chunk_keep(a.k, len, n);
-  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kChunk, n);
-  uint32_t key[kPer], kmin = 0xffffffffu, kmax = 0;
+  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kC, n);
+  uint32_t key[PER], kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {                 // empty slots: key 0
+  for (int q = 0; q < PER; ++q) {                  // empty slots: key 0
     const bool in = q * kTopkThreads + (int)threadIdx.x < len;
     key[q] = in ? float_key(v[q]) : 0u;
     kmin = min(kmin, in ? key[q] : 0xffffffffu);
@@ -451,15 +476,15 @@ __global__ void __launch_bounds__(kTopkThreads) topk_chunk_kernel(TopkArgs a) {
   uint32_t T;
   if (r >= len) {                              // the whole chunk is kept; X_c = its smallest key
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
+    for (int q = 0; q < PER; ++q) {
       const int i = q * kTopkThreads + threadIdx.x;
       if (i < len) out[i] = make_uint2(key[q], (uint32_t)(lo + i));
     }
     T = kmin;
   } else {
     int need;
-    radix_select_reg<kPer>(key, r, kmin, kmax, sh, T, need);
-    take_reg<kPer>(key, T, need, sh, [&](int slot, int q) {
+    radix_select_reg<PER>(key, r, kmin, kmax, sh, T, need);
+    take_reg<PER>(key, T, need, sh, [&](int slot, int q) {
       if (slot < r) out[slot] = make_uint2(key[q], (uint32_t)(lo + q * kTopkThreads + (int)threadIdx.x));
     });
   }
@@ -532,16 +557,17 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
     return;
   }
   const float* src = a.scores + (int64_t)row * a.stride;
-  const int nch = (n + kChunk - 1) / kChunk;
+  const int chunk = a.chunk;
+  const int nch = (n + chunk - 1) / chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r_full = chunk_keep(a.k, kChunk, n);
-  const int n_cand = (nch - 1) * r_full + chunk_keep(a.k, n - (nch - 1) * kChunk, n);
+  const int r_full = chunk_keep(a.k, chunk, n);
+  const int n_cand = (nch - 1) * r_full + chunk_keep(a.k, n - (nch - 1) * chunk, n);
   // thread t < nch: chunk t's cut key, keep, and whether it left keys out
   uint32_t x_t = 0;
   int r_t = 0;
   bool cut_t = false;
   if ((int)threadIdx.x < nch) {
-    const int len_t = min(kChunk, n - (int)threadIdx.x * kChunk);
+    const int len_t = min(chunk, n - (int)threadIdx.x * chunk);
     x_t = x_ld;
     r_t = chunk_keep(a.k, len_t, n);
     cut_t = r_t < len_t;
@@ -639,8 +665,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   }
 }
 
-static void topk_geometry(int64_t stride, int k, int& max_chunks, int& cand_stride) {
-  max_chunks = (int)((stride + kChunk - 1) / kChunk);
+static void topk_geometry(int64_t stride, int k, int chunk, int& max_chunks, int& cand_stride) {
+  max_chunks = (int)((stride + chunk - 1) / chunk);
   // sum over chunks of min(len_c, 2 ceil(k len_c / n)) <= min(n, 2k + 2 * chunks)
   cand_stride = (int)std::min<int64_t>(stride, 2 * (int64_t)k + 2 * (int64_t)max_chunks);
 }
@@ -649,8 +675,10 @@ static void topk_geometry(int64_t stride, int k, int& max_chunks, int& cand_stri
 
 extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
   if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
+  // the 8192-position geometry; the 16384-position one needs no more (half the chunk
+  // slots, no more candidate slots)
   int max_chunks, cand_stride;
-  dsa::topk_geometry(score_stride, k, max_chunks, cand_stride);
+  dsa::topk_geometry(score_stride, k, dsa::kChunk, max_chunks, cand_stride);
   return (size_t)B * Sq * ((size_t)cand_stride * sizeof(uint2) + (size_t)max_chunks * sizeof(uint32_t));
 }
 
@@ -671,7 +699,10 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   a.seq_lens = seq_lens;
   a.Sq = Sq;
   a.k = k;
-  topk_geometry(score_stride, k, a.max_chunks, a.cand_stride);
+  const int64_t grid8 = (int64_t)B * Sq * ((score_stride + kChunk - 1) / kChunk);
+  const bool long_chunks = grid8 > kChunkRound;
+  a.chunk = long_chunks ? kTopkThreads * kLongPer : kChunk;
+  topk_geometry(score_stride, k, a.chunk, a.max_chunks, a.cand_stride);
   const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
   if (ws == nullptr || ws_bytes < need) {
     set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
@@ -684,11 +715,19 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   a.idx = idx;
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)(kSelectLds * sizeof(uint32_t)));
+    const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kSelectLds * sizeof(uint32_t)));
+    if (e != hipSuccess) {
+      set_last_error("dsa_topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
+      return DSA_ERR_HIP;
+    }
     attr = true;
   }
-  DSA_LAUNCH(topk_chunk_kernel, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
+  if (long_chunks)
+    DSA_LAUNCH(topk_chunk_kernel<kLongPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
+  else
+    DSA_LAUNCH(topk_chunk_kernel<kPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
   dsa_status_t st = launch_status("dsa_topk(chunk)");
   if (st != DSA_OK) return st;
   DSA_LAUNCH(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);

@@ -203,6 +203,48 @@ def test_topk_standalone_bit_exact(case):
     assert np.array_equal(idx.cpu().numpy()[0, 0], o_topk.select(s, k))
 
 
+def _long_chunk_rows(stride):
+    """Rows of a batch whose 8192-position chunks would take more than 512 work-groups, so
+    the chunk stage runs with 16384 positions per chunk."""
+    rng = np.random.default_rng(21)
+    s = np.zeros((6, 1, stride), dtype=np.float32)
+    lens = np.array([stride, 300000, 16385, 2000, 32769, 200004], dtype=np.int32)
+    s[0, 0] = rng.standard_normal(stride)
+    s[1, 0, :lens[1]] = np.sort(rng.standard_normal(lens[1]))        # answer in the last chunk
+    s[2, 0, :lens[2]] = rng.integers(-50, 50, lens[2])                 # ties; one past a boundary
+    s[3, 0, :lens[3]] = rng.standard_normal(lens[3])                   # n <= k
+    s[4, 0, :lens[4]] = 3.25                                           # all equal
+    s[5, 0, :lens[5]] = rng.standard_normal(lens[5]) * 1e-3 + 5.0      # close values
+    return s, lens
+
+
+@pytest.mark.parametrize("k", [2048, 8192])
+def test_topk_long_rows_use_16k_chunks_bit_exact(k):
+    stride = 1_100_000                                  # 135 chunks of 8192 per row, 6 rows
+    assert 6 * -(-stride // 8192) > 512
+    s, lens = _long_chunk_rows(stride)
+    idx = torch.empty((6, 1, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
+    got = idx.cpu().numpy()
+    for b in range(6):
+        assert np.array_equal(got[b, 0], o_topk.select(s[b, 0, :lens[b]], k)), b
+
+
+def test_topk_long_chunk_grid_mtp_rows():
+    rng = np.random.default_rng(5)
+    B, Sq, Lmax, k = 40, 4, 24600, 512                  # 160 rows x 4 chunks of 8192
+    lens = rng.integers(400, Lmax + 1, B).astype(np.int32)
+    lens[:3] = [Lmax, 515, 16387]
+    s = rng.integers(0, 300, (B, Sq, Lmax)).astype(np.float32)
+    idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        for t in range(Sq):
+            n = o_idx.visible_len(lens[b], Sq, t)
+            assert np.array_equal(got[b, t], o_topk.select(s[b, t, :n], k)), (b, t)
+
+
 def test_topk_batched_mtp_rows():
     rng = np.random.default_rng(3)
     B, Sq, Lmax, k = 5, 4, 16390, 512
