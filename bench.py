@@ -101,7 +101,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.j
 ENTRY_KERNELS = {
     "indexer": (["void dsa::indexer_mfma_kernel<false, false, 2, 1, 1>"], ["indexer.hip"]),
     "indexer_mxfp4": (["void dsa::indexer_mfma_kernel<false, true, 2, 1, 1>"], ["indexer.hip"]),
-    "topk": (["dsa::topk_chunk_kernel", "dsa::topk_select_kernel"], ["topk.hip"]),
+    "topk": (["void dsa::topk_chunk_kernel<", "dsa::topk_select_kernel"], ["topk.hip"]),
     "mla": (["void dsa::mla_decode_kernel<", "void dsa::mla_merge_kernel<"], ["mla.hip"]),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0   # counter KiB -> bytes/1024, from a 256 MiB device copy

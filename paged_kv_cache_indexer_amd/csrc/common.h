@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dsa.h"
 
 namespace dsa {
@@ -39,6 +41,15 @@ dsa_status_t launch_status(const char* what);
     (void)hipGetLastError();                    \
     hipLaunchKernelGGL(__VA_ARGS__);            \
   } while (0)
+
+// Host-side launch parameters (CU counts, occupancy grids, kernel attributes set) are cached
+// per device: slot = the current device's id, or -1 past kMaxDevices (then nothing is
+// cached).  Concurrent first calls may both compute the value; they store the same one.
+constexpr int kMaxDevices = 64;
+inline int current_device_slot() {
+  int d = -1;
+  return (hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxDevices) ? d : -1;
+}
 
 #define DSA_CHECK_SUPPORTED(cond, ...)          \
   do {                                          \

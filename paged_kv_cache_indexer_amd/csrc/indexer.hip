@@ -474,16 +474,20 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
 
 template <bool QFP8, bool KFP4, int HMT, int NQ, int RG>
 static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
-  static int grid = 0;
+  static std::atomic<int> grid_by_dev[kMaxDevices];
+  const int slot = current_device_slot();
+  int grid = slot >= 0 ? grid_by_dev[slot].load(std::memory_order_relaxed) : 0;
   if (grid == 0) {
-    int dev = 0, cus = 256, per_cu = 1;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 256, per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, slot < 0 ? 0 : slot) != hipSuccess ||
+        cus < 1)
+      cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>, 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     grid = cus * per_cu;
+    if (slot >= 0) grid_by_dev[slot].store(grid, std::memory_order_relaxed);
   }
   DSA_LAUNCH((indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
   return launch_status("dsa_indexer_scores");

@@ -501,11 +501,14 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
 }
 
 static int device_cus() {
-  static int cus = 0;
+  static std::atomic<int> cus_by_dev[kMaxDevices];
+  const int slot = current_device_slot();
+  int cus = slot >= 0 ? cus_by_dev[slot].load(std::memory_order_relaxed) : 0;
   if (cus == 0) {
-    int dev = 0;
-    hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, slot < 0 ? 0 : slot) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (slot >= 0) cus_by_dev[slot].store(cus, std::memory_order_relaxed);
   }
   return cus;
 }

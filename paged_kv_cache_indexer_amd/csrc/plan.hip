@@ -324,15 +324,16 @@ extern "C" dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int3
   DSA_CHECK_SUPPORTED(Sq * k <= kPlanMaxE && n_sets <= kPlanMaxSets && ways <= 64 &&
                           (int64_t)n_sets * ways <= (1 << 24),
                       "dsa_plan: needs Sq*k <= 8192, n_sets <= 4096, ways <= 64");
-  static bool attr = false;
-  if (!attr) {
+  static std::atomic<bool> attr_by_dev[kMaxDevices];
+  const int dev_slot = current_device_slot();
+  if (dev_slot < 0 || !attr_by_dev[dev_slot].load(std::memory_order_relaxed)) {
     const hipError_t e =
         hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan_smem());
     if (e != hipSuccess) {
       set_last_error("dsa_plan: hipFuncSetAttribute: %s", hipGetErrorString(e));
       return DSA_ERR_HIP;
     }
-    attr = true;
+    if (dev_slot >= 0) attr_by_dev[dev_slot].store(true, std::memory_order_relaxed);
   }
   PlanArgs args{topk, Sq, k, pool_ids, id_to_slot, ptr, n_sets, ways, id_range, is_hit, slot,
                 miss_pos, miss_slot, miss_count, commit, err_count};

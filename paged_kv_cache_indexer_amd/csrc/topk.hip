@@ -713,8 +713,9 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   a.cand = static_cast<uint2*>(ws);
   a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.cand_stride);
   a.idx = idx;
-  static bool attr = false;
-  if (!attr) {
+  static std::atomic<bool> attr_by_dev[kMaxDevices];
+  const int slot = current_device_slot();
+  if (slot < 0 || !attr_by_dev[slot].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)(kSelectLds * sizeof(uint32_t)));
@@ -722,7 +723,7 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
       set_last_error("dsa_topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
       return DSA_ERR_HIP;
     }
-    attr = true;
+    if (slot >= 0) attr_by_dev[slot].store(true, std::memory_order_relaxed);
   }
   if (long_chunks)
     DSA_LAUNCH(topk_chunk_kernel<kLongPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
