@@ -102,6 +102,22 @@ def test_indexer_bf16_e4m3_within_bound(L):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("cid,B,Sq", [(2, 1024, 1), (3, 300, 4)])
+def test_indexer_max_batch_ragged_within_bound(cid, B, Sq):
+    """The largest batch one launch takes (1024 requests; 300 with four fp8 queries, which
+    fills Sq*H = 256): the per-request unit prefix spans every thread's requests, with
+    empty, one-token, tile-edge and page-edge requests among them."""
+    L = 700
+    wl = synth.make_workload(synth.spec(cid).scaled(B=B, L=L), with_kv=False)
+    lens = np.random.default_rng(B).integers(0, L + 1, B).astype(np.int32)
+    lens[:9] = [0, 1, 31, 32, 33, 64, 65, L, Sq]
+    lens = np.maximum(lens, Sq - 1)                  # the oracle's visibility: seq_len >= Sq - 1
+    wl.seq_lens = lens
+    dw = DevWorkload(wl, with_kv=False)
+    check_scores(wl, dw.scores())
+    assert int(dw.err) == 0
+
+
 def test_indexer_e4m3_queries_mtp_within_bound():
     wl = synth.make_workload(synth.spec(3).scaled(B=2, L=1500), with_kv=False)
     wl.seq_lens = np.array([1500, 1031], dtype=np.int32)
@@ -261,7 +277,8 @@ def test_topk_batched_mtp_rows():
 
 # ------------------------------------------------------------------ sparse MLA
 @pytest.mark.parametrize("H,k,L", [(128, 2048, 3000), (16, 256, 4096), (64, 300, 700), (128, 100, 100),
-                                   (32, 512, 2000), (48, 300, 1000)])
+                                   (32, 512, 2000), (48, 300, 1000),
+                                   (16, 65536, 70000)])          # the largest selection one call takes
 def test_mla_against_oracle(H, k, L):
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=L, mla_heads=H, topk=k))
     rng = np.random.default_rng(H + k)
