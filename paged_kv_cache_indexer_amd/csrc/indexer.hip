@@ -517,7 +517,7 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
   }
   RowStore ks = RowStore::from(*keys);
   if (q_dtype == DSA_F32 && k_dtype == DSA_F32) {
-    DSA_CHECK_SUPPORTED(Sq * H * D <= kF32MaxQ && Sq * H <= 256 && D % 4 == 0,
+    DSA_CHECK_SUPPORTED((int64_t)Sq * H * D <= kF32MaxQ && (int64_t)Sq * H <= 256 && D % 4 == 0,
                         "dsa_indexer_scores: fp32 path needs Sq*H*D <= 4096, Sq*H <= 256, D %% 4 == 0");
     DSA_CHECK_ARG(keys->row_bytes == D * 4, "dsa_indexer_scores: row_bytes != D*4");
     DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
@@ -529,7 +529,7 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
   }
   DSA_CHECK_SUPPORTED((k_dtype == DSA_E4M3 || k_dtype == DSA_MXFP4) && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
                       "dsa_indexer_scores: supported dtypes are (f32,f32) and q bf16/e4m3 with k e4m3/mxfp4");
-  DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && Sq * H <= 256 && B <= kMaxB,
+  DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && (int64_t)Sq * H <= 256 && B <= kMaxB,
                       "dsa_indexer_scores: MFMA path needs D == 128, H %% 32 == 0, Sq*H <= 256, B <= 1024");
   const bool fp4 = k_dtype == DSA_MXFP4;
   if (fp4) {

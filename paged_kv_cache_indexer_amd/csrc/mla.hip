@@ -556,8 +556,17 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   DSA_CHECK_ARG(scale > 0.0f && scale < INFINITY, "dsa_sparse_mla_decode: scale must be positive and finite");
   DSA_CHECK_SUPPORTED(H % 16 == 0 && k <= 65536, "dsa_sparse_mla_decode: needs H %% 16 == 0 and k <= 65536");
   if (rows->page_table) DSA_CHECK_ARG(rows->page_size > 0, "dsa_sparse_mla_decode: bad page_size");
+  DSA_CHECK_SUPPORTED((int64_t)B * Sq * ((H + 15) / 16) <= (1 << 24),
+                      "dsa_sparse_mla_decode: more than 2^24 (query row, 16-head group) pairs");
   int splits, per;
   mla_split_plan(B, Sq, H, k, splits, per);
+  {
+    // the launch's work-items (blocks x threads) must fit the 32-bit grid size
+    const int nw_ = mla_waves(H);
+    const int64_t blocks = (int64_t)splits * B * Sq * ((H + 16 * nw_ - 1) / (16 * nw_));
+    DSA_CHECK_SUPPORTED(blocks * 128 * nw_ < ((int64_t)1 << 32),
+                        "dsa_sparse_mla_decode: %lld work-groups exceed one launch", (long long)blocks);
+  }
   const size_t need = dsa_sparse_mla_workspace_size(B, Sq, H, k);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) {
     set_last_error("dsa_sparse_mla_decode: workspace %zu < %zu bytes", ws_bytes, need);

@@ -321,7 +321,7 @@ extern "C" dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int3
   if (B == 0) return DSA_OK;
   DSA_CHECK_ARG(topk && pool_ids && id_to_slot && ptr && is_hit && slot && miss_pos && miss_slot && miss_count,
                 "dsa_plan: null pointer");
-  DSA_CHECK_SUPPORTED(Sq * k <= kPlanMaxE && n_sets <= kPlanMaxSets && ways <= 64 &&
+  DSA_CHECK_SUPPORTED((int64_t)Sq * k <= kPlanMaxE && n_sets <= kPlanMaxSets && ways <= 64 &&
                           (int64_t)n_sets * ways <= (1 << 24),
                       "dsa_plan: needs Sq*k <= 8192, n_sets <= 4096, ways <= 64");
   static std::atomic<bool> attr_by_dev[kMaxDevices];

@@ -86,3 +86,23 @@ def test_invalid_arguments_rejected_without_device():
                                 None, None, None) == _lib.DSA_ERR_UNSUPPORTED
     # empty batches are valid no-ops
     assert L.dsa_topk(None, 1, None, 0, 1, 8, None, None, 0, None) == _lib.DSA_OK
+
+
+def test_size_products_checked_in_64_bits():
+    """Sizes whose products overflow 32 bits are rejected, not wrapped into small values."""
+    L = _lib.load()
+    p = ctypes.c_void_p(16)
+    rows = _lib.dsa_rows_t()
+    rows.base, rows.row_bytes, rows.num_rows = 16, 1152, 64
+    # 2^20 x 64 query rows x 8 head groups of 16: past the 2^24 pairs one launch covers
+    assert L.dsa_sparse_mla_decode(p, p, ctypes.byref(rows), 1 << 20, 64, 128, 2048, ctypes.c_float(0.1), p,
+                                   _lib.DSA_BF16, p, None, 0, None, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert b"pairs" in L.dsa_last_error()
+    keys = _lib.dsa_rows_t()
+    keys.base, keys.row_bytes, keys.num_rows = 16, 128, 64
+    # Sq * H = 2^32 wraps to 0 in 32 bits
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(keys), _lib.DSA_E4M3, p, p, 1, 1 << 26, 64, 128,
+                                64, p, None, None, None) == _lib.DSA_ERR_UNSUPPORTED
+    # Sq * k = 2^32 wraps to 0 in 32 bits
+    assert L.dsa_plan(p, 1, 1 << 29, 8, p, p, p, 4, 2, 10, p, p, p, p, p, 1, None,
+                      None) == _lib.DSA_ERR_UNSUPPORTED
