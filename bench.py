@@ -192,7 +192,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is described in DESIGN.md and not built", file=sys.stderr)
+              "sharding of this path is not built", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, dtype or alignment              */
-  DSA_ERR_UNSUPPORTED = -2,  /* valid request outside what this build implements        */
+  DSA_ERR_UNSUPPORTED = -2,  /* valid request outside what this library implements      */
   DSA_ERR_HIP = -3,          /* a HIP launch/runtime call failed; see dsa_last_error()   */
   DSA_ERR_WORKSPACE = -4     /* workspace pointer NULL or smaller than *_workspace_size  */
 } dsa_status_t;
