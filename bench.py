@@ -96,6 +96,64 @@ def cpu_baseline(wl, budget_s=15.0, max_workers=16):
                             "sample": f"{done} of {wl.B} requests in {dt:.1f} s, scaled to the full batch"}}
 
 
+def measure_peaks(torch):
+    """What the running device reaches, beside the published peaks: non-temporal streaming
+    read and copy over buffers far larger than the 256 MB last-level cache, and
+    dependency-free MFMA loops (bf16 32x32x16, fp8 e4m3 32x32x64) on two waves per SIMD.
+    Each figure is the best of five launches timed with HIP events."""
+    import ctypes
+    from paged_kv_cache_indexer_amd import peaks
+    from tests.dsa_dev import HipMark
+    L = peaks.load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best(launch, reps=5):
+        launch()
+        t = []
+        for _ in range(reps):
+            m0, m1 = HipMark(), HipMark()
+            m0.record(stream)
+            launch()
+            m1.record(stream)
+            torch.cuda.synchronize()
+            t.append(m0.elapsed_ms(m1) * 1e-3)
+        return min(t)
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: HIP error {rc}")
+
+    out = {}
+    n16 = (2 << 30) // 16
+    buf = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
+    blocks = cus * 8
+    xo = torch.empty(blocks * 4, dtype=torch.int32, device="cuda")
+    t = best(lambda: ok(L.dsa_peak_stream_read(buf.data_ptr(), n16, blocks, xo.data_ptr(), sp), "stream read"))
+    out["hbm_read_GBps"] = n16 * 16 / t / 1e9
+    del buf
+    n16c = (1 << 30) // 16
+    src = torch.empty(n16c * 16, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = best(lambda: ok(L.dsa_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16c, blocks, sp), "stream copy"))
+    out["hbm_copy_GBps"] = 2 * n16c * 16 / t / 1e9          # bytes read + bytes written
+    del src, dst
+    mblocks, iters = cus * 2, 2048
+    res = torch.empty(mblocks * 4 * 2, dtype=torch.float32, device="cuda")
+    for name, fp8, K in (("bf16_mfma_TFLOPs", 0, 16), ("fp8_mfma_TFLOPs", 1, 64)):
+        t = best(lambda: ok(L.dsa_peak_mfma(fp8, iters, mblocks, res.data_ptr(), sp), "mfma loop"))
+        r = res.cpu()
+        if not (r == float(K * iters)).all():
+            raise RuntimeError(f"{name}: MFMA loop gave {r.min().item()}..{r.max().item()}, expected {K * iters}")
+        out[name] = mblocks * 4 * iters * 8 * 2 * 32 * 32 * K / t / 1e12
+    torch.cuda.synchronize()
+    out["probe"] = ("streaming read of 2 GiB and copy of 1 GiB (16-byte non-temporal accesses, "
+                    f"{blocks} work-groups); MFMA loops with 8 independent 32x32 accumulators per wave, "
+                    f"{mblocks} work-groups of 4 waves; best of 5 launches")
+    return out
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.json")
 # entry point -> (kernel name prefixes in rocprofv3 output, sources the kernels are built from)
 ENTRY_KERNELS = {
@@ -169,6 +227,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak probes (streaming read / copy, MFMA loops)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -269,6 +329,7 @@ def main():
         torch.cuda.synchronize()
         per[n] = m0.elapsed_ms(m1) * 1e-3 / args.steps             # seconds per launch
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
+    meas = None if args.no_peaks else measure_peaks(torch)
 
     fp8_q = wl.idx_q_dtype == "e4m3"                 # the indexer then runs on the fp8 MFMA
     work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys, Sq=Sq,
@@ -319,6 +380,8 @@ def main():
                    "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},
         "roofline": roofline,
         "step_roofline": {"t_star_us": t_star * 1e6, "measured_us": ms * 1e3, "frac": t_star * 1e6 / (ms * 1e3)},
+        "measured_peaks": (None if meas is None else
+                           {**meas, "dominant_kernel_frac_of_read_peak": by / per[dom] / 1e9 / meas["hbm_read_GBps"]}),
         "kernels": kernels,
         "cpu_baseline": cpu,
     }

@@ -106,3 +106,12 @@ def test_size_products_checked_in_64_bits():
     # Sq * k = 2^32 wraps to 0 in 32 bits
     assert L.dsa_plan(p, 1, 1 << 29, 8, p, p, p, 4, 2, 10, p, p, p, p, p, 1, None,
                       None) == _lib.DSA_ERR_UNSUPPORTED
+
+
+def test_peak_probe_library_exports():
+    from paged_kv_cache_indexer_amd import peaks
+    out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True, text=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert {"dsa_peak_stream_read", "dsa_peak_stream_copy", "dsa_peak_mfma"} <= names
+    L = peaks.load()
+    assert L.dsa_peak_mfma(0, 0, 1, None, None) != 0         # rejected before any launch
