@@ -329,7 +329,13 @@ def main():
         torch.cuda.synchronize()
         per[n] = m0.elapsed_ms(m1) * 1e-3 / args.steps             # seconds per launch
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
-    meas = None if args.no_peaks else measure_peaks(torch)
+    meas, meas_err = None, None
+    if not args.no_peaks:
+        try:                                   # auxiliary: a missing probe library costs only this field
+            meas = measure_peaks(torch)
+        except (OSError, RuntimeError) as e:
+            meas_err = str(e)
+            print(f"bench.py: peak probes skipped ({e})", file=sys.stderr)
 
     fp8_q = wl.idx_q_dtype == "e4m3"                 # the indexer then runs on the fp8 MFMA
     work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys, Sq=Sq,
@@ -380,7 +386,7 @@ def main():
                    "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},
         "roofline": roofline,
         "step_roofline": {"t_star_us": t_star * 1e6, "measured_us": ms * 1e3, "frac": t_star * 1e6 / (ms * 1e3)},
-        "measured_peaks": (None if meas is None else
+        "measured_peaks": (({"error": meas_err} if meas_err else None) if meas is None else
                            {**meas, "dominant_kernel_frac_of_read_peak": by / per[dom] / 1e9 / meas["hbm_read_GBps"]}),
         "kernels": kernels,
         "cpu_baseline": cpu,
