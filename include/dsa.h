@@ -123,11 +123,14 @@ const char* dsa_last_error(void);
  *            sync with the load stream before it launches; [HCCP] §1.3 ordering).
  *
  * Supported: (q F32, k F32): any H*D <= 4096; q BF16 or E4M3 with k E4M3 or MXFP4:
- * D = 128, H a multiple of 32, Sq*H <= 256.  Page size (paged keys) a multiple of 32.
+ * D = 128, H a multiple of 32, Sq*H <= 256, B <= 1024, B * ceil(score_stride / 32) < 2^31.
+ * Page size (paged keys) a multiple of 32.
  * MXFP4 block-scale codes: 0x00..0xFE with E4M3 queries (the scaled MFMA applies them);
  * 0x00..0xFE with BF16 queries as long as every scaled key element is a finite bf16
  * (|element| * 2^(c-127) < 2^128).  Code 0xFF (NaN) gives an unspecified score.
  * Out-of-range page ids: the affected tokens score -inf, and each adds one to err_count.
+ * A seq_lens[b] above score_stride is clamped to score_stride (nothing is written past a
+ * score row); on the BF16 / E4M3 path each such request also adds one to err_count.
  */
 dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
                                 const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,

@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(256) indexer_f32_kernel(
   for (int i = threadIdx.x; i < Sq * H; i += blockDim.x) ws[i] = w[(int64_t)b * Sq * H + i];
   __syncthreads();
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= L) return;
+  if (s >= L || s >= score_stride) return;        // a length past the row is clamped to it
   const int64_t r = keys.row(b, s);
   float* out = scores + (int64_t)b * Sq * score_stride + s;
   if (r < 0) {
@@ -109,16 +109,35 @@ constexpr int kPrefixPerThread = (kMaxB + 255) / 256;
 constexpr int kSlots = 2;
 constexpr int kMaxUnit = (64 / kSlots) * kSlots;   // tiles per unit: at most one per lane
 
-// unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; returns ut
-__device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int max_unit, int* unit_off,
-                              int* wsum) {
+// tiles per unit for `total` tiles over `wave_slots` waves: one round, whole passes over the
+// register slots, at most one tile per lane
+__device__ __forceinline__ int unit_tiles(int total, int wave_slots, int max_unit) {
+  int ut = (total + wave_slots - 1) / wave_slots;
+  ut = ((ut + kSlots - 1) / kSlots) * kSlots;
+  if (ut < kSlots) ut = kSlots;
+  if (ut > max_unit) ut = max_unit;
+  return ut;
+}
+
+// unit_off[b] = first unit of request b (units of ut tiles), unit_off[B] = total; len_sh[b] =
+// request b's length clamped to [0, stride] (a longer one is counted once, by work-group 0);
+// returns ut
+__device__ int indexer_units(const int32_t* seq_lens, int B, int64_t stride, int wave_slots, int max_unit,
+                              int* unit_off, int* len_sh, int* wsum, int32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tiles[kPrefixPerThread];
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < kPrefixPerThread; ++i) {
     const int b = tid * kPrefixPerThread + i;
-    tiles[i] = (b < B) ? (seq_lens[b] + kTile - 1) / kTile : 0;
+    int len = (b < B) ? seq_lens[b] : 0;
+    if (len > stride) {
+      if (blockIdx.x == 0) count_error(err);
+      len = (int)stride;
+    }
+    len = max(len, 0);
+    if (b < B) len_sh[b] = len;
+    tiles[i] = (len + kTile - 1) / kTile;
     mine += tiles[i];
   }
   auto block_scan = [&](int v, int& total) {     // exclusive scan over the 256 threads
@@ -143,10 +162,7 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int wave_slots, int
   };
   int total_tiles = 0;
   block_scan(mine, total_tiles);
-  int ut = (total_tiles + wave_slots - 1) / wave_slots;
-  ut = ((ut + kSlots - 1) / kSlots) * kSlots;     // whole passes over the register slots
-  if (ut < kSlots) ut = kSlots;
-  if (ut > max_unit) ut = max_unit;               // tile rows one per lane; scores fit the LDS buffer
+  const int ut = unit_tiles(total_tiles, wave_slots, max_unit);
   int units[kPrefixPerThread];
   int my_units = 0;
 #pragma unroll
@@ -200,6 +216,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   constexpr int kLoads = kRowBytes * kTile / 1024; // 16-byte loads per lane per tile
   constexpr int kHalf = kRowBytes / 2;             // key bytes per lane group after the re-layout
   __shared__ int unit_off[kMaxB + 1];              // prefix of units per request
+  __shared__ int len_sh[kMaxB];                    // request lengths, clamped to the score row
   __shared__ __attribute__((aligned(16))) float wsm[4][MT_W * 32];   // per-wave head weights
   constexpr int kStageStride = kRowBytes + 16;                        // key rows, padded
   __shared__ __attribute__((aligned(16))) char kstage[4][kTile * kStageStride];
@@ -222,8 +239,8 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   const int tpp_shift = (tpp > 0 && (tpp & (tpp - 1)) == 0) ? __builtin_ctz(tpp) : -1;
 
   __shared__ int scan_wsum[4];
-  const int ut = __builtin_amdgcn_readfirstlane(
-      indexer_units(a.seq_lens, a.B, gridDim.x * WPU, kMaxUnit, unit_off, scan_wsum));
+  const int ut = __builtin_amdgcn_readfirstlane(indexer_units(a.seq_lens, a.B, a.score_stride, gridDim.x * WPU,
+                                                              kMaxUnit, unit_off, len_sh, scan_wsum, a.err));
   const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
   const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
@@ -246,7 +263,7 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
       }
       b = __builtin_amdgcn_readfirstlane(lo);
     }
-    const int L = scalar_load(a.seq_lens + b);
+    const int L = __builtin_amdgcn_readfirstlane(len_sh[b]);
     const int n_tiles_b = (L + kTile - 1) / kTile;
     const int t_begin = (u - __builtin_amdgcn_readfirstlane(unit_off[b])) * ut;
     const int t_end = min(t_begin + ut, n_tiles_b);
@@ -540,6 +557,8 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
     DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
   }
   if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "dsa_indexer_scores: page_size %% 32 != 0");
+  DSA_CHECK_SUPPORTED((int64_t)B * ((score_stride + kTile - 1) / kTile) < ((int64_t)1 << 31),
+                      "dsa_indexer_scores: B * ceil(score_stride / 32) must be below 2^31");
   MfmaArgs a{q, w, ks, k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count};
   const int HMT = H / 32;
   const bool f8 = q_dtype == DSA_E4M3;

@@ -118,6 +118,24 @@ def test_indexer_max_batch_ragged_within_bound(cid, B, Sq):
     assert int(dw.err) == 0
 
 
+def test_indexer_length_past_the_score_row_is_clamped():
+    """seq_lens[0] = 900 over a 700-wide score row: request 0 scores as a 700-token request,
+    counts one error, and nothing is written past the rows (a sentinel row follows them)."""
+    wl = synth.make_workload(synth.spec(2).scaled(B=3, L=900), with_kv=False)
+    wl.seq_lens = np.array([900, 700, 300], dtype=np.int32)
+    dw = DevWorkload(wl, with_kv=False)
+    stride = 700
+    buf = torch.full((wl.B * wl.Sq + 1, stride), 123.0, dtype=torch.float32, device=DEV)
+    sc = buf[:wl.B * wl.Sq].view(wl.B, wl.Sq, stride)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, dw.k_scale, dw.seq_lens, sc, k_dtype=dw.k_dtype, err=err,
+                           q_dtype=dw.q_dtype)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert (buf[-1] == 123.0).all()
+    check_scores(dataclasses.replace(wl, seq_lens=np.array([700, 700, 300], dtype=np.int32)), sc)
+
+
 def test_indexer_e4m3_queries_mtp_within_bound():
     wl = synth.make_workload(synth.spec(3).scaled(B=2, L=1500), with_kv=False)
     wl.seq_lens = np.array([1500, 1031], dtype=np.int32)
