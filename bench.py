@@ -40,7 +40,7 @@ def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2)
     idx_bytes = (B * L * KEY_BYTES[keys](D)  # keys and their scales, read once for all Sq queries
                  + Q * H_idx * D * q_bytes  # queries
                  + Q * H_idx * 4      # head weights
-                 + B * (L // ps) * 4  # page table
+                 + B * -(-L // ps) * 4  # page table (a partial last page counts)
                  + Q * L * 4)         # scores out
     idx_flops = 2 * Q * H_idx * D * L
     topk_bytes = Q * L * 4 + Q * k * 4
