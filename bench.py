@@ -103,7 +103,7 @@ def measure_peaks(torch):
     Each figure is the best of five launches timed with HIP events."""
     import ctypes
     from paged_kv_cache_indexer_amd import peaks
-    from tests.dsa_dev import HipMark
+    from paged_kv_cache_indexer_amd.pipeline import HipMark
     L = peaks.load()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
@@ -257,7 +257,8 @@ def main():
 
     import torch
     import synth
-    from tests.dsa_dev import DevWorkload, DecodeStep, HipMark
+    from synth.device import DevWorkload
+    from paged_kv_cache_indexer_amd.pipeline import HipMark
 
     if args.entry == "kv_write":
         torch.cuda.set_device(0)
@@ -274,7 +275,7 @@ def main():
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
-    step = DecodeStep(dw, layers=args.layers)
+    step = dw.decode_step(args.layers)
     names = ["indexer", "topk", "mla"]
     stream = torch.cuda.Stream()            # non-default stream: the step is captured and replayed
 
@@ -400,7 +401,7 @@ def bench_kv_write(args):
     into an e4m3 and into an MXFP4 indexer cache."""
     import torch
     import paged_kv_cache_indexer_amd as dsa
-    from tests.dsa_dev import HipMark
+    from paged_kv_cache_indexer_amd.pipeline import HipMark
     res = []
     for (B, Sq), cache in ((b_sq, c) for c in ("e4m3", "mxfp4") for b_sq in ((32, 1), (8, 4))):
         ps, L, D = 64, 65536, 128
@@ -450,7 +451,7 @@ def bench_pool_group(args):
     import synth
     from synth import gen as sgen
     import paged_kv_cache_indexer_amd as dsa
-    from tests.dsa_dev import HipMark, PoolGroupStep, host_device_ptr
+    from paged_kv_cache_indexer_amd.pipeline import HipMark, PoolGroupStep, host_device_ptr
     cfg = synth.spec(4)
     traj = sgen.topk_trajectory(cfg)
     hosts = []
@@ -473,8 +474,7 @@ def bench_pool_group(args):
                 e0.record(stream)
                 for s in range(cfg.steps):
                     pg.run(stream, tks[s], q)
-                if aux:
-                    stream.wait_event(pg.plan_free[(pg.step_no - 1) % 2])
+                pg.drain(stream)
                 e1.record(stream)
                 torch.cuda.synchronize()
                 ms = e0.elapsed_ms(e1) / cfg.steps
@@ -486,7 +486,7 @@ def bench_pool_group(args):
                         "ms_per_step": best, "ms_per_layer": best / cfg.layers, "last_step_hit_rate": hit})
     # MTP draft steps over a frozen selection (next_n = 4 attention passes per verify step):
     # serve once and reuse the selection buffer, or serve again before every draft step
-    from tests.dsa_dev import MtpDraftSteps
+    from paged_kv_cache_indexer_amd.pipeline import MtpDraftSteps
     next_n = 4
     qd = [q for _ in range(next_n)]
     mtp = []

@@ -12,6 +12,7 @@
  *   dsa_plan               shared-group pool plan, set-associative FIFO            [GLM52] §3, §4.2-4.3, §5
  *   dsa_gather_kv          per-layer serve (pool / paged / host rows) and install  [GLM52] §4.4, §5
  *   dsa_sparse_mla_decode  MLA latent attention over the selected rows only        [TSA] "MLA", [GLM52] §2.1
+ *   dsa_merge_partials     LSE merge of per-rank (or per-split) partial attention  [TSA] "MLA", [HCCP] §1.1
  *   dsa_page_translate     page-sharded ownership closed form                      [HCCP] §1.1
  *   dsa_kv_write           new tokens' latent rows and e4m3 or MXFP4 indexer keys into the
  *                          paged caches (fused quantise + scatter)                 [TSA] "KV host tiering"
@@ -122,9 +123,12 @@ const char* dsa_last_error(void);
  *            read keys that are not yet resident ([GLM5R] "BugFix#2": the indexer must
  *            sync with the load stream before it launches; [HCCP] §1.3 ordering).
  *
- * Supported: (q F32, k F32): any H*D <= 4096; q BF16 or E4M3 with k E4M3 or MXFP4:
- * D = 128, H a multiple of 32, Sq*H <= 256, B <= 1024, B * ceil(score_stride / 32) < 2^31.
- * Page size (paged keys) a multiple of 32.
+ * Supported: (q F32, k F32): any H*D <= 4096, Sq*H <= 256, B <= 65535; q BF16 or E4M3 with
+ * k E4M3 or MXFP4: D = 128, (H / 32, Sq) in {(1,1), (1,2), (1,4), (1,8), (2,1), (2,2), (2,4),
+ * (4,1), (4,2)}, B <= 1024, B * ceil(score_stride / 32) < 2^31, keys->num_rows >= 32 (the
+ * scan reads whole 32-token tiles); paged keys: page size a multiple of 32; dense keys:
+ * num_rows and req_stride multiples of 32.  Outside these the call returns
+ * DSA_ERR_UNSUPPORTED before anything is enqueued (the wait on `ready` included).
  * MXFP4 block-scale codes: 0x00..0xFE with E4M3 queries (the scaled MFMA applies them);
  * 0x00..0xFE with BF16 queries as long as every scaled key element is a finite bf16
  * (|element| * 2^(c-127) < 2^128).  Code 0xFF (NaN) gives an unspecified score.
@@ -209,10 +213,15 @@ dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int32_t* pool_i
  *     reader of the overwritten pool rows ([GLM52] §4.4: backfill is off the critical
  *     path, on an auxiliary stream).
  *
- *   src    row store of the full cache for this layer (paged device cache, dense device
- *          rows, or mapped pinned host rows); row_bytes must equal `row_bytes`
- *   pool   [B, pool_rows, row_bytes] bytes (NULL allowed when is_hit is NULL in SERVE)
- *   sel    [B, Sq, k, row_bytes] bytes
+ *   src      row store of the full cache for this layer (paged device cache, dense device
+ *            rows, or mapped pinned host rows); row_bytes must equal `row_bytes`
+ *   pool     [B, pool_rows, row_bytes] bytes (NULL allowed when is_hit is NULL in SERVE)
+ *   sel      [B, Sq, k, row_bytes] bytes
+ *   sel_idx  SERVE only, optional (NULL = not written): [B, Sq, k] int32, t * k + j where
+ *            entry (b,t,j) received a row and -1 where it got the zero row (padding or an
+ *            invalid entry).  Passed as `idx` to dsa_sparse_mla_decode together with a dense
+ *            row store over `sel` (req_stride = Sq * k), attention then skips the padded
+ *            entries instead of weighting their zero rows.  4-byte aligned.
  * Supported: row_bytes a multiple of 16, <= 4096.  Invalid slots / positions: zero row
  * (SERVE) or skipped (INSTALL), counted in err_count.
  */
@@ -220,8 +229,8 @@ dsa_status_t dsa_plan(const int32_t* topk, int B, int Sq, int k, int32_t* pool_i
 #define DSA_GATHER_INSTALL 1
 dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int32_t* slot, int B,
                            int Sq, int k, const dsa_rows_t* src, void* pool, int64_t pool_rows,
-                           int32_t row_bytes, void* sel, int mode, int32_t* err_count,
-                           hipStream_t stream);
+                           int32_t row_bytes, void* sel, int32_t* sel_idx, int mode,
+                           int32_t* err_count, hipStream_t stream);
 
 /*
  * dsa_sparse_mla_decode — MLA latent attention over the selected rows only.  One
@@ -252,6 +261,27 @@ dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_
                                    int B, int Sq, int H, int k, float scale, void* o,
                                    dsa_dtype_t o_dtype, float* lse, void* ws, size_t ws_bytes,
                                    int32_t* err_count, hipStream_t stream);
+
+/*
+ * dsa_merge_partials — combine R partial attention results, each over its own disjoint set
+ * of rows, into the result over the union of the rows ([TSA] "MLA": split-KV partials merged
+ * by LSE rescaling; [HCCP] §1.1: under page-sharded KV each rank attends over the pages it
+ * owns, so the ranks' partials are merged this way).  For every output row n:
+ *     lse[n] = ln sum_r exp(lse_r[n])
+ *     o[n,:] = sum_r exp(lse_r[n] - lse[n]) * o_r[n,:]
+ * A part with lse_r = -inf (no rows) contributes nothing; if every part is empty the result is
+ * o = 0, lse = -inf.
+ *
+ *   o_parts    [R, N, V] part_dtype (F32 or BF16), 16-byte aligned: rank r's normalised o
+ *              (e.g. [R, B, Sq, H, 512] from dsa_sparse_mla_decode with o_dtype F32)
+ *   lse_parts  [R, N] float32
+ *   o          [N, V] o_dtype (F32 or BF16, round to nearest even), 16-byte aligned
+ *   lse        [N] float32
+ * Supported: V a multiple of 8, ceil(N / 4) < 2^31.
+ */
+dsa_status_t dsa_merge_partials(const void* o_parts, dsa_dtype_t part_dtype, const float* lse_parts, int R,
+                                int64_t N, int V, void* o, dsa_dtype_t o_dtype, float* lse,
+                                hipStream_t stream);
 
 /*
  * dsa_page_translate — owner rank and owner-local row of logical cache slots under

@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED
 
 EXPORTED = ["dsa_version", "dsa_last_error", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
             "dsa_plan", "dsa_gather_kv", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_page_translate", "dsa_kv_write"]
+            "dsa_merge_partials", "dsa_page_translate", "dsa_kv_write"]
 
 
 class dsa_rows_t(ctypes.Structure):
@@ -54,11 +54,13 @@ def load() -> ctypes.CDLL:
         "dsa_plan": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp]),
         "dsa_gather_kv": (ctypes.c_int, [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, prow, vp, i64,
-                                         i32, vp, ctypes.c_int, vp, vp]),
+                                         i32, vp, vp, ctypes.c_int, vp, vp]),
         "dsa_sparse_mla_workspace_size": (sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "dsa_sparse_mla_decode": (ctypes.c_int, [vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, sz, vp,
                                                  vp]),
+        "dsa_merge_partials": (ctypes.c_int, [vp, ctypes.c_int, vp, ctypes.c_int, i64, ctypes.c_int, vp,
+                                              ctypes.c_int, vp, vp]),
         "dsa_page_translate": (ctypes.c_int, [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]),
         "dsa_kv_write": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, prow,
                                         prow, ctypes.c_int, vp, vp, vp]),

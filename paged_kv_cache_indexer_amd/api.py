@@ -114,12 +114,14 @@ def dsa_plan(topk: torch.Tensor, pool_ids: torch.Tensor, id_to_slot: torch.Tenso
 
 def dsa_gather_kv(topk: torch.Tensor, is_hit: Optional[torch.Tensor], slot: Optional[torch.Tensor],
                   src: Optional[Rows], pool: Optional[torch.Tensor], sel: torch.Tensor, mode: int = DSA_GATHER_SERVE,
-                  row_bytes: int = 1152, err: Optional[torch.Tensor] = None, stream=None):
+                  row_bytes: int = 1152, err: Optional[torch.Tensor] = None, stream=None,
+                  sel_idx: Optional[torch.Tensor] = None):
+    """sel_idx (SERVE, optional): [B, Sq, k] int32 out, t*k + j where a row was served, else -1."""
     B, Sq, k = topk.shape
     pool_rows = 0 if pool is None else (pool.numel() * pool.element_size()) // (B * row_bytes)
     _check(_lib.load().dsa_gather_kv(_ptr(topk), _ptr(is_hit), _ptr(slot), B, Sq, k,
                                      src.ref() if src is not None else None, _ptr(pool), pool_rows, row_bytes,
-                                     _ptr(sel), mode, _ptr(err), _stream(stream)), "dsa_gather_kv")
+                                     _ptr(sel), _ptr(sel_idx), mode, _ptr(err), _stream(stream)), "dsa_gather_kv")
 
 
 def dsa_sparse_mla_workspace_size(B: int, Sq: int, H: int, k: int) -> int:
@@ -135,6 +137,18 @@ def dsa_sparse_mla_decode(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale:
     _check(_lib.load().dsa_sparse_mla_decode(_ptr(q), _ptr(idx), rows.ref(), B, Sq, H, k, float(scale), _ptr(o),
                                              _dtype_code(o), _ptr(lse), _ptr(ws), ws_bytes, _ptr(err),
                                              _stream(stream)), "dsa_sparse_mla_decode")
+
+
+def dsa_merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                       stream=None):
+    """o_parts [R, ..., V] (float32 or bf16), lse_parts [R, ...] float32 -> o [..., V], lse [...]:
+    the LSE merge of R partial attention results over disjoint row sets."""
+    R, V = o_parts.shape[0], o_parts.shape[-1]
+    N = lse_parts[0].numel()
+    if o_parts.numel() != R * N * V or o.numel() != N * V or lse.numel() != N:
+        raise ValueError("dsa_merge_partials: shapes disagree")
+    _check(_lib.load().dsa_merge_partials(_ptr(o_parts), _dtype_code(o_parts), _ptr(lse_parts), R, N, V, _ptr(o),
+                                          _dtype_code(o), _ptr(lse), _stream(stream)), "dsa_merge_partials")
 
 
 def dsa_page_translate(x: torch.Tensor, page_size: int, n_ranks: int, rank: torch.Tensor, local_row: torch.Tensor,

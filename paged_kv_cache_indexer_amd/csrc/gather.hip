@@ -21,6 +21,7 @@ struct GatherArgs {
   int64_t pool_rows;
   int row_bytes;
   char* sel;                // [B, Sq, k, row_bytes]
+  int32_t* sel_idx;         // [B, Sq, k] or null (SERVE: t * k + j where a row was served, else -1)
   int32_t* err;
 };
 
@@ -36,6 +37,7 @@ __global__ void __launch_bounds__(256) serve_kernel(GatherArgs a, int64_t n_entr
     const int b = (int)(e / E);
     const int32_t p = a.topk[e];
     u32x4 v = {0, 0, 0, 0};
+    bool served = false;
     if (p >= 0) {
       const char* rowp = nullptr;
       if (a.is_hit && a.is_hit[e]) {
@@ -50,8 +52,10 @@ __global__ void __launch_bounds__(256) serve_kernel(GatherArgs a, int64_t n_entr
       } else if (c == 0) {
         count_error(a.err);
       }
+      served = rowp != nullptr;
     }
     *(reinterpret_cast<u32x4*>(a.sel + e * a.row_bytes) + c) = v;
+    if (a.sel_idx && c == 0) a.sel_idx[e] = served ? (int32_t)(e - (int64_t)b * E) : -1;
   }
 }
 
@@ -97,13 +101,15 @@ __global__ void __launch_bounds__(256) install_kernel(GatherArgs a, int64_t n_en
 
 extern "C" dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int32_t* slot, int B, int Sq,
                                       int k, const dsa_rows_t* src, void* pool, int64_t pool_rows, int32_t row_bytes,
-                                      void* sel, int mode, int32_t* err_count, hipStream_t stream) {
+                                      void* sel, int32_t* sel_idx, int mode, int32_t* err_count,
+                                      hipStream_t stream) {
   using namespace dsa;
   DSA_CHECK_ARG(B >= 0 && Sq >= 1 && k >= 1, "dsa_gather_kv: bad sizes");
   if (B == 0) return DSA_OK;
   DSA_CHECK_ARG(row_bytes > 0 && row_bytes % 16 == 0 && row_bytes <= 4096, "dsa_gather_kv: bad row_bytes");
   DSA_CHECK_ARG(topk && sel, "dsa_gather_kv: null pointer");
   DSA_CHECK_ARG(((uintptr_t)sel & 15) == 0, "dsa_gather_kv: sel not 16-byte aligned");
+  DSA_CHECK_ARG(((uintptr_t)sel_idx & 3) == 0, "dsa_gather_kv: sel_idx not 4-byte aligned");
   DSA_CHECK_ARG(mode == DSA_GATHER_SERVE || mode == DSA_GATHER_INSTALL, "dsa_gather_kv: bad mode");
   if (is_hit || mode == DSA_GATHER_INSTALL) {
     DSA_CHECK_ARG(is_hit && slot && pool && pool_rows > 0, "dsa_gather_kv: pool mode needs is_hit, slot, pool");
@@ -119,6 +125,7 @@ extern "C" dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit
   a.pool_rows = pool_rows;
   a.row_bytes = row_bytes;
   a.sel = static_cast<char*>(sel);
+  a.sel_idx = mode == DSA_GATHER_SERVE ? sel_idx : nullptr;
   a.err = err_count;
   if (mode == DSA_GATHER_SERVE) {
     DSA_CHECK_ARG(src && src->base, "dsa_gather_kv: null src");

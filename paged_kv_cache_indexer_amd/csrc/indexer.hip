@@ -525,20 +525,26 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
   DSA_CHECK_ARG(keys->num_rows >= 1, "dsa_indexer_scores: num_rows < 1");
   DSA_CHECK_ARG(((uintptr_t)keys->base & 15) == 0, "dsa_indexer_scores: keys not 16-byte aligned");
   if (keys->page_table) DSA_CHECK_ARG(keys->page_size > 0 && keys->pt_stride >= 0, "dsa_indexer_scores: bad paging");
-  if (ready) {
+  // the stream joins the load stream only once every argument check has passed, so a
+  // rejected call enqueues nothing
+  auto join_ready = [&]() -> dsa_status_t {
+    if (!ready) return DSA_OK;
     hipError_t e = hipStreamWaitEvent(stream, ready, 0);
     if (e != hipSuccess) {
       set_last_error("dsa_indexer_scores: hipStreamWaitEvent: %s", hipGetErrorString(e));
       return DSA_ERR_HIP;
     }
-  }
+    return DSA_OK;
+  };
   RowStore ks = RowStore::from(*keys);
   if (q_dtype == DSA_F32 && k_dtype == DSA_F32) {
     DSA_CHECK_SUPPORTED((int64_t)Sq * H * D <= kF32MaxQ && (int64_t)Sq * H <= 256 && D % 4 == 0,
                         "dsa_indexer_scores: fp32 path needs Sq*H*D <= 4096, Sq*H <= 256, D %% 4 == 0");
     DSA_CHECK_ARG(keys->row_bytes == D * 4, "dsa_indexer_scores: row_bytes != D*4");
     DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
+    DSA_CHECK_SUPPORTED(B <= 65535, "dsa_indexer_scores: fp32 path takes at most 65535 requests (grid y)");
     const int64_t gx = (score_stride + 255) / 256;
+    if (dsa_status_t st = join_ready(); st != DSA_OK) return st;
     DSA_LAUNCH(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
                        static_cast<const float*>(q), w, ks, static_cast<const float*>(k_scale), seq_lens, Sq, H, D, score_stride, scores,
                        err_count);
@@ -557,11 +563,27 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
     DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
   }
   if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "dsa_indexer_scores: page_size %% 32 != 0");
+  // the MFMA path reads whole 32-token tiles (an unresolvable tile reads rows 0..31 as a
+  // stand-in), so the key rows hold at least one tile, and a dense tile never straddles the
+  // end of the rows or the boundary between two requests
+  DSA_CHECK_SUPPORTED(keys->num_rows >= kTile, "dsa_indexer_scores: MFMA path needs num_rows >= 32");
+  if (!keys->page_table)
+    DSA_CHECK_SUPPORTED(keys->num_rows % kTile == 0 && keys->req_stride % kTile == 0,
+                        "dsa_indexer_scores: dense keys on the MFMA path need num_rows and req_stride "
+                        "multiples of 32");
   DSA_CHECK_SUPPORTED((int64_t)B * ((score_stride + kTile - 1) / kTile) < ((int64_t)1 << 31),
                       "dsa_indexer_scores: B * ceil(score_stride / 32) must be below 2^31");
   MfmaArgs a{q, w, ks, k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count};
   const int HMT = H / 32;
   const bool f8 = q_dtype == DSA_E4M3;
+  {
+    // the (H / 32, Sq) combinations instantiated below
+    static const int kInst[][2] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
+    bool known = false;
+    for (const auto& c : kInst) known = known || (HMT == c[0] && Sq == c[1]);
+    DSA_CHECK_SUPPORTED(known, "dsa_indexer_scores: unsupported (Sq, H) combination for the MFMA path");
+  }
+  if (dsa_status_t st = join_ready(); st != DSA_OK) return st;
   // one wave covers up to 4 M tiles; queries beyond that go to a second wave on the same tile
 #define DSA_CASE(HM, NQ_, RG_)                                                                  \
   if (HMT == HM && Sq == NQ_ * RG_) {                                                            \

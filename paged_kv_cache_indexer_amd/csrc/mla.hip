@@ -437,8 +437,9 @@ __device__ __forceinline__ void merge_add(float w, const u32x4& v0, const u32x4&
 
 template <int SMAX, bool F32>
 __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) {
-  const int qr = blockIdx.y;
-  const int head = blockIdx.x * kMergeHeads + (threadIdx.x >> 6);
+  const int hblocks = (a.H + kMergeHeads - 1) / kMergeHeads;   // 1-D grid: query row x head block
+  const int qr = blockIdx.x / hblocks;
+  const int head = (blockIdx.x - qr * hblocks) * kMergeHeads + (threadIdx.x >> 6);
   if (head >= a.H) return;
   const int S = a.splits;
   const int d = (threadIdx.x & 63) * 8;
@@ -601,7 +602,7 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
     DSA_LAUNCH((mla_decode_kernel<1, 2>), grid, dim3(128), 0, stream, a);
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
   if (st != DSA_OK || splits == 1) return st;
-  const dim3 mgrid((H + kMergeHeads - 1) / kMergeHeads, QR);
+  const dim3 mgrid((unsigned)(((H + kMergeHeads - 1) / kMergeHeads) * QR));
   const dim3 mblock(64 * kMergeHeads);
   // (the unrolled fp32 variant needs four times the registers, so fp32 keeps the loop)
   if (a.o_f32)
@@ -611,4 +612,92 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   else
     DSA_LAUNCH((mla_merge_kernel<0, false>), mgrid, mblock, 0, stream, a);
   return launch_status("dsa_sparse_mla_decode(merge)");
+}
+
+namespace dsa {
+
+// Merge of R partial attention results over disjoint row sets (the ranks of a page-sharded
+// cache, TokenSpeed audit page "MLA": split-KV partials combined by LSE rescaling; HiCache
+// page §1.1: each rank holds and attends over its own pages only).  64 threads per output
+// row n, 8 values per thread per pass.  Parts are [R, N, V] (the layout an all-gather of the
+// ranks' outputs produces); PF32 / OF32: float32 parts / output, else bf16.
+template <bool PF32, bool OF32>
+__global__ void __launch_bounds__(256) rank_merge_kernel(const void* parts, const float* plse, int R, int64_t N,
+                                                          int V, void* o, float* lse) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
+  for (int r = 0; r < R; ++r) mx = fmaxf(mx, plse[(int64_t)r * N + n]);
+  float wsum = 0.0f;
+  if (mx > -INFINITY)
+    for (int r = 0; r < R; ++r) {
+      const float l = plse[(int64_t)r * N + n];
+      wsum += (l == -INFINITY) ? 0.0f : expf(l - mx);
+    }
+  const float inv = (mx > -INFINITY) ? 1.0f / wsum : 0.0f;
+  for (int d = lane * 8; d < V; d += 512) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (mx > -INFINITY)
+      for (int r = 0; r < R; ++r) {
+        const float l = plse[(int64_t)r * N + n];
+        if (l == -INFINITY) continue;
+        const float w = expf(l - mx) * inv;
+        const int64_t off = ((int64_t)r * N + n) * V + d;
+        if constexpr (PF32) {
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(parts) + off);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(parts) + off + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += w * v0[i];
+            acc[4 + i] += w * v1[i];
+          }
+        } else {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(parts) + off);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += w * __uint_as_float(v[i] << 16);
+            acc[2 * i + 1] += w * __uint_as_float(v[i] & 0xffff0000u);
+          }
+        }
+      }
+    const int64_t ob = n * V + d;
+    if constexpr (OF32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(o) + ob) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>(static_cast<float*>(o) + ob + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o) + ob) =
+          u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                pack_bf16x2(acc[6], acc[7])};
+    }
+  }
+  if (lane == 0) lse[n] = (mx > -INFINITY) ? mx + logf(wsum) : -INFINITY;
+}
+
+}  // namespace dsa
+
+extern "C" dsa_status_t dsa_merge_partials(const void* o_parts, dsa_dtype_t part_dtype, const float* lse_parts, int R,
+                                           int64_t N, int V, void* o, dsa_dtype_t o_dtype, float* lse,
+                                           hipStream_t stream) {
+  using namespace dsa;
+  DSA_CHECK_ARG(R >= 1 && N >= 0 && V >= 8 && V % 8 == 0, "dsa_merge_partials: bad sizes");
+  if (N == 0) return DSA_OK;
+  DSA_CHECK_ARG(o_parts && lse_parts && o && lse, "dsa_merge_partials: null pointer");
+  DSA_CHECK_ARG(((uintptr_t)o_parts & 15) == 0 && ((uintptr_t)o & 15) == 0,
+                "dsa_merge_partials: o_parts and o must be 16-byte aligned");
+  DSA_CHECK_ARG((part_dtype == DSA_F32 || part_dtype == DSA_BF16) && (o_dtype == DSA_F32 || o_dtype == DSA_BF16),
+                "dsa_merge_partials: dtypes must be F32 or BF16");
+  DSA_CHECK_SUPPORTED((N + 3) / 4 < ((int64_t)1 << 31) && (int64_t)R * N < ((int64_t)1 << 40),
+                      "dsa_merge_partials: N too large for one launch");
+  const dim3 grid((unsigned)((N + 3) / 4)), block(256);
+  const bool pf = part_dtype == DSA_F32, of = o_dtype == DSA_F32;
+  if (pf && of)
+    DSA_LAUNCH((rank_merge_kernel<true, true>), grid, block, 0, stream, o_parts, lse_parts, R, N, V, o, lse);
+  else if (pf)
+    DSA_LAUNCH((rank_merge_kernel<true, false>), grid, block, 0, stream, o_parts, lse_parts, R, N, V, o, lse);
+  else if (of)
+    DSA_LAUNCH((rank_merge_kernel<false, true>), grid, block, 0, stream, o_parts, lse_parts, R, N, V, o, lse);
+  else
+    DSA_LAUNCH((rank_merge_kernel<false, false>), grid, block, 0, stream, o_parts, lse_parts, R, N, V, o, lse);
+  return launch_status("dsa_merge_partials");
 }

@@ -53,8 +53,10 @@ def test_invalid_arguments_rejected_without_device():
     assert L.dsa_sparse_mla_decode(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(rows), 1, 1, 128, 64,
                                    ctypes.c_float(0.1), ctypes.c_void_p(16), _lib.DSA_BF16, ctypes.c_void_p(16),
                                    None, 0, None, None) == _lib.DSA_ERR_INVALID_ARG
-    assert L.dsa_gather_kv(ctypes.c_void_p(16), None, None, 1, 1, 4, None, None, 0, 100, ctypes.c_void_p(16), 0,
-                           None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_gather_kv(ctypes.c_void_p(16), None, None, 1, 1, 4, None, None, 0, 100, ctypes.c_void_p(16), None,
+                           0, None, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_gather_kv(ctypes.c_void_p(16), None, None, 1, 1, 4, None, None, 0, 1152, ctypes.c_void_p(16),
+                           ctypes.c_void_p(18), 0, None, None) == _lib.DSA_ERR_INVALID_ARG   # sel_idx misaligned
     kv, ic = _lib.dsa_rows_t(), _lib.dsa_rows_t()
     kv.base, kv.row_bytes, ic.base, ic.row_bytes = 16, 1152, 16, 128
     p = ctypes.c_void_p(16)
@@ -115,3 +117,44 @@ def test_peak_probe_library_exports():
     assert {"dsa_peak_stream_read", "dsa_peak_stream_copy", "dsa_peak_mfma"} <= names
     L = peaks.load()
     assert L.dsa_peak_mfma(0, 0, 1, None, None) != 0         # rejected before any launch
+
+
+def test_indexer_rejects_before_joining_the_load_stream():
+    """Unsupported shapes and short key stores are rejected before the stream waits on the
+    caller's event: the event passed here is not a valid handle, so a wait would fail."""
+    L = _lib.load()
+    p = ctypes.c_void_p(16)
+    bogus_event = ctypes.c_void_p(0x1000)
+    keys = _lib.dsa_rows_t()
+    keys.base, keys.row_bytes, keys.num_rows = 16, 128, 16            # fewer than one 32-token tile
+    keys.page_table, keys.page_size, keys.pt_stride = 16, 64, 4
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(keys), _lib.DSA_E4M3, p, p, 1, 1, 64, 128, 64, p,
+                                None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert b"num_rows" in L.dsa_last_error()
+    keys.num_rows, keys.page_table, keys.req_stride = 1000, None, 1000  # dense, not whole tiles
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(keys), _lib.DSA_E4M3, p, p, 2, 1, 64, 128, 1000,
+                                p, None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
+    keys.num_rows, keys.req_stride = 1024, 500
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(keys), _lib.DSA_E4M3, p, p, 2, 1, 64, 128, 500,
+                                p, None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
+    keys.req_stride = 512
+    # (H / 32, Sq) = (4, 4) has no instantiation
+    assert L.dsa_indexer_scores(p, _lib.DSA_BF16, p, ctypes.byref(keys), _lib.DSA_E4M3, p, p, 2, 4, 128, 128, 512,
+                                p, None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
+    # fp32 path: the batch sits on the grid's y axis
+    kf = _lib.dsa_rows_t()
+    kf.base, kf.row_bytes, kf.num_rows = 16, 256, 1 << 20
+    assert L.dsa_indexer_scores(p, _lib.DSA_F32, p, ctypes.byref(kf), _lib.DSA_F32, None, p, 70000, 1, 4, 64, 64,
+                                p, None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
+
+
+def test_merge_partials_rejects_bad_arguments():
+    L = _lib.load()
+    p = ctypes.c_void_p(16)
+    assert L.dsa_merge_partials(p, _lib.DSA_F32, p, 0, 8, 512, p, _lib.DSA_BF16, p, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_merge_partials(p, _lib.DSA_F32, p, 4, 8, 500, p, _lib.DSA_BF16, p, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_merge_partials(p, _lib.DSA_E4M3, p, 4, 8, 512, p, _lib.DSA_BF16, p, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_merge_partials(ctypes.c_void_p(24), _lib.DSA_F32, p, 4, 8, 512, p, _lib.DSA_BF16, p,
+                                None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_merge_partials(None, _lib.DSA_F32, p, 4, 8, 512, p, _lib.DSA_BF16, p, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_merge_partials(None, _lib.DSA_F32, None, 4, 0, 512, None, _lib.DSA_BF16, None, None) == _lib.DSA_OK

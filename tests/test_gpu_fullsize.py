@@ -68,7 +68,7 @@ def test_decode_b32_ctx65536_full_step():
     """The benchmarked workload (B=32, 64K context, top-2048, 128 heads), as DecodeStep runs it."""
     wl = synth.make_workload(2)
     dw = DevWorkload(wl)
-    step = DecodeStep(dw)
+    step = dw.decode_step()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         step.run(stream)
@@ -87,7 +87,7 @@ def test_full_step_over_the_fp4_indexer_cache(cid):
     with MXFP4 indexer keys instead of e4m3, full size, sampled requests against the oracle."""
     wl = synth.make_workload(synth.spec(cid).scaled(idx_k_kind="mxfp4"), with_kv=True)
     dw = DevWorkload(wl)
-    step = DecodeStep(dw)
+    step = dw.decode_step()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         step.run(stream)
@@ -104,7 +104,7 @@ def test_mtp_verify_b8_ctx200k_full_step():
     """Four draft queries per request (fp8 queries, causal visibility), full size."""
     wl = synth.make_workload(3)
     dw = DevWorkload(wl)
-    step = DecodeStep(dw)
+    step = dw.decode_step()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         step.run(stream)
@@ -176,7 +176,6 @@ def test_pool_group_b16_ctx128k_full_trajectory():
     ptr = torch.zeros((B, S), dtype=torch.int32, device=DEV)
     state = [o_plan.empty_state(S, W, cfg.id_range) for _ in range(B)]
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ident = torch.arange(k, dtype=torch.int32, device=DEV).repeat(B, 1).view(B, 1, k)
     H = cfg.mla_heads
     hits = []
     for s in range(cfg.steps):
@@ -189,12 +188,13 @@ def test_pool_group_b16_ctx128k_full_trajectory():
         mc = torch.empty(B, dtype=torch.int32, device=DEV)
         dsa.dsa_plan(tkd, pids, its, ptr, S, W, is_hit, slot, mp, ms, mc, commit=False, err=err)
         sel = torch.empty((B, 1, k, cfg.kv_dim), dtype=torch.bfloat16, device=DEV)
-        dsa.dsa_gather_kv(tkd, is_hit, slot, src, pool, sel, dsa.DSA_GATHER_SERVE, err=err)
+        sel_idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+        dsa.dsa_gather_kv(tkd, is_hit, slot, src, pool, sel, dsa.DSA_GATHER_SERVE, err=err, sel_idx=sel_idx)
         q = t_u16_as_bf16(wl.extra["mla_q"][s, layer][:, None])
         o = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=DEV)
         lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
         ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, 1, H, k)), dtype=torch.uint8, device=DEV)
-        dsa.dsa_sparse_mla_decode(q, ident, dsa.Rows(sel, 1152, req_stride=k), cfg.scale, o, lse, ws=ws, err=err)
+        dsa.dsa_sparse_mla_decode(q, sel_idx, dsa.Rows(sel, 1152, req_stride=k), cfg.scale, o, lse, ws=ws, err=err)
         # group end: commit the plan, then install the surviving misses
         dsa.dsa_plan(tkd, pids, its, ptr, S, W, is_hit, slot, mp, ms, mc, commit=True, err=err)
         dsa.dsa_gather_kv(tkd, is_hit, slot, None, pool, sel, dsa.DSA_GATHER_INSTALL, err=err)

@@ -143,3 +143,28 @@ def test_mxfp4_block_scale_acts_on_its_own_32_dimensions():
             s1 = indexer.scores(dataclasses.replace(base, idx_k_scale=sc), 0)[0]
             assert np.array_equal(s1, s0 * (2 if k == j else 1)), (j, k)
     assert (s0 > 0).any()
+
+
+def test_exact_grid_scores_equal_integer_arithmetic():
+    """The tiny workload's grid (q, k integers in [-4, 4], w in {1/4, 1/2, 1}): 4 * score is
+    the integer sum_h (4 w_h) max(0, sum_d q_hd k_sd), computed here in int64 from the page
+    table by hand; the oracle's float32 scores equal it exactly, and so do scores over a
+    three-query draft window."""
+    for Sq in (1, 3):
+        wl = synth.make_workload(synth.spec(1).scaled(Sq=Sq), with_kv=False)
+        L, ps = int(wl.seq_lens[0]), wl.page_size
+        D = wl.idx_k.shape[-1]
+        flat = wl.idx_k.reshape(-1, D)
+        K = np.empty((L, D), dtype=np.int64)
+        for pos in range(L):
+            K[pos] = flat[int(wl.page_table[0, pos // ps]) * ps + pos % ps].astype(np.int64)
+        got = indexer.scores(wl, 0)
+        for t in range(Sq):
+            q = wl.idx_q[0, t].astype(np.int64)                  # [H, D]
+            w4 = (wl.idx_w[0, t] * 4).astype(np.int64)
+            assert np.array_equal(w4.astype(np.float32) / 4, wl.idx_w[0, t])
+            want4 = (np.maximum(K @ q.T, 0) * w4).sum(axis=1)      # [L] int64
+            n = L - Sq + 1 + t
+            assert np.array_equal(got[t, :n].astype(np.float64) * 4, want4[:n].astype(np.float64))
+            assert np.isneginf(got[t, n:]).all()
+            assert (want4 > 0).any() and (np.abs(want4[:n]) < 2 ** 24).all()

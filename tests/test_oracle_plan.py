@@ -193,3 +193,91 @@ def test_lru_special_cases():
     assert np.array_equal(plan.lru_hits(t, 1000), want)
     # one set of enough ways never evicts either
     assert np.array_equal(plan.fifo_hits(t, 1, 64, 64), want)
+
+
+# ---------------------------------------------------------------- one plan per group of 4 layers
+def way_fifo_sim(n_sets, W):
+    """A textbook set-associative FIFO cache with explicit ways, for one layer: each set is an
+    array of W ways and a pointer to the next way to fill.  A step's ids are looked up against
+    the contents before the step; then its misses are installed one at a time, ascending, at
+    the pointer's way (evicting whatever sat there), and the pointer moves on.  Returns a
+    stepping function giving, per id of the step, its slot for serving: the hit's slot, the
+    slot a miss still occupies after the step, or -1 for a miss evicted within the step."""
+    ways = [[-1] * W for _ in range(n_sets)]
+    ptr = [0] * n_sets
+
+    def step(U):
+        U = sorted(set(int(u) for u in U))
+        before = {ways[s][w]: s * W + w for s in range(n_sets) for w in range(W) if ways[s][w] >= 0}
+        put = {}
+        for u in U:
+            if u in before:
+                continue
+            s = u % n_sets
+            ways[s][ptr[s]] = u
+            put[u] = s * W + ptr[s]
+            ptr[s] = (ptr[s] + 1) % W
+        after = {ways[s][w]: s * W + w for s in range(n_sets) for w in range(W) if ways[s][w] >= 0}
+        res = {}
+        for u in U:
+            if u in before:
+                res[u] = (1, before[u])
+            else:
+                res[u] = (0, put[u] if after.get(u) == put[u] else -1)
+        return res
+
+    return step, ways, ptr
+
+
+@pytest.mark.parametrize("n_sets,W", [(8, 2), (16, 4), (4, 8)])
+def test_group_of_four_layers_shares_one_plan(n_sets, W):
+    """[GLM52] §4.1-§4.2: the 4 layers of a group share one top-k, and an id sits in the same
+    slot of every layer's pool, so one plan serves the whole group.  Four layers, each with its
+    own rows and its own pool kept by its own textbook FIFO (way_fifo_sim), walk a trajectory;
+    per step, planning each layer separately from the same pre-step state gives identical
+    plans, that plan equals every layer's own simulator slot for slot, serving each layer
+    through it returns that layer's rows, and committing it once at the group's end leaves
+    the state every layer's simulator holds."""
+    rng = np.random.default_rng(n_sets * 100 + W)
+    id_range, k, layers = 400, 3 * n_sets, 4
+    host = [rng.integers(0, 2 ** 16, size=(id_range, 6), dtype=np.uint16) for _ in range(layers)]
+    pools = [np.zeros((n_sets * W, 6), dtype=np.uint16) for _ in range(layers)]
+    sims = [way_fifo_sim(n_sets, W) for _ in range(layers)]
+    state = plan.empty_state(n_sets, W, id_range)
+    prev = None
+    for s in range(14):
+        if prev is None:
+            U = rng.choice(id_range, size=k, replace=False)
+        else:                               # about half of the previous set recurs
+            keep = rng.choice(prev, size=k // 2, replace=False)
+            fresh = rng.choice(np.setdiff1d(np.arange(id_range), prev), size=k - k // 2, replace=False)
+            U = np.concatenate([keep, fresh])
+        prev = np.sort(U)
+        tk = np.concatenate([prev, [-1, -1]]).astype(np.int32)[None]   # two padding entries
+        per_layer = [plan.plan_step(tk, *state, n_sets, W) for _ in range(layers)]
+        out, new_state = per_layer[0]
+        for o2, st2 in per_layer[1:]:
+            for key in ("is_hit", "slot", "miss_pos", "miss_slot"):
+                assert np.array_equal(o2[key], out[key]), key
+            assert all(np.array_equal(a, b) for a, b in zip(st2, new_state))
+        for l in range(layers):
+            want = sims[l][0](prev)
+            for j, u in enumerate(prev):
+                assert (int(out["is_hit"][0, j]), int(out["slot"][0, j])) == want[int(u)], (s, l, int(u))
+            assert (out["slot"][0, -2:] == -1).all() and (out["is_hit"][0, -2:] == 0).all()
+            # serve this layer: hits from its pool, misses from its rows; then install
+            served = np.where(out["is_hit"][0, :k, None] == 1, pools[l][np.maximum(out["slot"][0, :k], 0)],
+                              host[l][prev])
+            assert np.array_equal(served, host[l][prev]), (s, l)
+            for u, sl in zip(out["miss_pos"], out["miss_slot"]):
+                if sl >= 0:
+                    pools[l][sl] = host[l][u]
+        state = new_state
+        pool_ids, its, ptr = state
+        for l in range(layers):
+            _, ways, sptr = sims[l]
+            assert [pool_ids[sset * W + w] for sset in range(n_sets) for w in range(W)] == \
+                [ways[sset][w] for sset in range(n_sets) for w in range(W)]
+            assert list(ptr) == sptr
+            live = np.nonzero(pool_ids >= 0)[0]
+            assert np.array_equal(pools[l][live], host[l][pool_ids[live]])
