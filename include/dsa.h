@@ -22,7 +22,8 @@
  *     library never allocates memory: scratch space is a caller buffer sized by the
  *     matching *_workspace_size() call.
  *   - Every call only enqueues work on `stream` (a hipStream_t; 0 = the null stream)
- *     and returns; nothing synchronises.  There is no global mutable state.
+ *     and returns; nothing synchronises.  There is no global mutable state, except the
+ *     scratch array that dsa_sparse_mla_decode_noalloc uses instead of a workspace.
  *   - Argument checks that need no device access (null pointers, sizes, dtypes,
  *     alignment) happen before anything is enqueued and return DSA_ERR_INVALID_ARG or
  *     DSA_ERR_UNSUPPORTED; then nothing was enqueued.  A failed launch returns
@@ -261,6 +262,28 @@ dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_
                                    int B, int Sq, int H, int k, float scale, void* o,
                                    dsa_dtype_t o_dtype, float* lse, void* ws, size_t ws_bytes,
                                    int32_t* err_count, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode_noalloc — dsa_sparse_mla_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the split partials go to a scratch array inside the library instead of a
+ * caller workspace; the caller still passes q, idx, rows, o and lse.  Arguments, results and
+ * errors are those of dsa_sparse_mla_decode.
+ *   - The scratch array holds dsa_sparse_mla_noalloc_max_workspace() bytes (64 MiB) on every
+ *     device the library runs on, until the process ends.  A call whose
+ *     dsa_sparse_mla_workspace_size(B, Sq, H, k) exceeds it returns DSA_ERR_UNSUPPORTED with
+ *     nothing enqueued.
+ *   - The call allocates nothing.  Its first call on a device looks up that device's copy
+ *     of the array (hipGetSymbolAddress).
+ *   - Every call on a device shares that device's array: calls that may overlap on one
+ *     device (other streams, other threads) race on it and must be ordered by the caller.
+ *     Nothing in it needs to start at zero; each call writes every partial it reads.
+ */
+size_t dsa_sparse_mla_noalloc_max_workspace(void);
+dsa_status_t dsa_sparse_mla_decode_noalloc(const void* q, const int32_t* idx, const dsa_rows_t* rows,
+                                           int B, int Sq, int H, int k, float scale, void* o,
+                                           dsa_dtype_t o_dtype, float* lse, int32_t* err_count,
+                                           hipStream_t stream);
 
 /*
  * dsa_merge_partials — combine R partial attention results, each over its own disjoint set

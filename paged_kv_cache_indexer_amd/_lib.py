@@ -14,7 +14,8 @@ STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED
 
 EXPORTED = ["dsa_version", "dsa_last_error", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
             "dsa_plan", "dsa_gather_kv", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_merge_partials", "dsa_page_translate", "dsa_kv_write"]
+            "dsa_sparse_mla_noalloc_max_workspace", "dsa_sparse_mla_decode_noalloc", "dsa_merge_partials",
+            "dsa_page_translate", "dsa_kv_write"]
 
 
 class dsa_rows_t(ctypes.Structure):
@@ -59,6 +60,9 @@ def load() -> ctypes.CDLL:
         "dsa_sparse_mla_decode": (ctypes.c_int, [vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, sz, vp,
                                                  vp]),
+        "dsa_sparse_mla_noalloc_max_workspace": (sz, []),
+        "dsa_sparse_mla_decode_noalloc": (ctypes.c_int, [vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                         ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, vp]),
         "dsa_merge_partials": (ctypes.c_int, [vp, ctypes.c_int, vp, ctypes.c_int, i64, ctypes.c_int, vp,
                                               ctypes.c_int, vp, vp]),
         "dsa_page_translate": (ctypes.c_int, [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]),

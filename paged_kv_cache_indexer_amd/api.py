@@ -139,6 +139,16 @@ def dsa_sparse_mla_decode(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale:
                                              _stream(stream)), "dsa_sparse_mla_decode")
 
 
+def dsa_sparse_mla_decode_noalloc(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale: float, o: torch.Tensor,
+                                  lse: torch.Tensor, err: Optional[torch.Tensor] = None, stream=None):
+    """dsa_sparse_mla_decode with the split partials in the library's own scratch array."""
+    B, Sq, H, _ = q.shape
+    k = idx.shape[-1]
+    _check(_lib.load().dsa_sparse_mla_decode_noalloc(_ptr(q), _ptr(idx), rows.ref(), B, Sq, H, k, float(scale),
+                                                     _ptr(o), _dtype_code(o), _ptr(lse), _ptr(err), _stream(stream)),
+           "dsa_sparse_mla_decode_noalloc")
+
+
 def dsa_merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                        stream=None):
     """o_parts [R, ..., V] (float32 or bf16), lse_parts [R, ...] float32 -> o [..., V], lse [...]:

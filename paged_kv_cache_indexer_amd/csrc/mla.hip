@@ -701,3 +701,61 @@ extern "C" dsa_status_t dsa_merge_partials(const void* o_parts, dsa_dtype_t part
     DSA_LAUNCH((rank_merge_kernel<false, false>), grid, block, 0, stream, o_parts, lse_parts, R, N, V, o, lse);
   return launch_status("dsa_merge_partials");
 }
+
+// ---------------------------------------------------------------------------------------------
+// dsa_sparse_mla_decode_noalloc: the same kernels with their split partials in a scratch array
+// of the library instead of a caller workspace, for callers that cannot allocate.  Host code
+// never names `scratch` itself (its host-side symbol is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+namespace dsa {
+
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::atomic<void*> g_scratch_by_dev[kMaxDevices];
+
+// device address of this device's scratch array, or nullptr (error text set)
+static void* scratch_for_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_last_error("dsa_sparse_mla_decode_noalloc: no current device below %d (%s)", kMaxDevices,
+                   hipGetErrorString(e));
+    return nullptr;
+  }
+  void* p = g_scratch_by_dev[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // concurrent first calls on one device both obtain the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_last_error("dsa_sparse_mla_decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_by_dev[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace dsa
+
+extern "C" size_t dsa_sparse_mla_noalloc_max_workspace(void) { return dsa::kNoAllocScratchBytes; }
+
+extern "C" dsa_status_t dsa_sparse_mla_decode_noalloc(const void* q, const int32_t* idx, const dsa_rows_t* rows,
+                                                      int B, int Sq, int H, int k, float scale, void* o,
+                                                      dsa_dtype_t o_dtype, float* lse, int32_t* err_count,
+                                                      hipStream_t stream) {
+  using namespace dsa;
+  DSA_CHECK_ARG(B >= 0 && Sq >= 1 && H >= 1 && k >= 1, "dsa_sparse_mla_decode_noalloc: bad sizes");
+  if (B == 0) return DSA_OK;
+  const size_t need = dsa_sparse_mla_workspace_size(B, Sq, H, k);
+  DSA_CHECK_SUPPORTED(need <= kNoAllocScratchBytes,
+                      "dsa_sparse_mla_decode_noalloc: needs %zu bytes of split partials, above the %zu-byte "
+                      "scratch array (use dsa_sparse_mla_decode with a workspace)",
+                      need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_for_current_device();
+    if (ws == nullptr) return DSA_ERR_HIP;
+  }
+  return dsa_sparse_mla_decode(q, idx, rows, B, Sq, H, k, scale, o, o_dtype, lse, ws, need, err_count, stream);
+}
