@@ -30,27 +30,46 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 KEY_BYTES = {"e4m3": lambda D: D + 4,          # e4m3 codes + float32 per-token scale
-             "mxfp4": lambda D: D // 2 + D // 32}  # E2M1 codes + E8M0 block scales
+             "mxfp4": lambda D: D // 2 + D // 32,  # E2M1 codes + E8M0 block scales
+             "f32": lambda D: 4 * D}       # float32 keys, no scale
 
 
-def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2):
+def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2, o_bytes=2):
     """Bytes / flops each kernel must move or compute for one layer-step (no re-reads); Sq
-    query tokens per request, each scoring the whole cache and attending its own top-k."""
+    query tokens per request, each scoring the whole cache and attending its own top-k.
+    L is one cache length for every request or a list of per-request lengths."""
+    lens = [int(L)] * B if isinstance(L, (int, np.integer)) else [int(x) for x in L]
     Q = B * Sq
-    idx_bytes = (B * L * KEY_BYTES[keys](D)  # keys and their scales, read once for all Sq queries
+    tokens = sum(lens)
+    sel = sum(min(k, l - Sq + 1 + t) for l in lens for t in range(Sq))   # rows each query attends
+    idx_bytes = (tokens * KEY_BYTES[keys](D)  # keys and their scales, read once for all Sq queries
                  + Q * H_idx * D * q_bytes  # queries
                  + Q * H_idx * 4      # head weights
-                 + B * -(-L // ps) * 4  # page table (a partial last page counts)
-                 + Q * L * 4)         # scores out
-    idx_flops = 2 * Q * H_idx * D * L
-    topk_bytes = Q * L * 4 + Q * k * 4
-    mla_bytes = (Q * k * 1152         # selected latent rows
+                 + sum(-(-l // ps) for l in lens) * 4  # page table (a partial last page counts)
+                 + Sq * tokens * 4)   # scores out
+    idx_flops = 2 * Sq * H_idx * D * tokens
+    topk_bytes = Sq * tokens * 4 + Q * k * 4
+    mla_bytes = (sel * 1152           # selected latent rows
                  + Q * H_mla * 576 * 2  # q
                  + Q * k * 4          # indices
-                 + Q * H_mla * 512 * 2  # o (bf16)
+                 + Q * H_mla * 512 * o_bytes  # o
                  + Q * H_mla * 4)     # lse
-    mla_flops = 2 * Q * H_mla * k * (576 + 512)
+    mla_flops = 2 * H_mla * sel * (576 + 512)
     return {"indexer": (idx_bytes, idx_flops), "topk": (topk_bytes, 0), "mla": (mla_bytes, mla_flops)}
+
+
+# per workload: metric, workload name, attention output dtype
+CONFIG_LINES = {
+    1: ("DSA decode layer-steps/s, tiny workload (B=1, 4K ctx, top-256, fp32 grid indexer); launch-bound",
+        "decode_tiny_b1_ctx4096_top256", "bf16"),
+    2: ("DSA decode layer-steps/s (B=32, 64K ctx, top-2048); % HBM/MFMA roofline",
+        "decode_b32_ctx65536_top2048", "bf16"),
+    3: ("DSA MTP-verify layer-steps/s (B=8, 200K ctx, 4 query tokens, top-2048); % HBM/MFMA roofline",
+        "mtp_verify_b8_ctx200004_sq4_top2048", "bf16"),
+    5: ("DSA decode layer-steps/s, rank-0 share of a 4-way page-sharded cache (66 requests, 30K-200K and 2 x 1M "
+        "ctx, top-2048 over owned tokens, float32 partial o); % HBM/MFMA roofline",
+        "rank0_share_b66_mixed_top2048", "f32"),
+}
 
 
 _CPU_WL = None       # the workload the forked oracle workers read (copy-on-write)
@@ -237,9 +256,13 @@ def main():
                     help="distinct per-layer caches the steps rotate through (a model's successive layers "
                          "read different caches; rotating keeps a step from hitting the previous step's "
                          "bytes in the 256 MB last-level cache)")
-    ap.add_argument("--config", type=int, choices=[2, 3], default=2,
-                    help="2: the decode workload (B=32, 64K context, one query token); 3: MTP verify (B=8, "
-                         "200K context, 4 query tokens with fp8 queries), printed as its own line")
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 5], default=2,
+                    help="2: the decode workload (B=32, 64K context, one query token); 1: the tiny workload "
+                         "(B=1, 4K context, fp32 grid indexer); 3: MTP verify (B=8, 200K context, 4 query tokens "
+                         "with fp8 queries); 5: rank 0's share of a 4-way page-sharded cache (66 mixed-length "
+                         "requests, float32 partial o); configs other than 2 print their own line")
+    ap.add_argument("--replays", type=int, default=5,
+                    help="timed replays of the K-step graph; value and ms_per_step are their median")
     ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
     ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
@@ -269,13 +292,19 @@ def main():
         bench_pool_group(args)
         return
     cfg = synth.spec(args.config)
-    wl = synth.make_workload(cfg.scaled(idx_k_kind="mxfp4") if args.keys == "mxfp4" else cfg)
+    if args.keys == "mxfp4":
+        if cfg.idx_k_kind == "grid_f32":
+            sys.exit("bench.py: the tiny workload's indexer keys are the fp32 grid; --keys mxfp4 does not apply")
+        cfg = cfg.scaled(idx_k_kind="mxfp4")
+    wl = synth.make_workload(cfg)
+    metric, workload, o_kind = CONFIG_LINES[args.config]
+    keys = "f32" if wl.idx_k_dtype == "f32" else args.keys
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)     # forks: before any GPU call
     torch.cuda.set_device(0)
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
-    step = dw.decode_step(args.layers)
+    step = dw.decode_step(args.layers, o_dtype=torch.float32 if o_kind == "f32" else torch.bfloat16)
     names = ["indexer", "topk", "mla"]
     stream = torch.cuda.Stream()            # non-default stream: the step is captured and replayed
 
@@ -312,11 +341,16 @@ def main():
         def run_timed():
             for i in range(args.steps):
                 step.run(stream, layer=i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_timed()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # the K timed steps are replayed `--replays` times, each bracketed by synchronisations;
+    # the median replay is the reported figure
+    walls = []
+    for _ in range(max(1, args.replays)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_timed()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    wall = float(np.median(walls))
     # per-stage duration: each stage launched K times back to back (layers rotating) between two
     # HIP events on the launch stream; the launches queue faster than they run, so the span
     # holds no launch gaps
@@ -339,8 +373,9 @@ def main():
             print(f"bench.py: peak probes skipped ({e})", file=sys.stderr)
 
     fp8_q = wl.idx_q_dtype == "e4m3"                 # the indexer then runs on the fp8 MFMA
-    work = algorithmic_work(B, L, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, args.keys, Sq=Sq,
-                            q_bytes=1 if fp8_q else 2)
+    q_bytes = {"e4m3": 1, "bf16": 2, "f32": 4}[wl.idx_q_dtype]
+    work = algorithmic_work(B, wl.seq_lens, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, keys,
+                            Sq=Sq, q_bytes=q_bytes, o_bytes=4 if o_kind == "f32" else 2)
     peak = {"indexer": FP8_PEAK_TFLOPS if fp8_q else BF16_PEAK_TFLOPS, "topk": BF16_PEAK_TFLOPS,
             "mla": BF16_PEAK_TFLOPS}
     kernels = {}
@@ -357,14 +392,13 @@ def main():
     by = work[dom][0]
     roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS,
-                "traffic": (measured_traffic(dom + ("_mxfp4" if dom == "indexer" and args.keys == "mxfp4" else ""))
+                "traffic": (measured_traffic(dom + ("_mxfp4" if dom == "indexer" and keys == "mxfp4" else ""))
                             if args.config == 2 else None),
                 "kernel": dom}
 
     ms = wall / args.steps * 1e3
     out = {
-        "metric": ("DSA decode layer-steps/s (B=32, 64K ctx, top-2048); % HBM/MFMA roofline" if args.config == 2 else
-                   "DSA MTP-verify layer-steps/s (B=8, 200K ctx, 4 query tokens, top-2048); % HBM/MFMA roofline"),
+        "metric": metric,
         "value": args.steps / wall,
         "unit": "layer-steps/s",
         "n_gpus": 1,
@@ -374,17 +408,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not fp8_q else "fp8 indexer, bf16 attention",
-        "data": ("synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)" if args.keys == "e4m3" else
+        "dtype": ("bf16" if wl.idx_q_dtype == "bf16" else "fp8 indexer, bf16 attention" if fp8_q else
+                  "f32 indexer (exact integer grid), bf16 attention"),
+        "data": ("synthetic (seeded N(0,1) / e4m3-scaled keys, random page permutation)" if keys == "e4m3" else
                  "synthetic (seeded N(0,1); MXFP4 keys drawn as uniform codes, E8M0 in 124..128; random page "
+                 "permutation)" if keys == "mxfp4" else
+                 "synthetic (seeded integer grid in [-4, 4] for the indexer, N(0,1) bf16 latent rows, random page "
                  "permutation)"),
         "launch": mode,
+        "replays_ms_per_step": [w / args.steps * 1e3 for w in walls],
         "kernel_timing": "per stage: HIP events on the launch stream around K back-to-back launches of that stage",
-        "config": {"workload": ("decode_b32_ctx65536_top2048" if args.config == 2 else
-                                "mtp_verify_b8_ctx200004_sq4_top2048"), "batch": B, "context": L, "query_tokens": Sq,
+        "config": {"workload": workload, "batch": B, "context": L, "query_tokens": Sq,
+                   "cached_tokens": int(np.sum(wl.seq_lens, dtype=np.int64)),
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
-                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "layers_rotated": args.layers,
-                   "keys": "e4m3 + fp32 scale" if args.keys == "e4m3" else "mxfp4 (e2m1 + e8m0 per 32)"},
+                   "topk": k, "mla_heads": H_mla, "latent": "512+64 bf16", "o": o_kind,
+                   "layers_rotated": args.layers,
+                   "keys": {"e4m3": "e4m3 + fp32 scale", "mxfp4": "mxfp4 (e2m1 + e8m0 per 32)",
+                            "f32": "fp32 integer grid"}[keys]},
         "roofline": roofline,
         "step_roofline": {"t_star_us": t_star * 1e6, "measured_us": ms * 1e3, "frac": t_star * 1e6 / (ms * 1e3)},
         "measured_peaks": (({"error": meas_err} if meas_err else None) if meas is None else
@@ -446,12 +486,17 @@ def bench_pool_group(args):
     group, 2048 selected rows per request): the 8-step top-k trajectory from an empty pool,
     per step one plan and per layer serve (hits from the device pool, misses from pinned
     host rows over the host link) -> attention -> install, with installs serial or on an
-    auxiliary stream overlapped with attention.  Host rows are zero (only time is measured)."""
+    auxiliary stream overlapped with attention.  Host rows are zero (only time is measured).
+
+    The host link is measured in the same run: an all-miss serve of 16 x 2048 random rows
+    from the pinned host rows (the access pattern of the misses) and a plain pinned-to-device
+    copy of 1 GiB.  Each configuration's miss bytes (counted from its plans in an untimed
+    pass) over its time give the host-link rate it sustains, reported against both."""
     import torch
     import synth
     from synth import gen as sgen
     import paged_kv_cache_indexer_amd as dsa
-    from paged_kv_cache_indexer_amd.pipeline import HipMark, PoolGroupStep, host_device_ptr
+    from paged_kv_cache_indexer_amd.pipeline import HipMark, MtpDraftSteps, PoolGroupStep, host_device_ptr
     cfg = synth.spec(4)
     traj = sgen.topk_trajectory(cfg)
     hosts = []
@@ -462,8 +507,53 @@ def bench_pool_group(args):
     H = cfg.mla_heads
     q = [torch.randn(cfg.B, 1, H, 576, device="cuda").to(torch.bfloat16) for _ in range(cfg.layers)]
     tks = [torch.from_numpy(np.ascontiguousarray(traj[s][:, None, :])).cuda() for s in range(cfg.steps)]
+
+    def timed(fn, reps=5):
+        stream = torch.cuda.Stream()
+        fn(stream)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = HipMark(), HipMark()
+            e0.record(stream)
+            fn(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = e0.elapsed_ms(e1) if best is None else min(best, e0.elapsed_ms(e1))
+        return best
+
+    # ---- the host link: an all-miss serve of random rows, and a plain pinned copy
+    g = torch.Generator().manual_seed(11)
+    rand_pos = torch.stack([torch.sort(torch.randperm(cfg.L, generator=g)[:cfg.topk]).values
+                            for _ in range(cfg.B)]).to(torch.int32).view(cfg.B, 1, cfg.topk).cuda()
+    sel = torch.empty((cfg.B, 1, cfg.topk, 576), dtype=torch.bfloat16, device="cuda")
+    serve_ms = timed(lambda st: dsa.dsa_gather_kv(rand_pos, None, None, rows[0], None, sel, dsa.DSA_GATHER_SERVE,
+                                                  stream=st))
+    serve_bytes = cfg.B * cfg.topk * 1152
+    pin = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dev_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def h2d(st):
+        with torch.cuda.stream(st):
+            dev_buf.copy_(pin, non_blocking=True)
+    copy_ms = timed(h2d, reps=3)
+    del pin, dev_buf
+    link = {"all_miss_serve_GBps": serve_bytes / serve_ms / 1e6, "pinned_copy_GBps": (1 << 30) / copy_ms / 1e6,
+            "serve_sample": f"{cfg.B} x {cfg.topk} random rows of 1152 B from pinned host rows"}
+
     res = []
     for n_sets, ways in ((1024, 8), (1024, 16)):
+        # untimed pass: the misses each step serves over the host link (all layers)
+        pg = PoolGroupStep(cfg.B, cfg.topk, H, n_sets, ways, cfg.id_range, rows, cfg.scale)
+        stream = torch.cuda.Stream()
+        misses = []
+        for s in range(cfg.steps):
+            pg.run(stream, tks[s], q)
+            torch.cuda.synchronize()
+            misses.append(int(pg.plan_out[s % 2]["mc"].sum().item()))
+        hits = [cfg.B * cfg.topk - m for m in misses]
+        del pg
+        miss_bytes = sum(misses) * 1152 * cfg.layers
         for aux in (False, True):
             best = None
             for rep in range(3):
@@ -480,13 +570,16 @@ def bench_pool_group(args):
                 ms = e0.elapsed_ms(e1) / cfg.steps
                 assert int(pg.err) == 0
                 best = ms if best is None else min(best, ms)
-                hit = float(sum(pg.plan_out[(cfg.steps - 1) % 2]["is_hit"].sum().item() for _ in [0])) / (cfg.B * cfg.topk)
                 del pg
+            rate = miss_bytes / cfg.steps / best / 1e6
             res.append({"pool": f"{n_sets}x{ways}", "install": "aux stream" if aux else "serial",
-                        "ms_per_step": best, "ms_per_layer": best / cfg.layers, "last_step_hit_rate": hit})
+                        "ms_per_step": best, "ms_per_layer": best / cfg.layers,
+                        "hit_rate_steps_1_7": sum(hits[1:]) / (len(hits[1:]) * cfg.B * cfg.topk),
+                        "miss_MB_per_step": miss_bytes / cfg.steps / 1e6, "host_link_GBps": rate,
+                        "frac_of_all_miss_serve": rate / link["all_miss_serve_GBps"],
+                        "frac_of_pinned_copy": rate / link["pinned_copy_GBps"]})
     # MTP draft steps over a frozen selection (next_n = 4 attention passes per verify step):
     # serve once and reuse the selection buffer, or serve again before every draft step
-    from paged_kv_cache_indexer_amd.pipeline import MtpDraftSteps
     next_n = 4
     qd = [q for _ in range(next_n)]
     mtp = []
@@ -510,8 +603,8 @@ def bench_pool_group(args):
                     "ms_per_verify_step": best})
     print(json.dumps({"metric": "pool-group decode ms per step (plan + 4 x (serve, attention, install))",
                       "entry": "pool_group", "data": "synthetic trajectory; zero host rows (timing only)",
-                      "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk, "runs": res,
-                      "mtp_draft": mtp}),
+                      "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk,
+                      "host_link": link, "runs": res, "mtp_draft": mtp}),
           flush=True)
 
 

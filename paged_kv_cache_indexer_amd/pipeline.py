@@ -91,7 +91,7 @@ class DecodeStep:
 
     def __init__(self, idx_q: torch.Tensor, idx_w: torch.Tensor, seq_lens: torch.Tensor, mla_q: torch.Tensor,
                  layers: List[LayerCaches], topk: int, scale: float, max_len: int, k_dtype: int, q_dtype: int,
-                 err: Optional[torch.Tensor] = None):
+                 err: Optional[torch.Tensor] = None, o_dtype=torch.bfloat16):
         dev = idx_q.device
         self.idx_q, self.idx_w, self.seq_lens, self.mla_q = idx_q, idx_w, seq_lens, mla_q
         self.layers, self.scale, self.k_dtype, self.q_dtype = layers, scale, k_dtype, q_dtype
@@ -100,7 +100,7 @@ class DecodeStep:
         H = mla_q.shape[2]
         self.scores = torch.empty((B, Sq, max_len), dtype=torch.float32, device=dev)
         self.idx = torch.empty((B, Sq, topk), dtype=torch.int32, device=dev)
-        self.o = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((B, Sq, H, 512), dtype=o_dtype, device=dev)
         self.lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
         self.ws_mla = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H, topk)), dtype=torch.uint8,
                                   device=dev)
