@@ -9,9 +9,11 @@
  *
  *   dsa_indexer_scores     Lightning-Indexer scan over every visible cached token   [GLM52] §2.1
  *   dsa_topk               top-k positions per query (k = 2048 in the pages)        [GLM52] §2.1
+ *   dsa_topk_union         de-duplicated union of a request's query selections     [GLM52] §4.2, §5.1
  *   dsa_plan               shared-group pool plan, set-associative FIFO            [GLM52] §3, §4.2-4.3, §5
  *   dsa_gather_kv          per-layer serve (pool / paged / host rows) and install  [GLM52] §4.4, §5
  *   dsa_sparse_mla_decode  MLA latent attention over the selected rows only        [TSA] "MLA", [GLM52] §2.1
+ *   dsa_sparse_mla_decode_union  the same over the union, query tokens packed       [TSA] "MLA", [GLM52] §5.1
  *   dsa_merge_partials     LSE merge of per-rank (or per-split) partial attention  [TSA] "MLA", [HCCP] §1.1
  *   dsa_page_translate     page-sharded ownership closed form                      [HCCP] §1.1
  *   dsa_kv_write           new tokens' latent rows and e4m3 or MXFP4 indexer keys into the
@@ -165,6 +167,25 @@ dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* 
                       int Sq, int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * dsa_topk_union — the de-duplicated union of each request's Sq selections ([GLM52] §4.2: the
+ * planner works on the de-duplicated union of a step's top-k positions; §5.1: the draft
+ * tokens of speculative decoding select overlapping positions), for serving each distinct row
+ * once and for attention over the union with per-query membership.
+ *
+ *   topk    [B, Sq, k] int32, each row ascending with -1 padding at the end (as dsa_topk writes)
+ *   uni     [B, Sq * k] int32 out: the distinct valid positions of request b, ascending, then -1
+ *   count   [B] int32 out: number of distinct positions
+ *   uidx    [B, Sq, k] int32 out, optional: index in uni[b] of each entry's position, -1 for
+ *           padding (so uni[b][uidx[b,t,j]] == topk[b,t,j])
+ *   member  [B, Sq, W] uint32 out, optional, W = ceil(Sq * k / 32): bit u % 32 of word u / 32
+ *           of row (b, t) is set iff uni[b][u] is one of query t's positions
+ * A row found out of order adds one to err_count per out-of-order entry (the union is then
+ * unspecified).  Supported: Sq <= 16, Sq * k <= 8192.
+ */
+dsa_status_t dsa_topk_union(const int32_t* topk, int B, int Sq, int k, int32_t* uni, int32_t* count,
+                            int32_t* uidx, uint32_t* member, int32_t* err_count, hipStream_t stream);
+
+/*
  * dsa_plan — shared-group pool plan ("DsaPlan", [GLM52] §4.2 and §5), run once per
  * decode step for a group of layers that share one top-k ([GLM52] §4.1, groups of 4).
  * The device pool of each request has n_sets sets of `ways` slots; id u belongs to
@@ -262,6 +283,34 @@ dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_
                                    int B, int Sq, int H, int k, float scale, void* o,
                                    dsa_dtype_t o_dtype, float* lse, void* ws, size_t ws_bytes,
                                    int32_t* err_count, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode_union — sparse MLA for the Sq query tokens of a request over the union
+ * of their selections (dsa_topk_union), with the query tokens packed into the head axis of
+ * the work-groups ([TSA] "MLA (tokenspeed-mla)": fold_sq_factor folds the query tokens of a
+ * step into the MMA M dimension; [GLM52] §5.1: draft tokens share most of their selection).
+ * Each union row is loaded once per work-group and every query token attends only over the
+ * entries its membership bits mark, so the result per (b, t, h) is dsa_sparse_mla_decode's
+ * over that query's own selection (up to rounding order).
+ *
+ *   q       [B, Sq, H, 576] bf16
+ *   uni     [B, U] int32 positions into `rows` (-1 = skip), from dsa_topk_union (U = Sq * k),
+ *           or any row list with its membership masks
+ *   count   [B] int32 or NULL: entries past count[b] are not read
+ *   member  [B, Sq, ceil(U / 32)] uint32 membership bits (as dsa_topk_union writes them)
+ *   rows, o [B, Sq, H, 512], lse [B, Sq, H], scale, err_count: as dsa_sparse_mla_decode
+ *   ws      workspace of dsa_sparse_mla_union_workspace_size(B, Sq, H, U) bytes
+ * Packing pays when one work-group holds more query heads than one query token has (a
+ * work-group holds 64 heads): then a row shared by several query tokens is loaded once
+ * instead of once per token.  Supported: H a multiple of 16, Sq * H <= 2^20, and the limits of
+ * dsa_sparse_mla_decode for B requests of Sq * H heads over U entries.
+ */
+size_t dsa_sparse_mla_union_workspace_size(int B, int Sq, int H, int U);
+dsa_status_t dsa_sparse_mla_decode_union(const void* q, const int32_t* uni, const int32_t* count,
+                                         const uint32_t* member, const dsa_rows_t* rows, int B, int Sq,
+                                         int H, int U, float scale, void* o, dsa_dtype_t o_dtype,
+                                         float* lse, void* ws, size_t ws_bytes, int32_t* err_count,
+                                         hipStream_t stream);
 
 /*
  * dsa_sparse_mla_decode_noalloc — dsa_sparse_mla_decode for callers that cannot allocate

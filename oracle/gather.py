@@ -26,3 +26,27 @@ def install(pool_rows: np.ndarray, full_rows: np.ndarray, miss_pos, miss_slot) -
         if s >= 0:
             pool[s] = full_rows[p]
     return pool
+
+
+def union_select(topk: np.ndarray):
+    """De-duplicated union of one request's selections (test infrastructure only).
+
+    [GLM52] §4.2: the planner works on the de-duplicated, ascending union of the positions
+    the query tokens of a step select, so a position several query tokens share is fetched
+    once; §5.1: in speculative decoding the draft tokens' selections overlap.  Each query
+    then attends over its own positions, which are a subset of the union.
+
+    topk  int [Sq, k] positions (each row ascending, -1 padding)
+    Returns (U int64 [n] ascending distinct valid positions,
+             uidx int32 [Sq, k] index of each entry's position in U, -1 for padding,
+             member bool [Sq, n] member[t, u] iff U[u] is one of query t's positions).
+    """
+    topk = np.asarray(topk, dtype=np.int64)
+    U = np.unique(topk[topk >= 0])
+    uidx = np.full(topk.shape, -1, dtype=np.int32)
+    ok = topk >= 0
+    uidx[ok] = np.searchsorted(U, topk[ok])
+    member = np.zeros((topk.shape[0], len(U)), dtype=bool)
+    for t in range(topk.shape[0]):
+        member[t, uidx[t][uidx[t] >= 0]] = True
+    return U, uidx, member

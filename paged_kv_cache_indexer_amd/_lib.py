@@ -13,6 +13,7 @@ STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED
                 -4: "DSA_ERR_WORKSPACE"}
 
 EXPORTED = ["dsa_version", "dsa_last_error", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+            "dsa_topk_union", "dsa_sparse_mla_union_workspace_size", "dsa_sparse_mla_decode_union",
             "dsa_plan", "dsa_gather_kv", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_noalloc_max_workspace", "dsa_sparse_mla_decode_noalloc", "dsa_merge_partials",
             "dsa_page_translate", "dsa_kv_write"]
@@ -60,6 +61,11 @@ def load() -> ctypes.CDLL:
         "dsa_sparse_mla_decode": (ctypes.c_int, [vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, sz, vp,
                                                  vp]),
+        "dsa_topk_union": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]),
+        "dsa_sparse_mla_union_workspace_size": (sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+        "dsa_sparse_mla_decode_union": (ctypes.c_int, [vp, vp, vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, sz, vp,
+                                                       vp]),
         "dsa_sparse_mla_noalloc_max_workspace": (sz, []),
         "dsa_sparse_mla_decode_noalloc": (ctypes.c_int, [vp, vp, prow, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                          ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, vp]),

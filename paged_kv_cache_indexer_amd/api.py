@@ -103,6 +103,14 @@ def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor, ws
                                 ws_bytes, _stream(stream)), "dsa_topk")
 
 
+def dsa_topk_union(topk: torch.Tensor, uni: torch.Tensor, count: torch.Tensor, uidx: Optional[torch.Tensor] = None,
+                   member: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None):
+    """topk [B, Sq, k] -> uni [B, Sq*k], count [B], uidx [B, Sq, k], member [B, Sq, ceil(Sq*k/32)] (int32 views)."""
+    B, Sq, k = topk.shape
+    _check(_lib.load().dsa_topk_union(_ptr(topk), B, Sq, k, _ptr(uni), _ptr(count), _ptr(uidx), _ptr(member),
+                                      _ptr(err), _stream(stream)), "dsa_topk_union")
+
+
 def dsa_plan(topk: torch.Tensor, pool_ids: torch.Tensor, id_to_slot: torch.Tensor, ptr: torch.Tensor, n_sets: int,
              ways: int, is_hit: torch.Tensor, slot: torch.Tensor, miss_pos: torch.Tensor, miss_slot: torch.Tensor,
              miss_count: torch.Tensor, commit: bool = True, err: Optional[torch.Tensor] = None, stream=None):
@@ -137,6 +145,23 @@ def dsa_sparse_mla_decode(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale:
     _check(_lib.load().dsa_sparse_mla_decode(_ptr(q), _ptr(idx), rows.ref(), B, Sq, H, k, float(scale), _ptr(o),
                                              _dtype_code(o), _ptr(lse), _ptr(ws), ws_bytes, _ptr(err),
                                              _stream(stream)), "dsa_sparse_mla_decode")
+
+
+def dsa_sparse_mla_union_workspace_size(B: int, Sq: int, H: int, U: int) -> int:
+    return _lib.load().dsa_sparse_mla_union_workspace_size(B, Sq, H, U)
+
+
+def dsa_sparse_mla_decode_union(q: torch.Tensor, uni: torch.Tensor, count: Optional[torch.Tensor],
+                                member: torch.Tensor, rows: Rows, scale: float, o: torch.Tensor, lse: torch.Tensor,
+                                ws: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None):
+    """q [B, Sq, H, 576]; uni [B, U]; member [B, Sq, ceil(U/32)] -> o [B, Sq, H, 512], lse [B, Sq, H]."""
+    B, Sq, H, _ = q.shape
+    U = uni.shape[-1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.load().dsa_sparse_mla_decode_union(_ptr(q), _ptr(uni), _ptr(count), _ptr(member), rows.ref(), B, Sq,
+                                                   H, U, float(scale), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
+                                                   ws_bytes, _ptr(err), _stream(stream)),
+           "dsa_sparse_mla_decode_union")
 
 
 def dsa_sparse_mla_decode_noalloc(q: torch.Tensor, idx: torch.Tensor, rows: Rows, scale: float, o: torch.Tensor,

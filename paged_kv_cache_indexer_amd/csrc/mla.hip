@@ -54,6 +54,12 @@ struct MlaArgs {
   void* part_o;            // [QR, splits, H, 512] in o's dtype, normalised   -- splits > 1
   float* part_lse;         // [QR, splits, H]
   int32_t* err;
+  // union form (query tokens folded into the head axis): entries of row qr past counts[qr]
+  // are skipped; wave heads of query t = head / fold_h only see entries whose bit is set in
+  // member[(qr * fold_sq + t) * mwords + entry / 32]
+  const int32_t* counts;   // [QR] or null
+  const uint32_t* member;  // or null
+  int fold_h, fold_sq, mwords;
 };
 
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -140,10 +146,11 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   static_assert(NSRC * NW == 4, "NW must divide the 4 token groups of a tile");
   constexpr int PD = (NS == 1) ? 2 : 1;     // iterations a tile is loaded ahead
   constexpr int RING = NS * (PD + 1);       // LDS tiles
-  static_assert(RING * kTileBytes + kMaxSplit * 8 + 128 <= 160 * 1024, "LDS budget");
+  static_assert(RING * kTileBytes + kMaxSplit * 8 + 128 + NW * kMaxSplit / 8 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t ring[RING][kTileBytes];
   __shared__ int64_t rowoff[kMaxSplit];     // byte offset of each selected row of the split, -1 = none
   __shared__ uint32_t tmask[kMaxSplit / kTT];  // valid-row bits per tile
+  __shared__ uint32_t mmask[NW][kMaxSplit / kTT];   // union form: the entries each head group's query selected
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,8 +166,9 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   const bool head_ok = head < a.H;
 
   const int e_begin = split * a.per_split;
-  const int e_end = min(e_begin + a.per_split, a.k);
-  const int ntiles = (e_end - e_begin + kTT - 1) / kTT;
+  const int kq = a.counts ? max(0, min(a.k, a.counts[qr])) : a.k;   // entries of this row
+  const int e_end = min(e_begin + a.per_split, kq);
+  const int ntiles = e_end > e_begin ? (e_end - e_begin + kTT - 1) / kTT : 0;
   const int32_t* idx = a.idx + (int64_t)qr * a.k;
   // rows that are padding or unresolvable are loaded from this query row instead (finite
   // values; their probabilities are exactly zero)
@@ -211,8 +219,13 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
 #pragma unroll
     for (int vm = 0; vm < 4; ++vm) voff[vm] = chunk_byte(tok, 2 * vm + (qq >> 1)) + (qq & 1) * 8;
   }
+  if (a.member && stream == 0 && lane < ntiles) {
+    // the query of this wave's 16 heads (fold_h is a multiple of 16, so they share one)
+    const int t = (hb * 16 * NW + ws * 16) / a.fold_h;
+    mmask[ws][lane] = (t < a.fold_sq) ? a.member[((int64_t)qr * a.fold_sq + t) * a.mwords + e_begin / kTT + lane] : 0u;
+  }
   wait_vmcnt<0>();              // q^T is resident before any row load is in flight
-  __syncthreads();              // rowoff / tmask ready
+  __syncthreads();              // rowoff / tmask / mmask ready
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
   const char* nsrc[NSRC];       // rows of the next tile this wave issues
@@ -292,7 +305,8 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
     float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};   // tokens 4g+i, 16+4g+i
 
     // ---- online softmax for head n
-    const uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[T]);
+    uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[T]);
+    if (a.member) vmask &= __builtin_amdgcn_readfirstlane(mmask[ws][T]);
     if (vmask != 0xffffffffu) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -543,9 +557,54 @@ extern "C" size_t dsa_sparse_mla_workspace_size(int B, int Sq, int H, int k) {
   return (size_t)B * Sq * splits * H * (dsa::kVDim + 1) * sizeof(float);
 }
 
+namespace dsa {
+struct MlaUnion {
+  const int32_t* counts = nullptr;
+  const uint32_t* member = nullptr;
+  int fold_h = 0, fold_sq = 0, mwords = 0;
+};
+static dsa_status_t mla_decode_impl(const void* q, const int32_t* idx, const dsa_rows_t* rows, int B, int Sq, int H,
+                                    int k, float scale, void* o, dsa_dtype_t o_dtype, float* lse, void* ws,
+                                    size_t ws_bytes, int32_t* err_count, hipStream_t stream, const MlaUnion& un);
+}  // namespace dsa
+
 extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_rows_t* rows, int B, int Sq,
                                               int H, int k, float scale, void* o, dsa_dtype_t o_dtype, float* lse,
                                               void* ws, size_t ws_bytes, int32_t* err_count, hipStream_t stream) {
+  return dsa::mla_decode_impl(q, idx, rows, B, Sq, H, k, scale, o, o_dtype, lse, ws, ws_bytes, err_count, stream,
+                              dsa::MlaUnion{});
+}
+
+extern "C" size_t dsa_sparse_mla_union_workspace_size(int B, int Sq, int H, int U) {
+  if (B <= 0 || Sq <= 0 || H <= 0 || U <= 0 || (int64_t)Sq * H > (1 << 20)) return 0;
+  return dsa_sparse_mla_workspace_size(B, 1, Sq * H, U);
+}
+
+extern "C" dsa_status_t dsa_sparse_mla_decode_union(const void* q, const int32_t* uni, const int32_t* count,
+                                                    const uint32_t* member, const dsa_rows_t* rows, int B, int Sq,
+                                                    int H, int U, float scale, void* o, dsa_dtype_t o_dtype,
+                                                    float* lse, void* ws, size_t ws_bytes, int32_t* err_count,
+                                                    hipStream_t stream) {
+  using namespace dsa;
+  DSA_CHECK_ARG(B >= 0 && Sq >= 1 && H >= 1 && U >= 1, "dsa_sparse_mla_decode_union: bad sizes");
+  if (B == 0) return DSA_OK;
+  DSA_CHECK_ARG(member, "dsa_sparse_mla_decode_union: null member");
+  DSA_CHECK_SUPPORTED(H % 16 == 0 && (int64_t)Sq * H <= (1 << 20),
+                      "dsa_sparse_mla_decode_union: needs H %% 16 == 0 and Sq * H <= 2^20");
+  MlaUnion un;
+  un.counts = count;
+  un.member = member;
+  un.fold_h = H;
+  un.fold_sq = Sq;
+  un.mwords = (U + 31) / 32;
+  // query tokens folded into the head axis: one row of Sq * H heads per request
+  return mla_decode_impl(q, uni, rows, B, 1, Sq * H, U, scale, o, o_dtype, lse, ws, ws_bytes, err_count, stream, un);
+}
+
+static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, const dsa_rows_t* rows, int B, int Sq,
+                                         int H, int k, float scale, void* o, dsa_dtype_t o_dtype, float* lse,
+                                         void* ws, size_t ws_bytes, int32_t* err_count, hipStream_t stream,
+                                         const MlaUnion& un) {
   using namespace dsa;
   DSA_CHECK_ARG(B >= 0 && Sq >= 1 && H >= 1 && k >= 1, "dsa_sparse_mla_decode: bad sizes");
   if (B == 0) return DSA_OK;
@@ -586,6 +645,11 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
   a.o = o;
   a.o_f32 = (o_dtype == DSA_F32);
   a.lse = lse;
+  a.counts = un.counts;
+  a.member = un.member;
+  a.fold_h = un.fold_h;
+  a.fold_sq = un.fold_sq;
+  a.mwords = un.mwords;
   if (splits > 1) {
     a.part_lse = static_cast<float*>(ws);
     a.part_o = a.part_lse + (size_t)B * Sq * splits * H;

@@ -255,3 +255,67 @@ class MtpDraftSteps:
             for l in range(pg.layers):
                 pg.install(stream, topk, po, l)
         return outs
+
+
+class MtpVerifyPoolStep:
+    """One verify step of Sq query tokens (the main token and its drafts) over the device pool
+    of a shared group.  With `union` (the de-duplicated multi-query gather): the union of the
+    query tokens' selections is planned once for the group, and per layer its rows are served
+    once, so a position several tokens select crosses the host link at most once; every token
+    then attends over its own entries of the served union through its union indices.  Without
+    `union`, every (token, entry) is served on its own, as dsa_gather_kv does for [B, Sq, k]
+    selections.  Either way the plan is committed at plan time and the installs follow each
+    layer's attention.
+
+    host : list (one per layer) of Rows over the request-major host rows [B*L, 576]
+    """
+
+    def __init__(self, B, Sq, k, H, n_sets, ways, id_range, host, scale, union=True, device="cuda"):
+        self.B, self.Sq, self.k, self.H, self.S, self.W = B, Sq, k, H, n_sets, ways
+        self.host, self.scale, self.union = host, scale, union
+        self.layers = len(host)
+        dev = device
+        cap = Sq * k
+        self.cap = cap
+        self.pool = [torch.zeros((B, n_sets * ways, 576), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.pids = torch.full((B, n_sets * ways), -1, dtype=torch.int32, device=dev)
+        self.its = torch.full((B, id_range), -1, dtype=torch.int32, device=dev)
+        self.ptr = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+        shape = (B, 1, cap) if union else (B, Sq, k)
+        self.plan_out = dict(is_hit=torch.empty(shape, dtype=torch.uint8, device=dev),
+                             slot=torch.empty(shape, dtype=torch.int32, device=dev),
+                             mp=torch.empty((B, cap), dtype=torch.int32, device=dev),
+                             ms=torch.empty((B, cap), dtype=torch.int32, device=dev),
+                             mc=torch.empty(B, dtype=torch.int32, device=dev))
+        self.uni = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty(B, dtype=torch.int32, device=dev)
+        self.uidx = torch.empty((B, Sq, k), dtype=torch.int32, device=dev)
+        self.sel = [torch.empty((B, cap, 576), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.sel_rows = [dsa.Rows(s, 1152, req_stride=cap) for s in self.sel]
+        self.o = [torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev) for _ in host]
+        self.lse = [torch.empty((B, Sq, H), dtype=torch.float32, device=dev) for _ in host]
+        self.ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H, k)), dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(self, stream, topk, q):
+        """topk [B, Sq, k] int32 (device, rows ascending); q: per layer [B, Sq, H, 576] bf16."""
+        for t in [topk] + list(q):
+            t.record_stream(stream)
+        po = self.plan_out
+        # the served entries: the union (one row) or every (token, entry)
+        served = self.uni if self.union else topk
+        if self.union:
+            dsa.dsa_topk_union(topk, self.uni.view(self.B, self.cap), self.count, self.uidx, err=self.err,
+                               stream=stream)
+        dsa.dsa_plan(served, self.pids, self.its, self.ptr, self.S, self.W, po["is_hit"], po["slot"], po["mp"],
+                     po["ms"], po["mc"], commit=True, err=self.err, stream=stream)
+        for l in range(self.layers):
+            sel4 = self.sel[l].view(served.shape + (576,))
+            dsa.dsa_gather_kv(served, po["is_hit"], po["slot"], self.host[l], self.pool[l], sel4,
+                              dsa.DSA_GATHER_SERVE, err=self.err, stream=stream,
+                              sel_idx=None if self.union else self.uidx)
+            # union: token t's entry j is union row uidx[t, j]; per entry: served row t * k + j
+            dsa.dsa_sparse_mla_decode(q[l], self.uidx, self.sel_rows[l], self.scale, self.o[l], self.lse[l],
+                                      ws=self.ws, err=self.err, stream=stream)
+            dsa.dsa_gather_kv(served, po["is_hit"], po["slot"], None, self.pool[l], sel4,
+                              dsa.DSA_GATHER_INSTALL, err=self.err, stream=stream)

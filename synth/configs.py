@@ -32,6 +32,7 @@ class WorkloadSpec:
     idx_q_kind: str = "bf16"    # "grid_f32" | "bf16" | "e4m3"
     idx_k_kind: str = "e4m3_scaled"  # "grid_f32" | "e4m3_scaled" | "mxfp4"
     w_kind: str = "u01_div64"   # "quarters" | "u01_div64"
+    draft_sigma: float = 0.0    # > 0: query t >= 1 of a request is query 0 + draft_sigma * its own draw
     topk: int = 2048
     # MLA
     mla_heads: int = 128

@@ -31,7 +31,7 @@ import torch
 from .configs import WorkloadSpec, spec as _spec
 
 # tensor ids (part of every seed key)
-T_PAGEPERM, T_IDXQ, T_IDXW, T_IDXK, T_MLAQ, T_KV, T_LENS, T_LOGPAGE, T_TRAJ, T_HOSTKV, T_POOLQ = range(1, 12)
+T_PAGEPERM, T_IDXQ, T_IDXW, T_IDXK, T_MLAQ, T_KV, T_LENS, T_LOGPAGE, T_TRAJ, T_HOSTKV, T_POOLQ, T_DRAFT = range(1, 13)
 
 CHUNK_ROWS = 1 << 14
 E4M3_MAX = 448.0
@@ -158,6 +158,17 @@ def _page_table(cfg: WorkloadSpec, lens: np.ndarray, tid_key=()):
     return pt, total
 
 
+def _draft_correlated(cfg: WorkloadSpec, x: np.ndarray) -> np.ndarray:
+    """Speculative-decoding drafts follow the token before them: with draft_sigma > 0, query
+    t >= 1 of every request is query 0 plus draft_sigma times its own N(0,1) draw (and its
+    head weights are pulled towards query 0's likewise, in _indexer_query)."""
+    if cfg.draft_sigma <= 0 or x.shape[1] < 2:
+        return x
+    y = x.copy()
+    y[:, 1:] = x[:, :1] + np.float32(cfg.draft_sigma) * x[:, 1:]
+    return y
+
+
 def _indexer_query(cfg: WorkloadSpec, B: int):
     """Indexer queries and head weights (identical on every rank of a sharded cache)."""
     H, D = cfg.idx_heads, cfg.idx_dim
@@ -167,11 +178,11 @@ def _indexer_query(cfg: WorkloadSpec, B: int):
         out["idx_q"] = _rng(s, c, T_IDXQ).integers(-4, 5, size=(B, cfg.Sq, H, D)).astype(np.float32)
         out["idx_q_dtype"] = "f32"
     elif cfg.idx_q_kind == "bf16":
-        x = _rng(s, c, T_IDXQ).standard_normal((B, cfg.Sq, H, D), dtype=np.float32)
+        x = _draft_correlated(cfg, _rng(s, c, T_IDXQ).standard_normal((B, cfg.Sq, H, D), dtype=np.float32))
         out["idx_q"] = to_bf16_bits(x)
         out["idx_q_dtype"] = "bf16"
     elif cfg.idx_q_kind == "e4m3":
-        x = _rng(s, c, T_IDXQ).standard_normal((B, cfg.Sq, H, D), dtype=np.float32)
+        x = _draft_correlated(cfg, _rng(s, c, T_IDXQ).standard_normal((B, cfg.Sq, H, D), dtype=np.float32))
         out["idx_q"] = to_e4m3_codes(np.clip(x, -E4M3_MAX, E4M3_MAX))
         out["idx_q_dtype"] = "e4m3"
     else:
@@ -182,6 +193,10 @@ def _indexer_query(cfg: WorkloadSpec, B: int):
     else:
         out["idx_w"] = (_rng(s, c, T_IDXW).random((B, cfg.Sq, H), dtype=np.float32)
                         / np.float32(64.0)).astype(np.float32)
+    if cfg.draft_sigma > 0 and cfg.Sq > 1:
+        # a draft's head weights follow the token before it the same way (and stay >= 0)
+        w = out["idx_w"]
+        w[:, 1:] = np.abs(w[:, :1] + np.float32(cfg.draft_sigma) * (w[:, 1:] - w[:, :1]))
     return out
 
 
@@ -343,6 +358,39 @@ def topk_trajectory(cfg: WorkloadSpec) -> np.ndarray:
             cur = np.sort(np.array(chosen, dtype=np.int64))
             out[s, b] = cur
             prev = cur
+    return out
+
+
+def draft_selections(cfg: WorkloadSpec, first: np.ndarray, Sq: int, keep: float, step: int) -> np.ndarray:
+    """Selections of Sq query tokens for one verify step: token 0 takes `first` [B, k]
+    (ascending); token t keeps round(keep * k) positions of token t - 1's selection uniformly
+    without replacement and adds Zipf(cfg.zipf_a) draws over the context that are not in it,
+    as topk_trajectory does between decode steps.  Returns int32 [B, Sq, k], rows ascending."""
+    L, k = cfg.L, cfg.topk
+    w = np.arange(1, L + 1, dtype=np.float64) ** (-cfg.zipf_a)
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    n_keep = int(round(keep * k))
+    out = np.empty((first.shape[0], Sq, k), dtype=np.int32)
+    for b in range(first.shape[0]):
+        rng = _rng(cfg.seed, cfg.cid, T_DRAFT, step, b)
+        prev = np.asarray(first[b], dtype=np.int64)
+        out[b, 0] = prev
+        for t in range(1, Sq):
+            kept = rng.choice(prev, size=n_keep, replace=False)
+            seen = set(int(x) for x in prev)
+            chosen = [int(x) for x in kept]
+            while len(chosen) < k:
+                for p in _zipf_positions(rng, cdf, L, 4 * (k - len(chosen)) + 16):
+                    p = int(p)
+                    if p in seen:
+                        continue
+                    seen.add(p)
+                    chosen.append(p)
+                    if len(chosen) == k:
+                        break
+            prev = np.sort(np.array(chosen, dtype=np.int64))
+            out[b, t] = prev
     return out
 
 
