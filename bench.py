@@ -265,7 +265,7 @@ def main():
                     help="timed replays of the K-step graph; value and ms_per_step are their median")
     ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
-    ap.add_argument("--entry", choices=["step", "kv_write", "pool_group"], default="step",
+    ap.add_argument("--entry", choices=["step", "kv_write", "pool_group", "mtp_union"], default="step",
                     help="kv_write: time dsa_kv_write alone (the new tokens of a decode step); pool_group: "
                          "time the device-pool workload with serial and auxiliary-stream installs; each "
                          "prints its own line instead of the step's")
@@ -290,6 +290,9 @@ def main():
     if args.entry == "pool_group":
         torch.cuda.set_device(0)
         bench_pool_group(args)
+        return
+    if args.entry == "mtp_union":
+        bench_mtp_union(args)
         return
     cfg = synth.spec(args.config)
     if args.keys == "mxfp4":
@@ -601,11 +604,106 @@ def bench_pool_group(args):
             del pg
         mtp.append({"selection": "reused" if reuse else "served per draft step", "draft_steps": next_n,
                     "ms_per_verify_step": best})
+    # MTP verify over the pool: 4 query tokens whose selections overlap (draft_selections);
+    # the union served once per layer against every entry served on its own
+    from paged_kv_cache_indexer_amd.pipeline import MtpVerifyPoolStep
+    Sq_v = 4
+    drafts = [torch.from_numpy(sgen.draft_selections(cfg, traj[s], Sq_v, 0.65, s)).cuda() for s in range(cfg.steps)]
+    qv = [torch.randn(cfg.B, Sq_v, H, 576, device="cuda").to(torch.bfloat16) for _ in range(cfg.layers)]
+    verify = []
+    for union in (False, True):
+        st = MtpVerifyPoolStep(cfg.B, Sq_v, cfg.topk, H, 1024, 8, cfg.id_range, rows, cfg.scale, union=union)
+        stream = torch.cuda.Stream()
+        host_rows = 0
+        for s in range(cfg.steps):                      # untimed pass: rows over the host link
+            st.run(stream, drafts[s], qv)
+            torch.cuda.synchronize()
+            po = st.plan_out
+            host_rows += (int(po["mc"].sum()) if union else
+                          int(((po["is_hit"] == 0) & (drafts[s] >= 0)).sum()))
+        del st
+        st = MtpVerifyPoolStep(cfg.B, Sq_v, cfg.topk, H, 1024, 8, cfg.id_range, rows, cfg.scale, union=union)
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        e0, e1 = HipMark(), HipMark()
+        e0.record(stream)
+        for s in range(cfg.steps):
+            st.run(stream, drafts[s], qv)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert int(st.err) == 0
+        verify.append({"serve": "union" if union else "per entry", "query_tokens": Sq_v,
+                       "ms_per_step": e0.elapsed_ms(e1) / cfg.steps,
+                       "host_rows_per_step_per_layer": host_rows / cfg.steps})
+        del st
     print(json.dumps({"metric": "pool-group decode ms per step (plan + 4 x (serve, attention, install))",
                       "entry": "pool_group", "data": "synthetic trajectory; zero host rows (timing only)",
                       "batch": cfg.B, "context": cfg.L, "layers": cfg.layers, "topk": cfg.topk,
-                      "host_link": link, "runs": res, "mtp_draft": mtp}),
+                      "host_link": link, "runs": res, "mtp_draft": mtp, "mtp_verify_over_pool": verify}),
           flush=True)
+
+
+def bench_mtp_union(args):
+    """MTP verify at full size (8 requests x 200K context, 4 query tokens with fp8 indexer
+    queries) with draft-correlated queries (draft_sigma 0.3: adjacent tokens share about 65%
+    of their top-2048): the union of each request's four selections (dsa_topk_union), and
+    attention per query token (dsa_sparse_mla_decode) against attention over the union with
+    the query tokens packed into the work-groups (dsa_sparse_mla_decode_union), for 128 heads
+    and for 16 heads (where one work-group holds all four tokens' heads)."""
+    import torch
+    import synth
+    from synth.device import DevWorkload
+    import paged_kv_cache_indexer_amd as dsa
+    from paged_kv_cache_indexer_amd.pipeline import HipMark
+    wl = synth.make_workload(synth.spec(3).scaled(draft_sigma=0.3))
+    torch.cuda.set_device(0)
+    dw = DevWorkload(wl)
+    B, Sq, k = wl.B, wl.Sq, wl.topk
+    idx = dw.topk(dw.scores())
+    U = Sq * k
+    W = (U + 31) // 32
+    uni = torch.empty((B, U), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, dtype=torch.int32, device="cuda")
+    uidx = torch.empty((B, Sq, k), dtype=torch.int32, device="cuda")
+    member = torch.empty((B, Sq, W), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def timed(fn, n=args.steps):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = HipMark(), HipMark()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / n * 1e3
+
+    us_union = timed(lambda: dsa.dsa_topk_union(idx, uni, cnt, uidx, member, stream=stream))
+    counts = cnt.cpu().numpy()
+    res = {"union_us": us_union, "union_rows_mean": float(counts.mean()),
+           "union_over_k": float(counts.mean() / k), "rows_without_union": Sq * k}
+    for H in (128, 16):
+        q = dw.mla_q[:, :, :H].contiguous()
+        o = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
+        ws1 = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, Sq, H, k)), dtype=torch.uint8, device="cuda")
+        ws2 = torch.empty(max(1, dsa.dsa_sparse_mla_union_workspace_size(B, Sq, H, U)), dtype=torch.uint8,
+                          device="cuda")
+        per_query = timed(lambda: dsa.dsa_sparse_mla_decode(q, idx, dw.rows, wl.scale, o, lse, ws=ws1, err=dw.err,
+                                                            stream=stream))
+        packed = timed(lambda: dsa.dsa_sparse_mla_decode_union(q, uni, cnt, member, dw.rows, wl.scale, o, lse, ws=ws2,
+                                                               err=dw.err, stream=stream))
+        res[f"H{H}"] = {"per_query_mla_us": per_query, "union_packed_mla_us": packed,
+                        "row_loads_per_query": B * Sq * k * max(1, H // 64),
+                        "row_loads_packed": int(counts.sum()) * max(1, Sq * H // 64)}
+    assert int(dw.err) == 0
+    print(json.dumps({"metric": "MTP verify: union of the query tokens' selections and attention over it, us per call",
+                      "entry": "mtp_union", "batch": B, "context": int(wl.seq_lens.max()), "query_tokens": Sq,
+                      "topk": k, "data": "synthetic, draft-correlated indexer queries (draft_sigma 0.3)",
+                      "steps": args.steps, **res}), flush=True)
 
 
 if __name__ == "__main__":

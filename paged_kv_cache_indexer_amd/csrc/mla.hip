@@ -165,9 +165,12 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   const int head = hb * 16 * NW + ws * 16 + n;
   const bool head_ok = head < a.H;
 
-  const int e_begin = split * a.per_split;
   const int kq = a.counts ? max(0, min(a.k, a.counts[qr])) : a.k;   // entries of this row
-  const int e_end = min(e_begin + a.per_split, kq);
+  // with a per-row count the row's entries are spread evenly over its splits (never more
+  // per split than the host sized for)
+  const int per = a.counts ? min(a.per_split, (((kq + a.splits - 1) / a.splits) + kTT - 1) / kTT * kTT) : a.per_split;
+  const int e_begin = split * per;
+  const int e_end = min(e_begin + per, kq);
   const int ntiles = e_end > e_begin ? (e_end - e_begin + kTT - 1) / kTT : 0;
   const int32_t* idx = a.idx + (int64_t)qr * a.k;
   // rows that are padding or unresolvable are loaded from this query row instead (finite
