@@ -4,20 +4,27 @@
 // Order: score descending, then position ascending; -0.0 == +0.0.  Scores map to
 // order-preserving uint32 keys.
 //
-// Stage 1 (one work-group per chunk of a row's positions, 8192 or, when the grid would
-// otherwise take more than one round of the chip's work-group slots, 16384): chunk c (len_c
-// positions) keeps its r_c = min(len_c, 2 ceil(k len_c / n)) best keys as candidates, in
-// position order, and records a cut key X_c: every key it left out is <= X_c, and one
-// equal to X_c sits after every kept key equal to it.  The chunks' candidates are written
-// back to back per row, so the row's candidate list is in position order.
-// Stage 2 (one work-group per row): the exact select over the ~2k candidates is the
-// row's answer whenever every chunk that left keys out has X_c below the smallest key
-// the answer may take.  Otherwise the row is selected again from its scores, filtered by
-// a lower bound of the k-th key derived from the X_c (see topk_select_kernel).
+// Stage 1 cuts each row into chunks; chunk c (len_c positions) keeps at most r_c =
+// min(len_c, 2 ceil(k len_c / n) + slack) of its best keys as candidates, in position
+// order, in fixed slots (unused slots hold key 0, which no select takes), and records its
+// candidate count and a cut key X_c: every key it left out is <= X_c, and one equal to X_c
+// sits after every kept key equal to it.  The chunks' slots are laid back to back per row,
+// so the row's candidate list is in position order.  Two forms:
+//   * wave chunks (rows up to 256K positions whose candidate bound fits the exact select's
+//     registers): one wave per 1024 positions, a threshold search whose count lands in a
+//     window just below r_c (see topk_wave_kernel); no barriers, no LDS;
+//   * work-group chunks of 8192 or, when the grid would otherwise take more than one
+//     round of the chip's work-group slots, 16384 positions: an exact select of r_c
+//     (slack 0).
+// Stage 2 (one work-group per row): the exact select over the candidates is the row's
+// answer whenever every chunk that left keys out has X_c below the smallest key the
+// answer may take.  Otherwise the row is selected again from its scores, filtered by a
+// lower bound of the k-th key derived from the X_c and the counts (see
+// topk_select_kernel).
 //
-// Hot paths keep each thread's kPer keys in registers: an MSB-first radix search (digits
-// of up to 11 bits, starting below the bits the smallest and largest key share; two
-// barriers per digit; it stops as soon as the chosen digit's keys are all taken), then
+// The work-group selects keep each thread's keys in registers: an MSB-first radix search
+// (digits of up to 11 bits, starting below the bits the smallest and largest key share;
+// two barriers per digit; it stops as soon as the chosen digit's keys are all taken), then
 // one ordered take from per-wave ballots.  The rare re-select runs the same search over
 // keys staged in LDS.
 #include <algorithm>
@@ -415,10 +422,12 @@ struct TopkArgs {
   int64_t stride;
   const int32_t* seq_lens;
   int Sq, k;
-  int chunk;          // positions per stage-1 chunk: kTopkThreads * (kPer or kLongPer)
+  int chunk;          // positions per stage-1 chunk: kWaveChunk, or kTopkThreads * (kPer or kLongPer)
+  int slack;          // extra candidates kept per chunk beyond twice its share (wave chunks)
   int max_chunks;     // chunk slots per row
   int cand_stride;    // candidate slots per row (>= the sum of the r_c)
   uint32_t* xc;       // [rows, max_chunks] cut key of each chunk
+  int32_t* cc;        // [rows, max_chunks] candidates each chunk kept (at most its r_c slots)
   uint2* cand;        // [rows, cand_stride] (key, position) candidates, position order
   int32_t* idx;
 };
@@ -431,10 +440,10 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
 }
 
 // candidates kept by a chunk of `len` of the row's `n` positions: twice its share
-// ceil(k * len / n) of the k, at most len.  The shares add up to at least k.
-__device__ __forceinline__ int chunk_keep(int k, int len, int n) {
+// ceil(k * len / n) of the k plus `slack`, at most len.  The shares add up to at least k.
+__device__ __forceinline__ int chunk_keep(int k, int len, int n, int slack) {
   const int share = (int)(((int64_t)k * len + n - 1) / n);
-  return min(len, 2 * share);
+  return min(len, 2 * share + slack);
 }
 
 // stage 1, grid (max_chunks, rows), PER keys per thread (a.chunk = kTopkThreads * PER).
@@ -462,8 +471,8 @@ topk_chunk_kernel(TopkArgs a) {
   if (n <= a.k) return;                       // stage 2 writes 0..n-1 directly
   if (lo >= n) return;
   const int len = min(kC, n - lo);
-  const int r = chunk_keep(a.k, len, n);
-  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kC, n);
+  const int r = chunk_keep(a.k, len, n, a.slack);
+  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kC, n, a.slack);
   uint32_t key[PER], kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {                  // empty slots: key 0
@@ -488,7 +497,215 @@ topk_chunk_kernel(TopkArgs a) {
       if (slot < r) out[slot] = make_uint2(key[q], (uint32_t)(lo + q * kTopkThreads + (int)threadIdx.x));
     });
   }
-  if (threadIdx.x == 0) a.xc[(int64_t)row * a.max_chunks + c] = T;
+  if (threadIdx.x == 0) {
+    a.xc[(int64_t)row * a.max_chunks + c] = T;
+    a.cc[(int64_t)row * a.max_chunks + c] = min(r, len);
+  }
+}
+
+// ---- stage 1 on wave chunks (no work-group barriers, no LDS) ----
+//
+// Each wave owns one chunk of kWaveChunk positions, kWavePer keys per lane (position
+// lo + 64 q + lane in slot q, so slot-major lane order is position order).  Instead of an
+// exact select of r_c keys, the wave searches for a threshold T whose count of keys above
+// it lies in a window [lo_c, r_c] just below its slot budget, and keeps exactly those keys
+// (fewer than r_c candidates are fine: the slots left over hold key 0, which no select
+// takes, and stage 2 is exact for any cut key that bounds what was left out).  Each probe
+// of the search is one compare per key and a wave sum.  The first probe is the chunk's
+// mean plus z standard deviations, z the normal upper-tail quantile of the target
+// fraction (Abramowitz and Stegun 26.2.23); later probes are Illinois regula falsi in key
+// space, then bisection, on the bracket [kmin - 1, kmax].  When ties leave no threshold
+// inside the window the bracket closes on adjacent keys (A, B = A + 1): T = B, and the
+// first r_c - count(> B) keys equal to B are taken in position order, as an exact select.
+constexpr int kWaveChunk = 1024;
+constexpr int kWavePer = kWaveChunk / 64;
+constexpr int kWaveSlack = 16;                     // candidates kept beyond twice the share
+constexpr int kWaveMinSlack = 8;                   // below this, the rows take the work-group chunks
+constexpr int kWaveThreads = 256;
+constexpr int64_t kWaveMaxStride = (int64_t)kMaxChunks * kWaveChunk;
+constexpr int kWaveInterp = 6;                     // regula-falsi probes before bisection
+
+// wave sum of a float through DPP lane moves (the scan's last lane holds the total)
+__device__ __forceinline__ float wave_fsum(float x) {
+  const uint32_t t = wave_scan_incl(__float_as_uint(x), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)t, 63));
+}
+
+// number of the wave's keys above m (empty slots hold key 0, below every probe)
+template <int P>
+__device__ __forceinline__ int wave_count_above(const uint32_t (&key)[P], uint32_t m) {
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < P; ++q) c += key[q] > m ? 1 : 0;
+  const int incl = wave_sum_incl(c);
+  return __builtin_amdgcn_readlane(incl, 63);
+}
+
+// upper-tail standard normal quantile: P(Z > z) = p for 0 < p <= 0.5 (Abramowitz and
+// Stegun 26.2.23, absolute error below 4.5e-4)
+__device__ __forceinline__ float normal_upper_quantile(float p) {
+  const float t = __builtin_amdgcn_sqrtf(-2.0f * __logf(p));
+  return t - (2.515517f + t * (0.802853f + t * 0.010328f)) *
+                 __builtin_amdgcn_rcpf(1.0f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
+}
+
+// the order-preserving key of float_key without its branches: -0.0 folds into +0.0, then
+// negative floats are inverted and positive ones get the top bit
+__device__ __forceinline__ uint32_t float_key_fast(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = u == 0x80000000u ? 0u : u;
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// One wave chunk (FULL: all kWaveChunk positions inside the row, no masks).  v: the
+// chunk's scores; returns the candidate count, writes the cut key to T.
+template <bool FULL>
+__device__ __forceinline__ int wave_chunk(const float (&v)[kWavePer], int len, int r, int share, int lo, uint2* out,
+                                          uint32_t& T) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[kWavePer], kmin = 0xffffffffu, kmax = 0u;
+  float xs = 0.0f, xq = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kWavePer; ++q) {
+    const bool in = FULL || q * 64 + lane < len;
+    const uint32_t kq = float_key_fast(v[q]);
+    key[q] = in ? kq : 0u;
+    kmin = min(kmin, in ? kq : 0xffffffffu);
+    kmax = max(kmax, key[q]);
+    const float x = in ? v[q] : 0.0f;
+    xs += x;
+    xq = fmaf(x, x, xq);
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  char* const ob = reinterpret_cast<char*>(out);
+  const uint32_t p0 = (uint32_t)(lo + lane);
+  if (r >= len) {                                 // the whole chunk is kept; X_c = its smallest key
+#pragma unroll
+    for (int q = 0; q < kWavePer; ++q)
+      if (FULL || q * 64 + lane < len)
+        *reinterpret_cast<uint2*>(ob + (uint32_t)(q * 64 + lane) * 8u) = make_uint2(key[q], p0 + q * 64);
+    T = kmin;
+    return len;
+  }
+  const int lo_c = r - max(2, (r - share) / 4);
+  const float tc = 0.5f * (float)(lo_c + r);
+  // first probe: mean + z * deviation of the chunk's scores (one pass; a poor guess only
+  // costs probes)
+  const float inv_len = __builtin_amdgcn_rcpf((float)len);
+  const float mean = wave_fsum(xs) * inv_len;
+  const float sd = __builtin_amdgcn_sqrtf(fmaxf(wave_fsum(xq) * inv_len - mean * mean, 0.0f));
+  const float p_up = tc * inv_len;                // target fraction of the chunk above T
+  const float z = p_up <= 0.5f ? normal_upper_quantile(p_up) : -normal_upper_quantile(1.0f - p_up);
+  const float g = fmaf(z, sd, mean);
+  uint32_t A = kmin - 1u, B = kmax;               // count(> A) = len > r, count(> B) = 0 < lo_c
+  int cB = 0;                                     // exact count above B
+  float fA = (float)len, fB = 0.0f;               // Illinois-damped counts at the bracket ends
+  uint32_t m = (g == g && fabsf(g) <= 3.0e38f) ? float_key_fast(g) : A + (B - A) / 2u;
+  int side = 0, probes = 0;
+  while (B - A > 1u) {                            // the bracket shrinks at every probe
+    m = min(max(m, A + 1u), B - 1u);
+    const int cm = wave_count_above(key, m);
+    ++probes;
+    if (cm > r) {
+      A = m;
+      fA = (float)cm;
+      if (side < 0) fB = 0.5f * (fB + tc);
+      side = -1;
+    } else if (cm < lo_c) {
+      B = m;
+      cB = cm;
+      fB = (float)cm;
+      if (side > 0) fA = 0.5f * (fA + tc);
+      side = 1;
+    } else {                                      // inside the window: keep the keys above m
+      T = m;
+      int base = 0;
+#pragma unroll
+      for (int q = 0; q < kWavePer; ++q) {
+        const uint64_t tm = __builtin_amdgcn_ballot_w64(key[q] > m);
+        const int slot = lanes_below(tm, base);
+        if (key[q] > m) *reinterpret_cast<uint2*>(ob + (uint32_t)slot * 8u) = make_uint2(key[q], p0 + q * 64);
+        base += (int)__builtin_popcountll(tm);
+      }
+      for (int i = cm + lane; i < r; i += 64) *reinterpret_cast<uint2*>(ob + (uint32_t)i * 8u) = make_uint2(0u, 0u);
+      return cm;
+    }
+    if (probes < kWaveInterp && fA > fB) {
+      const float f = fminf(fmaxf((fA - tc) * __builtin_amdgcn_rcpf(fA - fB), 0.0f), 1.0f);
+      m = A + (uint32_t)((float)(B - A) * f);
+    } else {
+      m = A + (B - A) / 2u;
+    }
+  }
+  // adjacent bracket (ties across the window): exact select of r at T = B, the first
+  // `need` keys equal to B in position order
+  T = B;
+  const int need = r - cB;
+  int base = 0, eq_base = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int q = 0; q < kWavePer; ++q) {
+    const bool eq = key[q] == B;                   // never an empty slot: B > 0
+    const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
+    const bool take = key[q] > B || (eq && eq_base + (int)__builtin_popcountll(em & lt) < need);
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+    const int slot = lanes_below(tm, base);
+    if (take && slot < r) *reinterpret_cast<uint2*>(ob + (uint32_t)slot * 8u) = make_uint2(key[q], p0 + q * 64);
+    base += (int)__builtin_popcountll(tm);
+    eq_base += (int)__builtin_popcountll(em);
+  }
+  return r;
+}
+
+// stage 1 on wave chunks, a 1-D grid of rows x G work-groups (G = ceil(max_chunks / 4)):
+// wave w of group g owns chunk 4g + w, its slots [c * r_full, c * r_full + r_c) of the row,
+// its cut key xc and its candidate count cc.  Work-groups are handed to the eight XCDs in
+// turn by their index, and stage 2 runs row r's select on XCD r % 8; when the row count is
+// a multiple of 8, the groups of row r are given indices on that same XCD, so that the
+// select reads its candidates from the XCD's own L2.
+__global__ void __launch_bounds__(kWaveThreads) topk_wave_kernel(TopkArgs a, int groups, int rows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int row, grp;
+  if ((rows & 7) == 0) {
+    const int j = (int)(blockIdx.x >> 3);
+    row = (int)(blockIdx.x & 7) + 8 * (j / groups);
+    grp = j % groups;
+  } else {
+    row = (int)blockIdx.x / groups;
+    grp = (int)blockIdx.x % groups;
+  }
+  const int c = grp * (kWaveThreads / 64) + wave;
+  const int lo = c * kWaveChunk;
+  if (lo >= a.stride) return;                     // whole waves leave; no barrier follows
+  // loads issued before the row's length arrives: a chunk inside the stride reads its 4 KB
+  // from one base address; the stride's last chunk clamps its positions
+  const float* src = a.scores + (int64_t)row * a.stride + lo;
+  float v[kWavePer];
+  if (lo + kWaveChunk <= a.stride) {
+#pragma unroll
+    for (int q = 0; q < kWavePer; ++q) v[q] = src[q * 64 + lane];
+  } else {
+    const int last = (int)a.stride - 1 - lo;
+#pragma unroll
+    for (int q = 0; q < kWavePer; ++q) v[q] = src[min(q * 64 + lane, last)];
+  }
+  const int n = row_len(a, row);
+  if (n <= a.k) return;                           // stage 2 writes 0..n-1 directly
+  if (lo >= n) return;
+  const int len = min(kWaveChunk, n - lo);
+  const int r = chunk_keep(a.k, len, n, a.slack);
+  const int share = (int)(((int64_t)a.k * len + n - 1) / n);
+  uint2* out = a.cand + (int64_t)row * a.cand_stride + (int64_t)c * chunk_keep(a.k, kWaveChunk, n, a.slack);
+  uint32_t T;
+  const int kept = len == kWaveChunk ? wave_chunk<true>(v, len, r, share, lo, out, T)
+                                     : wave_chunk<false>(v, len, r, share, lo, out, T);
+  if (lane == 0) {
+    a.xc[(int64_t)row * a.max_chunks + c] = T;
+    a.cc[(int64_t)row * a.max_chunks + c] = kept;
+  }
 }
 
 // Exact select of the k best of the row's n_cand candidates, PER per thread (candidate j =
@@ -500,11 +717,11 @@ __device__ bool select_candidates(const uint2 (&cv)[kPer], int n_cand, int k, bo
                                   RadixShared& rs, int32_t* out) {
   uint32_t key[PER], pos[PER], kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {                  // empty slots: key 0
+  for (int q = 0; q < PER; ++q) {                  // slots past n_cand and empty slots: key 0
     const bool in = q * kTopkThreads + (int)threadIdx.x < n_cand;
     key[q] = in ? cv[q].x : 0u;
     pos[q] = cv[q].y;
-    kmin = min(kmin, in ? key[q] : 0xffffffffu);
+    kmin = min(kmin, key[q] != 0u ? key[q] : 0xffffffffu);
     kmax = max(kmax, key[q]);
   }
   block_minmax(kmin, kmax, rs);
@@ -550,6 +767,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
 #pragma unroll
   for (int q = 0; q < kPer; ++q) cv[q] = cr[min(q * kTopkThreads + (int)threadIdx.x, a.cand_stride - 1)];
   const uint32_t x_ld = a.xc[(int64_t)row * a.max_chunks + min((int)threadIdx.x, a.max_chunks - 1)];
+  const int c_ld = a.cc[(int64_t)row * a.max_chunks + min((int)threadIdx.x, a.max_chunks - 1)];
   const int n = row_len(a, row);
   int32_t* out = a.idx + (int64_t)row * a.k;
   if (n <= a.k) {
@@ -560,8 +778,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   const int chunk = a.chunk;
   const int nch = (n + chunk - 1) / chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r_full = chunk_keep(a.k, chunk, n);
-  const int n_cand = (nch - 1) * r_full + chunk_keep(a.k, n - (nch - 1) * chunk, n);
+  const int r_full = chunk_keep(a.k, chunk, n, a.slack);
+  const int n_cand = (nch - 1) * r_full + chunk_keep(a.k, n - (nch - 1) * chunk, n, a.slack);
   // thread t < nch: chunk t's cut key, keep, and whether it left keys out
   uint32_t x_t = 0;
   int r_t = 0;
@@ -569,7 +787,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   if ((int)threadIdx.x < nch) {
     const int len_t = min(chunk, n - (int)threadIdx.x * chunk);
     x_t = x_ld;
-    r_t = chunk_keep(a.k, len_t, n);
+    r_t = c_ld;
     cut_t = r_t < len_t;
     xs[threadIdx.x] = x_t;
     rsz[threadIdx.x] = r_t;
@@ -665,21 +883,37 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   }
 }
 
-static void topk_geometry(int64_t stride, int k, int chunk, int& max_chunks, int& cand_stride) {
+static void topk_geometry(int64_t stride, int k, int chunk, int slack, int& max_chunks, int& cand_stride) {
   max_chunks = (int)((stride + chunk - 1) / chunk);
-  // sum over chunks of min(len_c, 2 ceil(k len_c / n)) <= min(n, 2k + 2 * chunks)
-  cand_stride = (int)std::min<int64_t>(stride, 2 * (int64_t)k + 2 * (int64_t)max_chunks);
+  // sum over chunks of min(len_c, 2 ceil(k len_c / n) + slack) <= min(n, 2k + (2 + slack) * chunks)
+  cand_stride = (int)std::min<int64_t>(stride, 2 * (int64_t)k + (2 + (int64_t)slack) * max_chunks);
+}
+
+// Wave chunks serve rows of up to kWaveMaxStride positions whose candidate lists fit the
+// exact select's registers: the slack is the largest one up to kWaveSlack that keeps the
+// candidate bound within kMaxCand.  Returns -1 when it would fall below kWaveMinSlack
+// (longer rows or larger k take the work-group chunks).
+static int topk_wave_slack(int64_t stride, int k) {
+  if (stride > kWaveMaxStride) return -1;
+  if (stride <= kMaxCand) return kWaveSlack;
+  const int64_t nch = (stride + kWaveChunk - 1) / kWaveChunk;
+  const int64_t slack = std::min<int64_t>(kWaveSlack, (kMaxCand - 2 * (int64_t)k) / nch - 2);
+  return slack >= kWaveMinSlack ? (int)slack : -1;
 }
 
 }  // namespace dsa
 
 extern "C" size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride) {
   if (B <= 0 || Sq <= 0 || k <= 0 || score_stride <= 0) return 0;
-  // the 8192-position geometry; the 16384-position one needs no more (half the chunk
-  // slots, no more candidate slots)
+  // the wave-chunk geometry when it serves the rows, else the 8192-position one (the
+  // 16384-position one needs no more: half the chunk slots, no more candidate slots)
   int max_chunks, cand_stride;
-  dsa::topk_geometry(score_stride, k, dsa::kChunk, max_chunks, cand_stride);
-  return (size_t)B * Sq * ((size_t)cand_stride * sizeof(uint2) + (size_t)max_chunks * sizeof(uint32_t));
+  const int slack = dsa::topk_wave_slack(score_stride, k);
+  if (slack >= 0)
+    dsa::topk_geometry(score_stride, k, dsa::kWaveChunk, slack, max_chunks, cand_stride);
+  else
+    dsa::topk_geometry(score_stride, k, dsa::kChunk, 0, max_chunks, cand_stride);
+  return (size_t)B * Sq * ((size_t)cand_stride * sizeof(uint2) + (size_t)max_chunks * 2 * sizeof(uint32_t));
 }
 
 extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int Sq,
@@ -699,10 +933,13 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   a.seq_lens = seq_lens;
   a.Sq = Sq;
   a.k = k;
+  const int wave_slack = topk_wave_slack(score_stride, k);
+  const bool wave_chunks = wave_slack >= 0;
   const int64_t grid8 = (int64_t)B * Sq * ((score_stride + kChunk - 1) / kChunk);
-  const bool long_chunks = grid8 > kChunkRound;
-  a.chunk = long_chunks ? kTopkThreads * kLongPer : kChunk;
-  topk_geometry(score_stride, k, a.chunk, a.max_chunks, a.cand_stride);
+  const bool long_chunks = !wave_chunks && grid8 > kChunkRound;
+  a.chunk = wave_chunks ? kWaveChunk : (long_chunks ? kTopkThreads * kLongPer : kChunk);
+  a.slack = wave_chunks ? wave_slack : 0;
+  topk_geometry(score_stride, k, a.chunk, a.slack, a.max_chunks, a.cand_stride);
   const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
   if (ws == nullptr || ws_bytes < need) {
     set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
@@ -712,6 +949,7 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   const size_t rows = (size_t)B * Sq;
   a.cand = static_cast<uint2*>(ws);
   a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.cand_stride);
+  a.cc = reinterpret_cast<int32_t*>(a.xc + rows * a.max_chunks);
   a.idx = idx;
   static std::atomic<bool> attr_by_dev[kMaxDevices];
   const int slot = current_device_slot();
@@ -725,7 +963,12 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
     }
     if (slot >= 0) attr_by_dev[slot].store(true, std::memory_order_relaxed);
   }
-  if (long_chunks)
+  if (wave_chunks) {
+    const int groups = (a.max_chunks + kWaveThreads / 64 - 1) / (kWaveThreads / 64);
+    DSA_LAUNCH(topk_wave_kernel, dim3((unsigned)(groups * B * Sq)), dim3(kWaveThreads), 0, stream, a, groups,
+               B * Sq);
+  }
+  else if (long_chunks)
     DSA_LAUNCH(topk_chunk_kernel<kLongPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
   else
     DSA_LAUNCH(topk_chunk_kernel<kPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);

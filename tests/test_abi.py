@@ -42,7 +42,14 @@ def test_invalid_arguments_rejected_without_device():
                       None) == _lib.DSA_ERR_UNSUPPORTED
     assert L.dsa_topk(ctypes.c_void_p(16), 100000, ctypes.c_void_p(16), 2, 1, 2048, ctypes.c_void_p(16), None, 0,
                       None) == _lib.DSA_ERR_WORKSPACE
-    assert L.dsa_topk_workspace_size(32, 1, 2048, 65536) == 32 * (4112 * 8 + 8 * 4)
+    # wave chunks of 1024 positions: 64 chunks, candidate bound 2k + 18 * 64 = 5248 slots of
+    # (key, position), a cut key and a count per chunk
+    assert L.dsa_topk_workspace_size(32, 1, 2048, 65536) == 32 * (5248 * 8 + 64 * 8)
+    # 300000 positions exceed the wave chunks' 262144: work-group chunks of 8192, 37 of them,
+    # bound 2k + 2 * 37 = 4170
+    assert L.dsa_topk_workspace_size(2, 1, 2048, 300000) == 2 * (4170 * 8 + 37 * 8)
+    # 250048 positions: the slack drops to (8192 - 4096) / 245 - 2 = 14, bound 4096 + 16 * 245 = 8016
+    assert L.dsa_topk_workspace_size(66, 1, 2048, 250048) == 66 * (8016 * 8 + 245 * 8)
     assert L.dsa_page_translate(None, 10, 0, 4, None, None, None, None) == _lib.DSA_ERR_INVALID_ARG
     assert L.dsa_plan(None, 1, 1, 8, None, None, None, 4, 2, 10, None, None, None, None, None, 1, None,
                       None) == _lib.DSA_ERR_INVALID_ARG

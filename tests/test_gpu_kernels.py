@@ -293,6 +293,33 @@ def test_topk_batched_mtp_rows():
             assert np.array_equal(got[b, t], o_topk.select(s[b, t, :n], k)), (b, t)
 
 
+def test_topk_wave_chunks_mixed_rows():
+    """Rows on the wave-chunk path at a stride that lowers its slack (250048 positions, as a
+    4-way page-sharded share of a 1M context): mixed lengths, a hot window whose 700
+    consecutive best scores overflow one chunk's slots (the re-select), a row whose chunks
+    are each constant (every search ends on an adjacent bracket), integer ties, and
+    close values."""
+    rng = np.random.default_rng(31)
+    stride, k = 250048, 2048
+    lens = np.array([250048, 200000, 65536, 40000, 9000, 2049, 2048, 100, 250048, 131072, 70001, 33000,
+                     150000, 250048, 8193, 250047], dtype=np.int32)
+    B = len(lens)
+    s = np.zeros((B, 1, stride), dtype=np.float32)
+    for b in range(B):
+        n = lens[b]
+        s[b, 0, :n] = rng.standard_normal(n)
+    s[2, 0, 30000:30700] = 10.0 + rng.random(700).astype(np.float32)      # hot window inside one chunk
+    s[3, 0, :40000] = np.repeat(rng.standard_normal(40), 1000)[:40000]     # constant within each 1000
+    s[9, 0, :131072] = rng.integers(-50, 50, 131072)                        # integer ties
+    s[10, 0, :70001] = rng.standard_normal(70001) * 1e-3 + 5.0              # close values
+    s[12, 0, :150000] = np.abs(rng.standard_normal(150000)) * np.float32(1e30)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b, 0], o_topk.select(s[b, 0, :lens[b]], k)), b
+
+
 # ------------------------------------------------------------------ sparse MLA
 @pytest.mark.parametrize("H,k,L", [(128, 2048, 3000), (16, 256, 4096), (64, 300, 700), (128, 100, 100),
                                    (32, 512, 2000), (48, 300, 1000),
