@@ -359,8 +359,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m, int acc) {
 // give each kept key its rank.  EMIT(slot, q) for each kept key.  Two barriers.
 template <int PER, typename EmitFn>
 __device__ void take_reg(const uint32_t (&key)[PER], uint32_t T, int need, RadixShared& sh, EmitFn EMIT) {
-  static_assert(PER * kTopkWaves % 64 == 0, "whole lanes of counts");
   static_assert(PER <= 64, "lane q publishes slot q's counts");
+  constexpr int NC = PER * kTopkWaves;             // (slot, wave) counts
+  static_assert(NC <= kLongPer * kTopkWaves, "counts fit sh.cnt");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t gtm[PER], eqm[PER];
   int mine = 0;                                    // lane q: packed (eq, gt) counts of slot q
@@ -374,17 +375,17 @@ __device__ void take_reg(const uint32_t (&key)[PER], uint32_t T, int need, Radix
   if (lane < PER) sh.cnt[lane * kTopkWaves + wave] = mine;
   __syncthreads();
   if (wave == 0) {                                 // exclusive scan of the packed counts
-    constexpr int E = PER * kTopkWaves / 64;
+    constexpr int E = (NC + 63) / 64;
     int c[E], sum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c[e] = sh.cnt[lane * E + e];
+      c[e] = lane * E + e < NC ? sh.cnt[lane * E + e] : 0;
       sum += c[e];
     }
     int run = wave_sum_incl(sum) - sum;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      sh.cnt[lane * E + e] = run;
+      if (lane * E + e < NC) sh.cnt[lane * E + e] = run;
       run += c[e];
     }
   }
@@ -796,8 +797,15 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   uint32_t* fpos = fl + kFiltLds;
   uint32_t T;
   int need;
-  if (n_cand <= kTopkThreads * 4) {
+  // the register select sized to the candidate count (its work scales with the slots)
+  if (n_cand <= kTopkThreads * 2) {
+    if (select_candidates<2>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
+  } else if (n_cand <= kTopkThreads * 4) {
     if (select_candidates<4>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
+  } else if (n_cand <= kTopkThreads * 5) {
+    if (select_candidates<5>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
+  } else if (n_cand <= kTopkThreads * 6) {
+    if (select_candidates<6>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
   } else if (n_cand <= kMaxCand) {
     if (select_candidates<kPer>(cv, n_cand, a.k, cut_t, x_t, rs, out)) return;
   }
