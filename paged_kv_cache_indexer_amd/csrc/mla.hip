@@ -1,11 +1,14 @@
 // Sparse MLA decode over the selected rows (TokenSpeed audit page, "MLA
 // (tokenspeed-mla)": one 576-wide latent row per token is both key (all 576 values)
 // and value (the first 512); "Shared-Indexer KV Cache Offload for GLM-5.2", §2.1:
-// attention reads only the top-k positions).  Split-KV decode with fp32 partial
-// (o, lse) and an LSE-rescaling merge (TokenSpeed audit, two-stage split-KV decode).
+// attention reads only the top-k positions).  Split-KV decode: each split writes its
+// normalised partial o (in o's dtype) and its lse, and an LSE-rescaling merge combines
+// them (TokenSpeed audit, two-stage split-KV decode).
 //
-// Work-group = NW waves (one per SIMD) for 16*NW heads of one query row and one split of
-// its selected rows.  Each wave owns 16 heads over the whole latent row:
+// Work-group = two token streams of NW waves (one per SIMD per stream) for 16*NW heads of
+// one query row and one split of its selected rows; stream s takes tiles T with
+// T % 2 == s, and the streams' softmax states are merged through LDS at the end.  Each
+// wave owns 16 heads over the whole latent row:
 //   S^T[32 tokens x 16 heads] = K_tile . q^T       (bf16 MFMA 16x16x32: two 16-token
 //     M tiles x 18 steps of 32 latent dims, q^T resident in VGPRs)
 //   O^T[512 dims x 16 heads] += V^T . P^T           (bf16 MFMA 16x16x32: 32 M tiles of 16
@@ -17,11 +20,11 @@
 // is read straight from the token-major K tile with LDS transpose reads
 // (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of the
 // 8-byte rows addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so no transposed copy is made.
-// Selected rows stream into a ring of three LDS tiles with LDS-direct loads
-// (global_load_lds_dwordx4: lane i of a wave instruction lands at M0 + 16 i), two tiles
-// ahead of the one being computed; no VGPRs hold rows in flight.  A tile is stored as
-// 1 KB blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one
-// wave instruction fetches eight whole 128-byte lines; the placement inside a block
+// Selected rows stream into a ring of four LDS tiles (each stream loads one tile ahead of
+// the one it computes) with LDS-direct loads (global_load_lds_dwordx4: lane i of a wave
+// instruction lands at M0 + 16 i); no VGPRs hold rows in flight.  A tile is stored as 1 KB
+// blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one wave
+// instruction fetches eight whole 128-byte lines; the placement inside a block
 // (chunk_byte) keeps both operand reads free of LDS bank conflicts.
 // Online softmax in base 2 with a lazy rescale (the running max is only moved when it
 // grows by more than 2^8), which leaves o and lse mathematically unchanged.
