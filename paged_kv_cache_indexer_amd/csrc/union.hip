@@ -1,6 +1,7 @@
 // De-duplicated union of the query tokens' selections ("Shared-Indexer KV Cache Offload for
-// GLM-5.2": §4.2, the planner works on the de-duplicated union of a step's top-k positions;
-// §5.1, the draft tokens of speculative decoding select overlapping positions).
+// GLM-5.2": §4.2, the plan classifies a step's top-k ids once and de-duplicates repeated
+// misses; §5.1, MTP draft steps reuse the first decode step's selection, so the positions
+// a request's draft tokens select largely coincide).
 //
 // One work-group per request.  The Sq selection rows (ascending, -1 padding at the end, as
 // dsa_topk writes them) are staged in LDS.  An entry x of row t owns its value when no
