@@ -34,10 +34,12 @@ KEY_BYTES = {"e4m3": lambda D: D + 4,          # e4m3 codes + float32 per-token 
              "f32": lambda D: 4 * D}       # float32 keys, no scale
 
 
-def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2, o_bytes=2):
+def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2, o_bytes=2, topk_fused=False):
     """Bytes / flops each kernel must move or compute for one layer-step (no re-reads); Sq
     query tokens per request, each scoring the whole cache and attending its own top-k.
-    L is one cache length for every request or a list of per-request lengths."""
+    L is one cache length for every request or a list of per-request lengths.  With
+    topk_fused, the top-k's chunk stage runs in the scan's epilogue on scores it still holds,
+    so the top-k stage itself only writes the indices."""
     lens = [int(L)] * B if isinstance(L, (int, np.integer)) else [int(x) for x in L]
     Q = B * Sq
     tokens = sum(lens)
@@ -48,7 +50,7 @@ def algorithmic_work(B, L, H_idx, D, k, H_mla, ps, keys="e4m3", Sq=1, q_bytes=2,
                  + sum(-(-l // ps) for l in lens) * 4  # page table (a partial last page counts)
                  + Sq * tokens * 4)   # scores out
     idx_flops = 2 * Sq * H_idx * D * tokens
-    topk_bytes = Sq * tokens * 4 + Q * k * 4
+    topk_bytes = Q * k * 4 if topk_fused else Sq * tokens * 4 + Q * k * 4
     mla_bytes = (sel * 1152           # selected latent rows
                  + Q * H_mla * 576 * 2  # q
                  + Q * k * 4          # indices
@@ -176,9 +178,13 @@ def measure_peaks(torch):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_b32_ctx65536.json")
 # entry point -> (kernel name prefixes in rocprofv3 output, sources the kernels are built from)
 ENTRY_KERNELS = {
-    "indexer": (["void dsa::indexer_mfma_kernel<false, false, 2, 1, 1>"], ["indexer.hip"]),
-    "indexer_mxfp4": (["void dsa::indexer_mfma_kernel<false, true, 2, 1, 1>"], ["indexer.hip"]),
-    "topk": (["void dsa::topk_chunk_kernel<", "dsa::topk_select_kernel"], ["topk.hip"]),
+    "indexer": (["void dsa::indexer_mfma_kernel<false, false, 2, 1, 1, false>"], ["indexer.hip", "topk_wave.h"]),
+    "indexer_fused": (["void dsa::indexer_mfma_kernel<false, false, 2, 1, 1, true>"], ["indexer.hip", "topk_wave.h"]),
+    "indexer_mxfp4": (["void dsa::indexer_mfma_kernel<false, true, 2, 1, 1, false>"], ["indexer.hip", "topk_wave.h"]),
+    "indexer_mxfp4_fused": (["void dsa::indexer_mfma_kernel<false, true, 2, 1, 1, true>"],
+                            ["indexer.hip", "topk_wave.h"]),
+    "topk": (["dsa::topk_wave_kernel", "dsa::topk_select_kernel"], ["topk.hip", "topk_wave.h"]),
+    "topk_select": (["dsa::topk_select_kernel"], ["topk.hip", "topk_wave.h"]),
     "mla": (["void dsa::mla_decode_kernel<", "void dsa::mla_merge_kernel<"], ["mla.hip"]),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0   # counter KiB -> bytes/1024, from a 256 MiB device copy
@@ -263,6 +269,9 @@ def main():
                          "requests, float32 partial o); configs other than 2 print their own line")
     ap.add_argument("--replays", type=int, default=5,
                     help="timed replays of the K-step graph; value and ms_per_step are their median")
+    ap.add_argument("--topk-form", choices=["fused", "separate"], default="fused",
+                    help="fused: one query token per request runs the top-k's chunk stage in the scan's epilogue "
+                         "(dsa_indexer_topk_chunks + dsa_topk_select_chunks); separate: dsa_indexer_scores + dsa_topk")
     ap.add_argument("--keys", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer key cache of the step: e4m3 + float32 scale, or MXFP4 (the FP4 indexer cache)")
     ap.add_argument("--entry", choices=["step", "kv_write", "pool_group", "mtp_union"], default="step",
@@ -307,7 +316,8 @@ def main():
     dw = DevWorkload(wl)
     B, Sq, L, k = wl.B, wl.Sq, int(wl.seq_lens.max()), wl.topk
     H_mla = wl.mla_q.shape[2]
-    step = dw.decode_step(args.layers, o_dtype=torch.float32 if o_kind == "f32" else torch.bfloat16)
+    step = dw.decode_step(args.layers, o_dtype=torch.float32 if o_kind == "f32" else torch.bfloat16,
+                          fused=args.topk_form == "fused")
     names = ["indexer", "topk", "mla"]
     stream = torch.cuda.Stream()            # non-default stream: the step is captured and replayed
 
@@ -357,15 +367,29 @@ def main():
     # per-stage duration: each stage launched K times back to back (layers rotating) between two
     # HIP events on the launch stream; the launches queue faster than they run, so the span
     # holds no launch gaps
-    per = {}
-    for n in names:
-        m0, m1 = HipMark(), HipMark()
-        m0.record(stream)
-        for i in range(args.steps):
-            step.stage(n, stream, layer=i)
-        m1.record(stream)
+    def stage_times(st):
+        out = {}
+        for n in names:
+            m0, m1 = HipMark(), HipMark()
+            m0.record(stream)
+            for i in range(args.steps):
+                st.stage(n, stream, layer=i)
+            m1.record(stream)
+            torch.cuda.synchronize()
+            out[n] = m0.elapsed_ms(m1) * 1e-3 / args.steps             # seconds per launch
+        return out
+
+    per = stage_times(step)
+    # with the fused scan, the separate entry points are timed as well (same inputs and caches),
+    # so the scan's and the top-k's own rooflines stay visible
+    per_sep = None
+    if step.fused:
+        sep = step.with_form(False)
+        with torch.cuda.stream(stream):
+            for i in range(2):
+                sep.run(stream, layer=i)
         torch.cuda.synchronize()
-        per[n] = m0.elapsed_ms(m1) * 1e-3 / args.steps             # seconds per launch
+        per_sep = stage_times(sep)
     assert int(dw.err) == 0, "device-side index errors during the benchmark"
     meas, meas_err = None, None
     if not args.no_peaks:
@@ -378,26 +402,37 @@ def main():
     fp8_q = wl.idx_q_dtype == "e4m3"                 # the indexer then runs on the fp8 MFMA
     q_bytes = {"e4m3": 1, "bf16": 2, "f32": 4}[wl.idx_q_dtype]
     work = algorithmic_work(B, wl.seq_lens, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, keys,
-                            Sq=Sq, q_bytes=q_bytes, o_bytes=4 if o_kind == "f32" else 2)
+                            Sq=Sq, q_bytes=q_bytes, o_bytes=4 if o_kind == "f32" else 2, topk_fused=bool(step.fused))
     peak = {"indexer": FP8_PEAK_TFLOPS if fp8_q else BF16_PEAK_TFLOPS, "topk": BF16_PEAK_TFLOPS,
             "mla": BF16_PEAK_TFLOPS}
-    kernels = {}
-    for n in names:
-        by, fl = work[n]
-        kernels[n] = {"avg_us": per[n] * 1e6, "algo_bytes": by, "algo_flops": fl,
-                      "GBps": by / per[n] / 1e9, "hbm_frac": by / per[n] / 1e9 / HBM_PEAK_GBS,
-                      "TFLOPs": fl / per[n] / 1e12, "mfma_dtype": "fp8" if (n == "indexer" and fp8_q) else "bf16",
-                      "mfma_frac": fl / per[n] / 1e12 / peak[n]}
+    def kernel_lines(pr, wk):
+        out = {}
+        for n in names:
+            by, fl = wk[n]
+            out[n] = {"avg_us": pr[n] * 1e6, "algo_bytes": by, "algo_flops": fl,
+                      "GBps": by / pr[n] / 1e9, "hbm_frac": by / pr[n] / 1e9 / HBM_PEAK_GBS,
+                      "TFLOPs": fl / pr[n] / 1e12, "mfma_dtype": "fp8" if (n == "indexer" and fp8_q) else "bf16",
+                      "mfma_frac": fl / pr[n] / 1e12 / peak[n]}
+        return out
+
+    kernels = kernel_lines(per, work)
+    separate = None
+    if per_sep is not None:
+        work_sep = algorithmic_work(B, wl.seq_lens, wl.spec.idx_heads, wl.spec.idx_dim, k, H_mla, wl.page_size, keys,
+                                    Sq=Sq, q_bytes=q_bytes, o_bytes=4 if o_kind == "f32" else 2)
+        separate = {n: v for n, v in kernel_lines(per_sep, work_sep).items() if n != "mla"}
     # step roofline: sum over the kernels of their time at peak (bytes at 8 TB/s or flops at
     # the MFMA peak of their dtype, whichever is longer) over the measured step time
     t_star = sum(max(work[n][0] / (HBM_PEAK_GBS * 1e9), work[n][1] / (peak[n] * 1e12)) for n in names)
     dom = max(names, key=lambda n: per[n])
     by = work[dom][0]
+    entry = {"indexer": "indexer" + ("_mxfp4" if keys == "mxfp4" else "") + ("_fused" if step.fused else ""),
+             "topk": "topk_select" if step.fused else "topk", "mla": "mla"}[dom]
     roofline = {"bound": "hbm", "achieved": by / per[dom] / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by / per[dom] / 1e9 / HBM_PEAK_GBS,
-                "traffic": (measured_traffic(dom + ("_mxfp4" if dom == "indexer" and keys == "mxfp4" else ""))
-                            if args.config == 2 else None),
-                "kernel": dom}
+                "traffic": measured_traffic(entry) if args.config == 2 else None,
+                "kernel": dom + (" (with the top-k chunk stage in its epilogue)" if dom == "indexer" and step.fused
+                                 else "")}
 
     ms = wall / args.steps * 1e3
     out = {
@@ -421,6 +456,8 @@ def main():
         "launch": mode,
         "replays_ms_per_step": [w / args.steps * 1e3 for w in walls],
         "kernel_timing": "per stage: HIP events on the launch stream around K back-to-back launches of that stage",
+        "topk_form": ("chunk stage in the scan's epilogue (dsa_indexer_topk_chunks + dsa_topk_select_chunks)"
+                      if step.fused else "separate scan and top-k (dsa_indexer_scores + dsa_topk)"),
         "config": {"workload": workload, "batch": B, "context": L, "query_tokens": Sq,
                    "cached_tokens": int(np.sum(wl.seq_lens, dtype=np.int64)),
                    "page_size": wl.page_size, "indexer_heads": wl.spec.idx_heads, "indexer_dim": wl.spec.idx_dim,
@@ -433,6 +470,7 @@ def main():
         "measured_peaks": (({"error": meas_err} if meas_err else None) if meas is None else
                            {**meas, "dominant_kernel_frac_of_read_peak": by / per[dom] / 1e9 / meas["hbm_read_GBps"]}),
         "kernels": kernels,
+        "kernels_separate_form": separate,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -156,15 +156,46 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float*
  *   idx      [B, Sq, k] int32 output
  *   ws       workspace of at least dsa_topk_workspace_size(B, Sq, k, score_stride) bytes,
  *            8-byte aligned, contents on entry ignored: per row, the best keys of each
- *            8192-position chunk as candidates plus each chunk's cut key, for a
- *            two-stage select (chunk c keeps twice its share ceil(k*len_c/n) of the k;
- *            the exact select over the candidates is checked against the cut keys and
- *            redone over the row's scores when a chunk could hold more)
+ *            chunk of positions as candidates (1024-position chunks for rows of up to
+ *            262144 positions whose candidates fit, else 8192 or 16384) plus each chunk's
+ *            cut key and candidate count, for a two-stage select (chunk c keeps at most
+ *            twice its share ceil(k*len_c/n) of the k plus a slack; the exact select over
+ *            the candidates is checked against the cut keys and redone over the row's
+ *            scores when a chunk could hold more)
  * Supported: 1 <= k <= 8192, B*Sq <= 65535, score_stride <= 2^21.
  */
 size_t dsa_topk_workspace_size(int B, int Sq, int k, int64_t score_stride);
 dsa_status_t dsa_topk(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B,
                       int Sq, int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_indexer_topk_chunks + dsa_topk_select_chunks — the same two results as
+ * dsa_indexer_scores followed by dsa_topk, for one query token per request (Sq = 1), with
+ * the top-k's chunk stage run inside the scan ([GLM52] §2.1: the indexer scores feed the
+ * top-2048 directly).  Each wave of the scan owns a 1024-position unit of one request;
+ * after writing the unit's scores it keeps the unit's candidates for the top-k in `ws`,
+ * as dsa_topk's wave-chunk stage does.  dsa_topk_select_chunks then runs the exact select
+ * over those candidates (re-selecting a row from `scores` when its candidates could miss
+ * part of the answer).  scores and idx are bit-identical to the two separate calls.
+ *
+ *   dsa_indexer_topk_chunks: the arguments of dsa_indexer_scores with Sq = 1 on the MFMA
+ *            path (q BF16 or E4M3, keys E4M3 or MXFP4, H in {32, 64, 128}), plus k and the
+ *            top-k workspace ws / ws_bytes (dsa_topk_workspace_size(B, 1, k, score_stride)
+ *            bytes, 8-byte aligned, contents on entry ignored).  `ready` and err_count as
+ *            for dsa_indexer_scores.
+ *   dsa_topk_select_chunks: the arguments of dsa_topk with Sq = 1; ws must hold what
+ *            dsa_indexer_topk_chunks wrote for the same scores, seq_lens, k and
+ *            score_stride, on the same stream or after it.
+ * Supported: 1 <= k <= 8192, score_stride <= 262144 with candidate lists that fit the
+ * select (dsa_topk's wave-chunk form; otherwise DSA_ERR_UNSUPPORTED with nothing
+ * enqueued, and the caller takes the two separate calls).
+ */
+dsa_status_t dsa_indexer_topk_chunks(const void* q, dsa_dtype_t q_dtype, const float* w, const dsa_rows_t* keys,
+                                     dsa_dtype_t k_dtype, const void* k_scale, const int32_t* seq_lens, int B, int H,
+                                     int D, int64_t score_stride, float* scores, int k, void* ws, size_t ws_bytes,
+                                     int32_t* err_count, hipEvent_t ready, hipStream_t stream);
+dsa_status_t dsa_topk_select_chunks(const float* scores, int64_t score_stride, const int32_t* seq_lens, int B, int k,
+                                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * dsa_topk_union — the de-duplicated union of each request's Sq selections ([GLM52] §4.2: the

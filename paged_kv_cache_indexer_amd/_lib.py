@@ -13,6 +13,7 @@ STATUS_NAMES = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED
                 -4: "DSA_ERR_WORKSPACE"}
 
 EXPORTED = ["dsa_version", "dsa_last_error", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+            "dsa_indexer_topk_chunks", "dsa_topk_select_chunks",
             "dsa_topk_union", "dsa_sparse_mla_union_workspace_size", "dsa_sparse_mla_decode_union",
             "dsa_plan", "dsa_gather_kv", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_noalloc_max_workspace", "dsa_sparse_mla_decode_noalloc", "dsa_merge_partials",
@@ -53,6 +54,10 @@ def load() -> ctypes.CDLL:
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
         "dsa_topk_workspace_size": (sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64]),
         "dsa_topk": (ctypes.c_int, [vp, i64, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]),
+        "dsa_indexer_topk_chunks": (ctypes.c_int, [vp, ctypes.c_int, vp, prow, ctypes.c_int, vp, vp, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, i64, vp, ctypes.c_int, vp, sz, vp, vp,
+                                                   vp]),
+        "dsa_topk_select_chunks": (ctypes.c_int, [vp, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]),
         "dsa_plan": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp]),
         "dsa_gather_kv": (ctypes.c_int, [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, prow, vp, i64,

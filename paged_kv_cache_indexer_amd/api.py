@@ -103,6 +103,34 @@ def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor, ws
                                 ws_bytes, _stream(stream)), "dsa_topk")
 
 
+def dsa_indexer_topk_chunks(q: torch.Tensor, w: torch.Tensor, keys: Rows, k_scale: Optional[torch.Tensor],
+                            seq_lens: torch.Tensor, scores: torch.Tensor, k: int, ws: torch.Tensor,
+                            k_dtype: int = DSA_E4M3, err: Optional[torch.Tensor] = None,
+                            ready: Optional[torch.cuda.Event] = None, stream=None, q_dtype: Optional[int] = None):
+    """The indexer scan (one query token per request) with the top-k chunk stage in its epilogue:
+    writes scores and the chunks' candidates into ws (dsa_topk_workspace_size(B, 1, k, stride) bytes)."""
+    B, Sq, H, D = q.shape
+    if Sq != 1:
+        raise ValueError("dsa_indexer_topk_chunks takes one query token per request")
+    qd = _dtype_code(q) if q_dtype is None else q_dtype
+    ev = ctypes.c_void_p(ready.cuda_event) if ready is not None else None
+    _check(_lib.load().dsa_indexer_topk_chunks(_ptr(q), qd, _ptr(w), keys.ref(), k_dtype, _ptr(k_scale),
+                                               _ptr(seq_lens), B, H, D, scores.shape[-1], _ptr(scores), k, _ptr(ws),
+                                               ws.numel() * ws.element_size(), _ptr(err), ev, _stream(stream)),
+           "dsa_indexer_topk_chunks")
+
+
+def dsa_topk_select_chunks(scores: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor, ws: torch.Tensor,
+                           stream=None):
+    """The exact select over the candidates dsa_indexer_topk_chunks left in ws; idx [B, 1, k]."""
+    B, Sq, k = idx.shape
+    if Sq != 1:
+        raise ValueError("dsa_topk_select_chunks takes one query token per request")
+    _check(_lib.load().dsa_topk_select_chunks(_ptr(scores), scores.shape[-1], _ptr(seq_lens), B, k, _ptr(idx),
+                                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "dsa_topk_select_chunks")
+
+
 def dsa_topk_union(topk: torch.Tensor, uni: torch.Tensor, count: torch.Tensor, uidx: Optional[torch.Tensor] = None,
                    member: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None):
     """topk [B, Sq, k] -> uni [B, Sq*k], count [B], uidx [B, Sq, k], member [B, Sq, ceil(Sq*k/32)] (int32 views)."""

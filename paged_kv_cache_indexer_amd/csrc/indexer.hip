@@ -27,7 +27,7 @@
 // inside one 32-element block.
 #include <type_traits>
 
-#include "common.h"
+#include "topk_wave.h"
 
 namespace dsa {
 
@@ -91,6 +91,9 @@ struct MfmaArgs {
   int64_t score_stride;
   float* scores;
   int32_t* err;
+  // fused top-k chunk stage (FUSE): one query row per request, 1024-position units, each
+  // unit's candidates, cut key and count written into the top-k workspace described here
+  TopkArgs tk;
 };
 
 // HMT: 32-row M tiles per query (H / 32); NQ: queries per wave; RG: waves that share one
@@ -123,7 +126,7 @@ __device__ __forceinline__ int unit_tiles(int total, int wave_slots, int max_uni
 // request b's length clamped to [0, stride] (a longer one is counted once, by work-group 0);
 // returns ut
 __device__ int indexer_units(const int32_t* seq_lens, int B, int64_t stride, int wave_slots, int max_unit,
-                              int* unit_off, int* len_sh, int* wsum, int32_t* err) {
+                              int fixed_ut, int* unit_off, int* len_sh, int* wsum, int32_t* err) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tiles[kPrefixPerThread];
   int mine = 0;
@@ -162,7 +165,7 @@ __device__ int indexer_units(const int32_t* seq_lens, int B, int64_t stride, int
   };
   int total_tiles = 0;
   block_scan(mine, total_tiles);
-  const int ut = unit_tiles(total_tiles, wave_slots, max_unit);
+  const int ut = fixed_ut > 0 ? fixed_ut : unit_tiles(total_tiles, wave_slots, max_unit);
   int units[kPrefixPerThread];
   int my_units = 0;
 #pragma unroll
@@ -207,8 +210,40 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-template <bool QFP8, bool KFP4, int HMT, int NQ, int RG>
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// Top-k wave chunk t_begin / 32 of row b (positions [lo, lo + len) of its n), from the unit's
+// scores staged in LDS.  Not inlined: inside the scan its address arithmetic was hoisted
+// across the unit loop and spilled under the loop's register pressure.
+__device__ __attribute__((noinline)) void fused_chunk_select(lds_f32* sb, int b, int t_begin, int n, uint2* cand,
+                                                             uint32_t* xc, int32_t* cc, int cand_stride,
+                                                             int max_chunks, int k, int slack) {
+  const int lane = threadIdx.x & 63;
+  const int c = t_begin / (kWaveChunk / kTile);
+  const int lo = t_begin * kTile;
+  const int len = min(kWaveChunk, n - lo);
+  const int r = chunk_keep(k, len, n, slack);
+  const int share = (int)(((int64_t)k * len + n - 1) / n);
+  uint2* out = cand + (int64_t)b * cand_stride + (int64_t)c * chunk_keep(k, kWaveChunk, n, slack);
+  float v[kWavePer];
+#pragma unroll
+  for (int q = 0; q < kWavePer; ++q) v[q] = sb[q * 64 + lane];   // positions past len are masked
+  uint32_t T;
+  const int kept = len == kWaveChunk ? wave_chunk<true>(v, len, r, share, lo, out, T)
+                                     : wave_chunk<false>(v, len, r, share, lo, out, T);
+  if (lane == 0) {
+    xc[(int64_t)b * max_chunks + c] = T;
+    cc[(int64_t)b * max_chunks + c] = kept;
+  }
+}
+
+// FUSE (one query row per request, one query per wave): units are exactly kWaveChunk / 32
+// tiles, so unit u of a request is top-k wave chunk u of its row; after writing the unit's
+// scores the wave runs the chunk's threshold search on the scores still staged in its LDS
+// buffer (topk_wave.h) and writes the chunk's candidates, cut key and count.
+template <bool QFP8, bool KFP4, int HMT, int NQ, int RG, bool FUSE>
 __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
+  static_assert(!FUSE || (NQ == 1 && RG == 1), "the fused top-k stage takes one query per wave");
   constexpr int MT_W = HMT * NQ;
   constexpr int WPU = 4 / RG;                      // units processed side by side per work-group
   constexpr int KSTEPS = QFP8 ? 2 : 8;
@@ -239,8 +274,10 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
   const int tpp_shift = (tpp > 0 && (tpp & (tpp - 1)) == 0) ? __builtin_ctz(tpp) : -1;
 
   __shared__ int scan_wsum[4];
+  static_assert(!FUSE || (kWaveChunk % kTile == 0 && kWaveChunk / kTile <= kMaxUnit / NQ), "a fused unit fits the score buffer");
   const int ut = __builtin_amdgcn_readfirstlane(indexer_units(a.seq_lens, a.B, a.score_stride, gridDim.x * WPU,
-                                                              kMaxUnit, unit_off, len_sh, scan_wsum, a.err));
+                                                              kMaxUnit, FUSE ? kWaveChunk / kTile : 0, unit_off,
+                                                              len_sh, scan_wsum, a.err));
   const int total_units = __builtin_amdgcn_readfirstlane(unit_off[a.B]);
   const int row0 = rg * MT_W * 32;                 // first query row (t*H + h) of this wave
 
@@ -486,10 +523,16 @@ __global__ void __launch_bounds__(256, 2) indexer_mfma_kernel(MfmaArgs a) {
       }
     }
     flush(t_flushed, t_end);
+    if constexpr (FUSE) {
+      // one query row: every position below L is visible
+      if (L > a.tk.k)
+        fused_chunk_select((const lds_f32*)&sbuf[wave][0], b, t_begin, L, a.tk.cand, a.tk.xc, a.tk.cc,
+                           a.tk.cand_stride, a.tk.max_chunks, a.tk.k, a.tk.slack);
+    }
   }
 }
 
-template <bool QFP8, bool KFP4, int HMT, int NQ, int RG>
+template <bool QFP8, bool KFP4, int HMT, int NQ, int RG, bool FUSE = false>
 static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
   static std::atomic<int> grid_by_dev[kMaxDevices];
   const int slot = current_device_slot();
@@ -499,17 +542,73 @@ static dsa_status_t launch_mfma(const MfmaArgs& a, hipStream_t stream) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, slot < 0 ? 0 : slot) != hipSuccess ||
         cus < 1)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG, FUSE>, 256,
+                                                     0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     grid = cus * per_cu;
     if (slot >= 0) grid_by_dev[slot].store(grid, std::memory_order_relaxed);
   }
-  DSA_LAUNCH((indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG>), dim3(grid), dim3(256), 0, stream, a);
+  DSA_LAUNCH((indexer_mfma_kernel<QFP8, KFP4, HMT, NQ, RG, FUSE>), dim3(grid), dim3(256), 0, stream, a);
   return launch_status("dsa_indexer_scores");
 }
 
+}  // namespace dsa
+
+namespace dsa {
+// Argument checks of the MFMA path (every check runs before anything is enqueued); fills the
+// launch arguments and the template selectors.
+static dsa_status_t mfma_setup(const char* who, const void* q, dsa_dtype_t q_dtype, const float* w,
+                               const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,
+                               const int32_t* seq_lens, int B, int Sq, int H, int D, int64_t score_stride,
+                               float* scores, int32_t* err_count, MfmaArgs& a, bool& f8, bool& fp4, int& HMT) {
+  DSA_CHECK_SUPPORTED((k_dtype == DSA_E4M3 || k_dtype == DSA_MXFP4) && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
+                      "%s: supported dtypes are (f32,f32) and q bf16/e4m3 with k e4m3/mxfp4", who);
+  DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && (int64_t)Sq * H <= 256 && B <= kMaxB,
+                      "%s: MFMA path needs D == 128, H %% 32 == 0, Sq*H <= 256, B <= 1024", who);
+  fp4 = k_dtype == DSA_MXFP4;
+  if (fp4) {
+    DSA_CHECK_ARG(keys->row_bytes == 64, "%s: MXFP4 row_bytes != 64", who);
+    DSA_CHECK_ARG(k_scale && ((uintptr_t)k_scale & 3) == 0, "%s: MXFP4 keys need 4-byte aligned E8M0 block scales",
+                  who);
+  } else {
+    DSA_CHECK_ARG(keys->row_bytes == 128, "%s: row_bytes != 128", who);
+  }
+  if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "%s: page_size %% 32 != 0", who);
+  // the MFMA path reads whole 32-token tiles (an unresolvable tile reads rows 0..31 as a
+  // stand-in), so the key rows hold at least one tile, and a dense tile never straddles the
+  // end of the rows or the boundary between two requests
+  DSA_CHECK_SUPPORTED(keys->num_rows >= kTile, "%s: MFMA path needs num_rows >= 32", who);
+  if (!keys->page_table)
+    DSA_CHECK_SUPPORTED(keys->num_rows % kTile == 0 && keys->req_stride % kTile == 0,
+                        "%s: dense keys on the MFMA path need num_rows and req_stride multiples of 32", who);
+  DSA_CHECK_SUPPORTED((int64_t)B * ((score_stride + kTile - 1) / kTile) < ((int64_t)1 << 31),
+                      "%s: B * ceil(score_stride / 32) must be below 2^31", who);
+  a = MfmaArgs{q, w, RowStore::from(*keys), k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count, TopkArgs{}};
+  HMT = H / 32;
+  f8 = q_dtype == DSA_E4M3;
+  {
+    // the (H / 32, Sq) combinations instantiated below
+    static const int kInst[][2] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
+    bool known = false;
+    for (const auto& c : kInst) known = known || (HMT == c[0] && Sq == c[1]);
+    DSA_CHECK_SUPPORTED(known, "%s: unsupported (Sq, H) combination for the MFMA path", who);
+  }
+  return DSA_OK;
+}
+
+// the stream joins the load stream only once every argument check has passed, so a rejected
+// call enqueues nothing
+static dsa_status_t join_ready(const char* who, hipEvent_t ready, hipStream_t stream) {
+  if (!ready) return DSA_OK;
+  const hipError_t e = hipStreamWaitEvent(stream, ready, 0);
+  if (e != hipSuccess) {
+    set_last_error("%s: hipStreamWaitEvent: %s", who, hipGetErrorString(e));
+    return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
 }  // namespace dsa
 
 extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, const float* w,
@@ -525,18 +624,6 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
   DSA_CHECK_ARG(keys->num_rows >= 1, "dsa_indexer_scores: num_rows < 1");
   DSA_CHECK_ARG(((uintptr_t)keys->base & 15) == 0, "dsa_indexer_scores: keys not 16-byte aligned");
   if (keys->page_table) DSA_CHECK_ARG(keys->page_size > 0 && keys->pt_stride >= 0, "dsa_indexer_scores: bad paging");
-  // the stream joins the load stream only once every argument check has passed, so a
-  // rejected call enqueues nothing
-  auto join_ready = [&]() -> dsa_status_t {
-    if (!ready) return DSA_OK;
-    hipError_t e = hipStreamWaitEvent(stream, ready, 0);
-    if (e != hipSuccess) {
-      set_last_error("dsa_indexer_scores: hipStreamWaitEvent: %s", hipGetErrorString(e));
-      return DSA_ERR_HIP;
-    }
-    return DSA_OK;
-  };
-  RowStore ks = RowStore::from(*keys);
   if (q_dtype == DSA_F32 && k_dtype == DSA_F32) {
     DSA_CHECK_SUPPORTED((int64_t)Sq * H * D <= kF32MaxQ && (int64_t)Sq * H <= 256 && D % 4 == 0,
                         "dsa_indexer_scores: fp32 path needs Sq*H*D <= 4096, Sq*H <= 256, D %% 4 == 0");
@@ -544,46 +631,20 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
     DSA_CHECK_ARG(score_stride <= (int64_t)65535 * 256, "dsa_indexer_scores: score_stride too large");
     DSA_CHECK_SUPPORTED(B <= 65535, "dsa_indexer_scores: fp32 path takes at most 65535 requests (grid y)");
     const int64_t gx = (score_stride + 255) / 256;
-    if (dsa_status_t st = join_ready(); st != DSA_OK) return st;
+    if (dsa_status_t st = join_ready("dsa_indexer_scores", ready, stream); st != DSA_OK) return st;
     DSA_LAUNCH(indexer_f32_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
-                       static_cast<const float*>(q), w, ks, static_cast<const float*>(k_scale), seq_lens, Sq, H, D, score_stride, scores,
-                       err_count);
+                       static_cast<const float*>(q), w, RowStore::from(*keys), static_cast<const float*>(k_scale),
+                       seq_lens, Sq, H, D, score_stride, scores, err_count);
     return launch_status("dsa_indexer_scores");
   }
-  DSA_CHECK_SUPPORTED((k_dtype == DSA_E4M3 || k_dtype == DSA_MXFP4) && (q_dtype == DSA_BF16 || q_dtype == DSA_E4M3),
-                      "dsa_indexer_scores: supported dtypes are (f32,f32) and q bf16/e4m3 with k e4m3/mxfp4");
-  DSA_CHECK_SUPPORTED(D == 128 && H % 32 == 0 && (int64_t)Sq * H <= 256 && B <= kMaxB,
-                      "dsa_indexer_scores: MFMA path needs D == 128, H %% 32 == 0, Sq*H <= 256, B <= 1024");
-  const bool fp4 = k_dtype == DSA_MXFP4;
-  if (fp4) {
-    DSA_CHECK_ARG(keys->row_bytes == 64, "dsa_indexer_scores: MXFP4 row_bytes != 64");
-    DSA_CHECK_ARG(k_scale && ((uintptr_t)k_scale & 3) == 0,
-                  "dsa_indexer_scores: MXFP4 keys need 4-byte aligned E8M0 block scales");
-  } else {
-    DSA_CHECK_ARG(keys->row_bytes == 128, "dsa_indexer_scores: row_bytes != 128");
-  }
-  if (keys->page_table) DSA_CHECK_SUPPORTED(keys->page_size % 32 == 0, "dsa_indexer_scores: page_size %% 32 != 0");
-  // the MFMA path reads whole 32-token tiles (an unresolvable tile reads rows 0..31 as a
-  // stand-in), so the key rows hold at least one tile, and a dense tile never straddles the
-  // end of the rows or the boundary between two requests
-  DSA_CHECK_SUPPORTED(keys->num_rows >= kTile, "dsa_indexer_scores: MFMA path needs num_rows >= 32");
-  if (!keys->page_table)
-    DSA_CHECK_SUPPORTED(keys->num_rows % kTile == 0 && keys->req_stride % kTile == 0,
-                        "dsa_indexer_scores: dense keys on the MFMA path need num_rows and req_stride "
-                        "multiples of 32");
-  DSA_CHECK_SUPPORTED((int64_t)B * ((score_stride + kTile - 1) / kTile) < ((int64_t)1 << 31),
-                      "dsa_indexer_scores: B * ceil(score_stride / 32) must be below 2^31");
-  MfmaArgs a{q, w, ks, k_scale, seq_lens, B, Sq, H, score_stride, scores, err_count};
-  const int HMT = H / 32;
-  const bool f8 = q_dtype == DSA_E4M3;
-  {
-    // the (H / 32, Sq) combinations instantiated below
-    static const int kInst[][2] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
-    bool known = false;
-    for (const auto& c : kInst) known = known || (HMT == c[0] && Sq == c[1]);
-    DSA_CHECK_SUPPORTED(known, "dsa_indexer_scores: unsupported (Sq, H) combination for the MFMA path");
-  }
-  if (dsa_status_t st = join_ready(); st != DSA_OK) return st;
+  MfmaArgs a;
+  bool f8 = false, fp4 = false;
+  int HMT = 0;
+  if (dsa_status_t st = mfma_setup("dsa_indexer_scores", q, q_dtype, w, keys, k_dtype, k_scale, seq_lens, B, Sq, H,
+                                   D, score_stride, scores, err_count, a, f8, fp4, HMT);
+      st != DSA_OK)
+    return st;
+  if (dsa_status_t st = join_ready("dsa_indexer_scores", ready, stream); st != DSA_OK) return st;
   // one wave covers up to 4 M tiles; queries beyond that go to a second wave on the same tile
 #define DSA_CASE(HM, NQ_, RG_)                                                                  \
   if (HMT == HM && Sq == NQ_ * RG_) {                                                            \
@@ -598,5 +659,48 @@ extern "C" dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t q_dtype, c
   DSA_CASE(4, 1, 1) DSA_CASE(4, 1, 2)
 #undef DSA_CASE
   set_last_error("dsa_indexer_scores: unsupported (Sq, H) combination for the MFMA path");
+  return DSA_ERR_UNSUPPORTED;
+}
+
+extern "C" dsa_status_t dsa_indexer_topk_chunks(const void* q, dsa_dtype_t q_dtype, const float* w,
+                                                const dsa_rows_t* keys, dsa_dtype_t k_dtype, const void* k_scale,
+                                                const int32_t* seq_lens, int B, int H, int D, int64_t score_stride,
+                                                float* scores, int k, void* ws, size_t ws_bytes, int32_t* err_count,
+                                                hipEvent_t ready, hipStream_t stream) {
+  using namespace dsa;
+  const char* who = "dsa_indexer_topk_chunks";
+  DSA_CHECK_ARG(B >= 0 && H >= 1 && D >= 1 && k >= 1, "%s: bad sizes", who);
+  if (B == 0) return DSA_OK;
+  DSA_CHECK_ARG(q && w && keys && keys->base && seq_lens && scores, "%s: null pointer", who);
+  DSA_CHECK_ARG(score_stride >= 1, "%s: score_stride < 1", who);
+  DSA_CHECK_ARG(keys->num_rows >= 1, "%s: num_rows < 1", who);
+  DSA_CHECK_ARG(((uintptr_t)keys->base & 15) == 0, "%s: keys not 16-byte aligned", who);
+  if (keys->page_table) DSA_CHECK_ARG(keys->page_size > 0 && keys->pt_stride >= 0, "%s: bad paging", who);
+  MfmaArgs a;
+  bool f8 = false, fp4 = false;
+  int HMT = 0;
+  if (dsa_status_t st = mfma_setup(who, q, q_dtype, w, keys, k_dtype, k_scale, seq_lens, B, 1, H, D, score_stride,
+                                   scores, err_count, a, f8, fp4, HMT);
+      st != DSA_OK)
+    return st;
+  bool wave_chunks = false;
+  if (dsa_status_t st = topk_setup(who, scores, score_stride, seq_lens, B, 1, k, nullptr, false, ws, ws_bytes, a.tk,
+                                   wave_chunks);
+      st != DSA_OK)
+    return st;
+  DSA_CHECK_SUPPORTED(wave_chunks, "%s: rows of %lld positions with k = %d do not take wave chunks", who,
+                      (long long)score_stride, k);
+  if (dsa_status_t st = join_ready(who, ready, stream); st != DSA_OK) return st;
+#define DSA_CASE(HM)                                                                             \
+  if (HMT == HM) {                                                                               \
+    if (fp4)                                                                                     \
+      return f8 ? launch_mfma<true, true, HM, 1, 1, true>(a, stream)                             \
+                : launch_mfma<false, true, HM, 1, 1, true>(a, stream);                           \
+    return f8 ? launch_mfma<true, false, HM, 1, 1, true>(a, stream)                              \
+              : launch_mfma<false, false, HM, 1, 1, true>(a, stream);                            \
+  }
+  DSA_CASE(1) DSA_CASE(2) DSA_CASE(4)
+#undef DSA_CASE
+  set_last_error("%s: unsupported head count for the MFMA path", who);
   return DSA_ERR_UNSUPPORTED;
 }

@@ -29,7 +29,7 @@
 // keys staged in LDS.
 #include <algorithm>
 
-#include "common.h"
+#include "topk_wave.h"
 
 namespace dsa {
 
@@ -38,11 +38,12 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kPer = 8;                            // keys per thread held in registers
 constexpr int kChunk = kTopkThreads * kPer;        // stage-1 chunk: 8192 positions
 constexpr int kLongPer = 16;                       // keys per thread of the long-row chunks
-constexpr int kMaxChunks = 256;                    // rows up to 2^21 positions
+constexpr int kMaxChunks = kTopkMaxChunks;         // rows up to 2^21 positions
 // Stage-1 work-groups that run in one round: 256 CUs x 2 work-groups of 1024 threads (the
 // chunk kernel fits eight waves per SIMD).  A larger grid switches to 16384-position chunks.
 constexpr int64_t kChunkRound = 512;
-constexpr int kMaxCand = kTopkThreads * kPer;      // stage-2 candidates held in registers
+constexpr int kMaxCand = kTopkMaxCand;             // stage-2 candidates held in registers
+static_assert(kMaxCand == kTopkThreads * kPer, "stage 2 holds kPer candidates per thread");
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
@@ -216,35 +217,6 @@ __device__ void ordered_take(KeyFn KEY, int n, uint32_t T, int need, int k, Topk
 
 // ---- register-resident select (both stages' hot path) ----
 
-// Wave-wide inclusive scans through DPP lane moves (no LDS round trips): four row
-// shifts build each 16-lane row's prefix, then row broadcasts of lanes 15 and 31 carry
-// the rows' totals forward.  Lanes with no source lane take the identity.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_move(uint32_t x, uint32_t identity) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
-}
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x, uint32_t identity, Op op) {
-  x = op(x, dpp_move<0x111, 0xf>(x, identity));   // row_shr:1
-  x = op(x, dpp_move<0x112, 0xf>(x, identity));   // row_shr:2
-  x = op(x, dpp_move<0x114, 0xf>(x, identity));   // row_shr:4
-  x = op(x, dpp_move<0x118, 0xf>(x, identity));   // row_shr:8
-  x = op(x, dpp_move<0x142, 0xa>(x, identity));   // row_bcast:15 into rows 1 and 3
-  x = op(x, dpp_move<0x143, 0xc>(x, identity));   // row_bcast:31 into rows 2 and 3
-  return x;
-}
-__device__ __forceinline__ int wave_sum_incl(int x) {
-  return (int)wave_scan_incl((uint32_t)x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-  x = wave_scan_incl(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-  x = wave_scan_incl(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-
 struct alignas(16) RadixShared {
   uint32_t hist[2][kBins];                 // digit histograms, alternating per pass
   uint32_t red[2 * kTopkWaves];            // per-wave min / max, then per-wave digit counts
@@ -349,11 +321,6 @@ __device__ void radix_select_reg(const uint32_t (&key)[PER], int k, uint32_t kmi
   need_out = remaining;
 }
 
-// number of set bits of m below this lane, plus acc
-__device__ __forceinline__ int lanes_below(uint64_t m, int acc) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)acc));
-}
-
 // Ordered take of the keys chosen by (T, need): slot q of thread t is the work-group's
 // element q * kTopkThreads + t, so element order is (q, wave, lane); per (q, wave) ballots
 // give each kept key its rank.  EMIT(slot, q) for each kept key.  Two barriers.
@@ -418,35 +385,6 @@ __device__ void take_reg(const uint32_t (&key)[PER], uint32_t T, int need, Radix
   }
 }
 
-struct TopkArgs {
-  const float* scores;
-  int64_t stride;
-  const int32_t* seq_lens;
-  int Sq, k;
-  int chunk;          // positions per stage-1 chunk: kWaveChunk, or kTopkThreads * (kPer or kLongPer)
-  int slack;          // extra candidates kept per chunk beyond twice its share (wave chunks)
-  int max_chunks;     // chunk slots per row
-  int cand_stride;    // candidate slots per row (>= the sum of the r_c)
-  uint32_t* xc;       // [rows, max_chunks] cut key of each chunk
-  int32_t* cc;        // [rows, max_chunks] candidates each chunk kept (at most its r_c slots)
-  uint2* cand;        // [rows, cand_stride] (key, position) candidates, position order
-  int32_t* idx;
-};
-
-// visible positions of the row, clamped to [0, stride]
-__device__ __forceinline__ int row_len(const TopkArgs& a, int row) {
-  const int b = row / a.Sq, t = row % a.Sq;
-  const int64_t n = (int64_t)a.seq_lens[b] - a.Sq + 1 + t;
-  return n < 0 ? 0 : (int)(n < a.stride ? n : a.stride);
-}
-
-// candidates kept by a chunk of `len` of the row's `n` positions: twice its share
-// ceil(k * len / n) of the k plus `slack`, at most len.  The shares add up to at least k.
-__device__ __forceinline__ int chunk_keep(int k, int len, int n, int slack) {
-  const int share = (int)(((int64_t)k * len + n - 1) / n);
-  return min(len, 2 * share + slack);
-}
-
 // stage 1, grid (max_chunks, rows), PER keys per thread (a.chunk = kTopkThreads * PER).
 // Chunk c's candidates start at c * r_full in the row's list (r_full: the keep of a full
 // chunk; only the last chunk can be shorter).  Eight waves per SIMD (two work-groups per
@@ -502,163 +440,6 @@ topk_chunk_kernel(TopkArgs a) {
     a.xc[(int64_t)row * a.max_chunks + c] = T;
     a.cc[(int64_t)row * a.max_chunks + c] = min(r, len);
   }
-}
-
-// ---- stage 1 on wave chunks (no work-group barriers, no LDS) ----
-//
-// Each wave owns one chunk of kWaveChunk positions, kWavePer keys per lane (position
-// lo + 64 q + lane in slot q, so slot-major lane order is position order).  Instead of an
-// exact select of r_c keys, the wave searches for a threshold T whose count of keys above
-// it lies in a window [lo_c, r_c] just below its slot budget, and keeps exactly those keys
-// (fewer than r_c candidates are fine: the slots left over hold key 0, which no select
-// takes, and stage 2 is exact for any cut key that bounds what was left out).  Each probe
-// of the search is one compare per key and a wave sum.  The first probe is the chunk's
-// mean plus z standard deviations, z the normal upper-tail quantile of the target
-// fraction (Abramowitz and Stegun 26.2.23); later probes are Illinois regula falsi in key
-// space, then bisection, on the bracket [kmin - 1, kmax].  When ties leave no threshold
-// inside the window the bracket closes on adjacent keys (A, B = A + 1): T = B, and the
-// first r_c - count(> B) keys equal to B are taken in position order, as an exact select.
-constexpr int kWaveChunk = 1024;
-constexpr int kWavePer = kWaveChunk / 64;
-constexpr int kWaveSlack = 16;                     // candidates kept beyond twice the share
-constexpr int kWaveMinSlack = 8;                   // below this, the rows take the work-group chunks
-constexpr int kWaveThreads = 256;
-constexpr int64_t kWaveMaxStride = (int64_t)kMaxChunks * kWaveChunk;
-constexpr int kWaveInterp = 6;                     // regula-falsi probes before bisection
-
-// wave sum of a float through DPP lane moves (the scan's last lane holds the total)
-__device__ __forceinline__ float wave_fsum(float x) {
-  const uint32_t t = wave_scan_incl(__float_as_uint(x), 0u, [](uint32_t a, uint32_t b) {
-    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
-  });
-  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)t, 63));
-}
-
-// number of the wave's keys above m (empty slots hold key 0, below every probe)
-template <int P>
-__device__ __forceinline__ int wave_count_above(const uint32_t (&key)[P], uint32_t m) {
-  int c = 0;
-#pragma unroll
-  for (int q = 0; q < P; ++q) c += key[q] > m ? 1 : 0;
-  const int incl = wave_sum_incl(c);
-  return __builtin_amdgcn_readlane(incl, 63);
-}
-
-// upper-tail standard normal quantile: P(Z > z) = p for 0 < p <= 0.5 (Abramowitz and
-// Stegun 26.2.23, absolute error below 4.5e-4)
-__device__ __forceinline__ float normal_upper_quantile(float p) {
-  const float t = __builtin_amdgcn_sqrtf(-2.0f * __logf(p));
-  return t - (2.515517f + t * (0.802853f + t * 0.010328f)) *
-                 __builtin_amdgcn_rcpf(1.0f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
-}
-
-// the order-preserving key of float_key without its branches: -0.0 folds into +0.0, then
-// negative floats are inverted and positive ones get the top bit
-__device__ __forceinline__ uint32_t float_key_fast(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = u == 0x80000000u ? 0u : u;
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
-// One wave chunk (FULL: all kWaveChunk positions inside the row, no masks).  v: the
-// chunk's scores; returns the candidate count, writes the cut key to T.
-template <bool FULL>
-__device__ __forceinline__ int wave_chunk(const float (&v)[kWavePer], int len, int r, int share, int lo, uint2* out,
-                                          uint32_t& T) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[kWavePer], kmin = 0xffffffffu, kmax = 0u;
-  float xs = 0.0f, xq = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kWavePer; ++q) {
-    const bool in = FULL || q * 64 + lane < len;
-    const uint32_t kq = float_key_fast(v[q]);
-    key[q] = in ? kq : 0u;
-    kmin = min(kmin, in ? kq : 0xffffffffu);
-    kmax = max(kmax, key[q]);
-    const float x = in ? v[q] : 0.0f;
-    xs += x;
-    xq = fmaf(x, x, xq);
-  }
-  kmin = wave_min(kmin);
-  kmax = wave_max(kmax);
-  char* const ob = reinterpret_cast<char*>(out);
-  const uint32_t p0 = (uint32_t)(lo + lane);
-  if (r >= len) {                                 // the whole chunk is kept; X_c = its smallest key
-#pragma unroll
-    for (int q = 0; q < kWavePer; ++q)
-      if (FULL || q * 64 + lane < len)
-        *reinterpret_cast<uint2*>(ob + (uint32_t)(q * 64 + lane) * 8u) = make_uint2(key[q], p0 + q * 64);
-    T = kmin;
-    return len;
-  }
-  const int lo_c = r - max(2, (r - share) / 4);
-  const float tc = 0.5f * (float)(lo_c + r);
-  // first probe: mean + z * deviation of the chunk's scores (one pass; a poor guess only
-  // costs probes)
-  const float inv_len = __builtin_amdgcn_rcpf((float)len);
-  const float mean = wave_fsum(xs) * inv_len;
-  const float sd = __builtin_amdgcn_sqrtf(fmaxf(wave_fsum(xq) * inv_len - mean * mean, 0.0f));
-  const float p_up = tc * inv_len;                // target fraction of the chunk above T
-  const float z = p_up <= 0.5f ? normal_upper_quantile(p_up) : -normal_upper_quantile(1.0f - p_up);
-  const float g = fmaf(z, sd, mean);
-  uint32_t A = kmin - 1u, B = kmax;               // count(> A) = len > r, count(> B) = 0 < lo_c
-  int cB = 0;                                     // exact count above B
-  float fA = (float)len, fB = 0.0f;               // Illinois-damped counts at the bracket ends
-  uint32_t m = (g == g && fabsf(g) <= 3.0e38f) ? float_key_fast(g) : A + (B - A) / 2u;
-  int side = 0, probes = 0;
-  while (B - A > 1u) {                            // the bracket shrinks at every probe
-    m = min(max(m, A + 1u), B - 1u);
-    const int cm = wave_count_above(key, m);
-    ++probes;
-    if (cm > r) {
-      A = m;
-      fA = (float)cm;
-      if (side < 0) fB = 0.5f * (fB + tc);
-      side = -1;
-    } else if (cm < lo_c) {
-      B = m;
-      cB = cm;
-      fB = (float)cm;
-      if (side > 0) fA = 0.5f * (fA + tc);
-      side = 1;
-    } else {                                      // inside the window: keep the keys above m
-      T = m;
-      int base = 0;
-#pragma unroll
-      for (int q = 0; q < kWavePer; ++q) {
-        const uint64_t tm = __builtin_amdgcn_ballot_w64(key[q] > m);
-        const int slot = lanes_below(tm, base);
-        if (key[q] > m) *reinterpret_cast<uint2*>(ob + (uint32_t)slot * 8u) = make_uint2(key[q], p0 + q * 64);
-        base += (int)__builtin_popcountll(tm);
-      }
-      for (int i = cm + lane; i < r; i += 64) *reinterpret_cast<uint2*>(ob + (uint32_t)i * 8u) = make_uint2(0u, 0u);
-      return cm;
-    }
-    if (probes < kWaveInterp && fA > fB) {
-      const float f = fminf(fmaxf((fA - tc) * __builtin_amdgcn_rcpf(fA - fB), 0.0f), 1.0f);
-      m = A + (uint32_t)((float)(B - A) * f);
-    } else {
-      m = A + (B - A) / 2u;
-    }
-  }
-  // adjacent bracket (ties across the window): exact select of r at T = B, the first
-  // `need` keys equal to B in position order
-  T = B;
-  const int need = r - cB;
-  int base = 0, eq_base = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int q = 0; q < kWavePer; ++q) {
-    const bool eq = key[q] == B;                   // never an empty slot: B > 0
-    const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
-    const bool take = key[q] > B || (eq && eq_base + (int)__builtin_popcountll(em & lt) < need);
-    const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
-    const int slot = lanes_below(tm, base);
-    if (take && slot < r) *reinterpret_cast<uint2*>(ob + (uint32_t)slot * 8u) = make_uint2(key[q], p0 + q * 64);
-    base += (int)__builtin_popcountll(tm);
-    eq_base += (int)__builtin_popcountll(em);
-  }
-  return r;
 }
 
 // stage 1 on wave chunks, a 1-D grid of rows x G work-groups (G = ceil(max_chunks / 4)):
@@ -891,7 +672,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_select_kernel(TopkArgs a) {
   }
 }
 
-static void topk_geometry(int64_t stride, int k, int chunk, int slack, int& max_chunks, int& cand_stride) {
+void topk_geometry(int64_t stride, int k, int chunk, int slack, int& max_chunks, int& cand_stride) {
   max_chunks = (int)((stride + chunk - 1) / chunk);
   // sum over chunks of min(len_c, 2 ceil(k len_c / n) + slack) <= min(n, 2k + (2 + slack) * chunks)
   cand_stride = (int)std::min<int64_t>(stride, 2 * (int64_t)k + (2 + (int64_t)slack) * max_chunks);
@@ -901,12 +682,65 @@ static void topk_geometry(int64_t stride, int k, int chunk, int slack, int& max_
 // exact select's registers: the slack is the largest one up to kWaveSlack that keeps the
 // candidate bound within kMaxCand.  Returns -1 when it would fall below kWaveMinSlack
 // (longer rows or larger k take the work-group chunks).
-static int topk_wave_slack(int64_t stride, int k) {
+int topk_wave_slack(int64_t stride, int k) {
   if (stride > kWaveMaxStride) return -1;
   if (stride <= kMaxCand) return kWaveSlack;
   const int64_t nch = (stride + kWaveChunk - 1) / kWaveChunk;
   const int64_t slack = std::min<int64_t>(kWaveSlack, (kMaxCand - 2 * (int64_t)k) / nch - 2);
   return slack >= kWaveMinSlack ? (int)slack : -1;
+}
+
+dsa_status_t topk_setup(const char* who, const float* scores, int64_t score_stride, const int32_t* seq_lens, int B,
+                        int Sq, int k, int32_t* idx, bool need_idx, void* ws, size_t ws_bytes, TopkArgs& a,
+                        bool& wave_chunks) {
+  DSA_CHECK_ARG(scores && seq_lens && (idx || !need_idx), "%s: null pointer", who);
+  DSA_CHECK_ARG(score_stride >= 1 && score_stride < ((int64_t)1 << 31), "%s: bad score_stride", who);
+  DSA_CHECK_SUPPORTED(k <= 8192, "%s: k > 8192", who);
+  DSA_CHECK_ARG((int64_t)B * Sq <= 65535, "%s: more than 65535 rows", who);
+  DSA_CHECK_SUPPORTED(score_stride <= (int64_t)kMaxChunks * kChunk, "%s: score_stride above %d", who,
+                      kMaxChunks * kChunk);
+  a = TopkArgs{};
+  a.scores = scores;
+  a.stride = score_stride;
+  a.seq_lens = seq_lens;
+  a.Sq = Sq;
+  a.k = k;
+  const int wave_slack = topk_wave_slack(score_stride, k);
+  wave_chunks = wave_slack >= 0;
+  const int64_t grid8 = (int64_t)B * Sq * ((score_stride + kChunk - 1) / kChunk);
+  const bool long_chunks = !wave_chunks && grid8 > kChunkRound;
+  a.chunk = wave_chunks ? kWaveChunk : (long_chunks ? kTopkThreads * kLongPer : kChunk);
+  a.slack = wave_chunks ? wave_slack : 0;
+  topk_geometry(score_stride, k, a.chunk, a.slack, a.max_chunks, a.cand_stride);
+  const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
+  if (ws == nullptr || ws_bytes < need) {
+    set_last_error("%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+    return DSA_ERR_WORKSPACE;
+  }
+  DSA_CHECK_ARG(((uintptr_t)ws & 7) == 0, "%s: workspace not 8-byte aligned", who);
+  const size_t rows = (size_t)B * Sq;
+  a.cand = static_cast<uint2*>(ws);
+  a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.cand_stride);
+  a.cc = reinterpret_cast<int32_t*>(a.xc + rows * a.max_chunks);
+  a.idx = idx;
+  return DSA_OK;
+}
+
+dsa_status_t topk_launch_select(const TopkArgs& a, int rows, hipStream_t stream) {
+  static std::atomic<bool> attr_by_dev[kMaxDevices];
+  const int slot = current_device_slot();
+  if (slot < 0 || !attr_by_dev[slot].load(std::memory_order_relaxed)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kSelectLds * sizeof(uint32_t)));
+    if (e != hipSuccess) {
+      set_last_error("top-k select: hipFuncSetAttribute: %s", hipGetErrorString(e));
+      return DSA_ERR_HIP;
+    }
+    if (slot >= 0) attr_by_dev[slot].store(true, std::memory_order_relaxed);
+  }
+  DSA_LAUNCH(topk_select_kernel, dim3(rows), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
+  return launch_status("top-k select");
 }
 
 }  // namespace dsa
@@ -929,59 +763,39 @@ extern "C" dsa_status_t dsa_topk(const float* scores, int64_t score_stride, cons
   using namespace dsa;
   DSA_CHECK_ARG(B >= 0 && Sq >= 1 && k >= 1, "dsa_topk: bad sizes");
   if (B == 0) return DSA_OK;
-  DSA_CHECK_ARG(scores && seq_lens && idx, "dsa_topk: null pointer");
-  DSA_CHECK_ARG(score_stride >= 1 && score_stride < ((int64_t)1 << 31), "dsa_topk: bad score_stride");
-  DSA_CHECK_SUPPORTED(k <= 8192, "dsa_topk: k > 8192");
-  DSA_CHECK_ARG((int64_t)B * Sq <= 65535, "dsa_topk: more than 65535 rows");
-  DSA_CHECK_SUPPORTED(score_stride <= (int64_t)kMaxChunks * kChunk, "dsa_topk: score_stride above %d",
-                      kMaxChunks * kChunk);
-  TopkArgs a{};
-  a.scores = scores;
-  a.stride = score_stride;
-  a.seq_lens = seq_lens;
-  a.Sq = Sq;
-  a.k = k;
-  const int wave_slack = topk_wave_slack(score_stride, k);
-  const bool wave_chunks = wave_slack >= 0;
-  const int64_t grid8 = (int64_t)B * Sq * ((score_stride + kChunk - 1) / kChunk);
-  const bool long_chunks = !wave_chunks && grid8 > kChunkRound;
-  a.chunk = wave_chunks ? kWaveChunk : (long_chunks ? kTopkThreads * kLongPer : kChunk);
-  a.slack = wave_chunks ? wave_slack : 0;
-  topk_geometry(score_stride, k, a.chunk, a.slack, a.max_chunks, a.cand_stride);
-  const size_t need = dsa_topk_workspace_size(B, Sq, k, score_stride);
-  if (ws == nullptr || ws_bytes < need) {
-    set_last_error("dsa_topk: workspace %zu < %zu bytes", ws_bytes, need);
-    return DSA_ERR_WORKSPACE;
-  }
-  DSA_CHECK_ARG(((uintptr_t)ws & 7) == 0, "dsa_topk: workspace not 8-byte aligned");
-  const size_t rows = (size_t)B * Sq;
-  a.cand = static_cast<uint2*>(ws);
-  a.xc = reinterpret_cast<uint32_t*>(a.cand + rows * a.cand_stride);
-  a.cc = reinterpret_cast<int32_t*>(a.xc + rows * a.max_chunks);
-  a.idx = idx;
-  static std::atomic<bool> attr_by_dev[kMaxDevices];
-  const int slot = current_device_slot();
-  if (slot < 0 || !attr_by_dev[slot].load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(kSelectLds * sizeof(uint32_t)));
-    if (e != hipSuccess) {
-      set_last_error("dsa_topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
-      return DSA_ERR_HIP;
-    }
-    if (slot >= 0) attr_by_dev[slot].store(true, std::memory_order_relaxed);
-  }
+  TopkArgs a;
+  bool wave_chunks = false;
+  if (dsa_status_t st = topk_setup("dsa_topk", scores, score_stride, seq_lens, B, Sq, k, idx, true, ws, ws_bytes, a,
+                                   wave_chunks);
+      st != DSA_OK)
+    return st;
   if (wave_chunks) {
     const int groups = (a.max_chunks + kWaveThreads / 64 - 1) / (kWaveThreads / 64);
     DSA_LAUNCH(topk_wave_kernel, dim3((unsigned)(groups * B * Sq)), dim3(kWaveThreads), 0, stream, a, groups,
                B * Sq);
-  }
-  else if (long_chunks)
+  } else if (a.chunk == kTopkThreads * kLongPer) {
     DSA_LAUNCH(topk_chunk_kernel<kLongPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
-  else
+  } else {
     DSA_LAUNCH(topk_chunk_kernel<kPer>, dim3(a.max_chunks, B * Sq), dim3(kTopkThreads), 0, stream, a);
+  }
   dsa_status_t st = launch_status("dsa_topk(chunk)");
   if (st != DSA_OK) return st;
-  DSA_LAUNCH(topk_select_kernel, dim3(B * Sq), dim3(kTopkThreads), kSelectLds * sizeof(uint32_t), stream, a);
-  return launch_status("dsa_topk(select)");
+  return topk_launch_select(a, B * Sq, stream);
+}
+
+extern "C" dsa_status_t dsa_topk_select_chunks(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                                               int B, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  using namespace dsa;
+  DSA_CHECK_ARG(B >= 0 && k >= 1, "dsa_topk_select_chunks: bad sizes");
+  if (B == 0) return DSA_OK;
+  TopkArgs a;
+  bool wave_chunks = false;
+  if (dsa_status_t st = topk_setup("dsa_topk_select_chunks", scores, score_stride, seq_lens, B, 1, k, idx, true, ws,
+                                   ws_bytes, a, wave_chunks);
+      st != DSA_OK)
+    return st;
+  DSA_CHECK_SUPPORTED(wave_chunks, "dsa_topk_select_chunks: rows of %lld positions with k = %d do not take wave "
+                      "chunks", (long long)score_stride, k);
+  return topk_launch_select(a, B, stream);
 }

@@ -21,7 +21,7 @@ from typing import List, Optional
 
 import torch
 
-from . import api as dsa
+from . import _lib, api as dsa
 
 _hip = None
 
@@ -83,16 +83,23 @@ class DecodeStep:
     """One decode step (indexer -> top-k -> sparse MLA) over fixed device buffers.
 
     All buffers are allocated once, so the step can be captured into a HIP graph and
-    replayed.  `run(stream, marks, layer)` enqueues the three entry points on `stream`,
-    reading the caches of layer `layer % len(layers)` (successive layers of a model read
-    different caches).  `marks`, if given, are four objects with a `record(stream)` method,
-    recorded before, between and after the stages.
+    replayed.  `run(stream, marks, layer)` enqueues the three stages on `stream`, reading the
+    caches of layer `layer % len(layers)` (successive layers of a model read different
+    caches).  `marks`, if given, are four objects with a `record(stream)` method, recorded
+    before, between and after the stages.
+
+    With `fused` (the default), a step with one query token per request runs the top-k's
+    chunk stage inside the scan (dsa_indexer_topk_chunks, then dsa_topk_select_chunks);
+    shapes the fused entry points do not take (it rejects them before enqueuing anything)
+    fall back to dsa_indexer_scores and dsa_topk.  Both give identical results.
     """
 
     def __init__(self, idx_q: torch.Tensor, idx_w: torch.Tensor, seq_lens: torch.Tensor, mla_q: torch.Tensor,
                  layers: List[LayerCaches], topk: int, scale: float, max_len: int, k_dtype: int, q_dtype: int,
-                 err: Optional[torch.Tensor] = None, o_dtype=torch.bfloat16):
+                 err: Optional[torch.Tensor] = None, o_dtype=torch.bfloat16, fused: bool = True):
         dev = idx_q.device
+        self.fused = None if fused else False     # None: not tried yet
+        self.topk, self.max_len, self.o_dtype = topk, max_len, o_dtype
         self.idx_q, self.idx_w, self.seq_lens, self.mla_q = idx_q, idx_w, seq_lens, mla_q
         self.layers, self.scale, self.k_dtype, self.q_dtype = layers, scale, k_dtype, q_dtype
         self.err = err if err is not None else torch.zeros(1, dtype=torch.int32, device=dev)
@@ -107,14 +114,34 @@ class DecodeStep:
         self.ws_topk = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, Sq, topk, max_len)), dtype=torch.uint8,
                                    device=dev)
 
+    def with_form(self, fused: bool) -> "DecodeStep":
+        """A step over the same inputs and layer caches (own outputs and workspaces) that
+        takes the fused or the separate scan and top-k."""
+        return DecodeStep(self.idx_q, self.idx_w, self.seq_lens, self.mla_q, self.layers, self.topk, self.scale,
+                          self.max_len, self.k_dtype, self.q_dtype, err=self.err, o_dtype=self.o_dtype, fused=fused)
+
     def stage(self, name, stream, layer=0):
         """Enqueue one stage ("indexer", "topk" or "mla") of the step on `stream`."""
         lc = self.layers[layer % len(self.layers)]
         if name == "indexer":
+            if self.fused is not False and self.idx.shape[1] == 1:
+                try:
+                    dsa.dsa_indexer_topk_chunks(self.idx_q, self.idx_w, lc.keys, lc.k_scale, self.seq_lens,
+                                                self.scores, self.idx.shape[-1], self.ws_topk, k_dtype=self.k_dtype,
+                                                err=self.err, q_dtype=self.q_dtype, stream=stream)
+                    self.fused = True
+                    return
+                except dsa.DsaError as e:
+                    if self.fused or e.status != _lib.DSA_ERR_UNSUPPORTED:
+                        raise
+            self.fused = False
             dsa.dsa_indexer_scores(self.idx_q, self.idx_w, lc.keys, lc.k_scale, self.seq_lens, self.scores,
                                    k_dtype=self.k_dtype, err=self.err, q_dtype=self.q_dtype, stream=stream)
         elif name == "topk":
-            dsa.dsa_topk(self.scores, self.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
+            if self.fused:
+                dsa.dsa_topk_select_chunks(self.scores, self.seq_lens, self.idx, self.ws_topk, stream=stream)
+            else:
+                dsa.dsa_topk(self.scores, self.seq_lens, self.idx, ws=self.ws_topk, stream=stream)
         elif name == "mla":
             dsa.dsa_sparse_mla_decode(self.mla_q, self.idx, lc.kv, self.scale, self.o, self.lse, ws=self.ws_mla,
                                       err=self.err, stream=stream)

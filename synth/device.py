@@ -95,8 +95,8 @@ class DevWorkload:
                                    dsa.Rows(kv, 1152, self.page_table, self.wl.page_size)))
         return out
 
-    def decode_step(self, layers: int = 1, o_dtype=torch.bfloat16) -> DecodeStep:
+    def decode_step(self, layers: int = 1, o_dtype=torch.bfloat16, fused: bool = True) -> DecodeStep:
         """A DecodeStep over this workload, rotating through `layers` copies of its caches."""
         return DecodeStep(self.idx_q, self.idx_w, self.seq_lens, self.mla_q, self.layer_caches(layers),
                           self.wl.topk, self.wl.scale, self.Lmax, self.k_dtype, self.q_dtype, err=self.err,
-                          o_dtype=o_dtype)
+                          o_dtype=o_dtype, fused=fused)

@@ -155,6 +155,29 @@ def test_indexer_rejects_before_joining_the_load_stream():
                                 p, None, bogus_event, None) == _lib.DSA_ERR_UNSUPPORTED
 
 
+def test_fused_scan_topk_rejects_before_any_device_call():
+    """dsa_indexer_topk_chunks / dsa_topk_select_chunks check every argument on the host."""
+    L = _lib.load()
+    rows = _lib.dsa_rows_t()
+    rows.base, rows.row_bytes, rows.num_rows, rows.req_stride = 16, 128, 1 << 20, 65536
+    p = ctypes.c_void_p(16)
+    ws_need = L.dsa_topk_workspace_size(2, 1, 2048, 65536)
+
+    def fused(q_dtype=_lib.DSA_BF16, k_dtype=_lib.DSA_E4M3, H=64, stride=65536, k=2048, ws_bytes=ws_need):
+        return L.dsa_indexer_topk_chunks(p, q_dtype, p, ctypes.byref(rows), k_dtype, None, p, 2, H, 128, stride, p,
+                                         k, p, ws_bytes, None, None, None)
+    assert fused(k=0) == _lib.DSA_ERR_INVALID_ARG
+    assert fused(k=9000) == _lib.DSA_ERR_UNSUPPORTED
+    assert fused(q_dtype=_lib.DSA_F32, k_dtype=_lib.DSA_F32) == _lib.DSA_ERR_UNSUPPORTED   # no fp32 grid path
+    assert fused(H=96) == _lib.DSA_ERR_UNSUPPORTED
+    assert fused(stride=300000, ws_bytes=1 << 30) == _lib.DSA_ERR_UNSUPPORTED   # rows take work-group chunks
+    assert b"wave chunks" in L.dsa_last_error()
+    assert fused(ws_bytes=ws_need - 8) == _lib.DSA_ERR_WORKSPACE
+    assert L.dsa_topk_select_chunks(p, 65536, p, 2, 2048, None, p, ws_need, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_select_chunks(p, 300000, p, 2, 2048, p, p, 1 << 30, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert L.dsa_topk_select_chunks(p, 65536, p, 2, 2048, p, p, ws_need - 8, None) == _lib.DSA_ERR_WORKSPACE
+
+
 def test_merge_partials_rejects_bad_arguments():
     L = _lib.load()
     p = ctypes.c_void_p(16)

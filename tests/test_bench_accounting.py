@@ -25,6 +25,9 @@ def test_decode_step_work():
     assert w["indexer"] == (keys + sigma + q + wts + pages + scores, 2 * 32 * 64 * 128 * 65536)
     assert w["indexer"][0] == 285_876_224
     assert w["topk"] == (scores + 32 * 2048 * 4, 0)
+    # with the chunk stage in the scan's epilogue the top-k stage only writes the indices
+    wf = _bench().algorithmic_work(32, 65536, 64, 128, 2048, 128, 64, topk_fused=True)
+    assert wf["topk"] == (32 * 2048 * 4, 0) and wf["indexer"] == w["indexer"] and wf["mla"] == w["mla"]
     rows = 32 * 2048 * 1152                   # selected 576-wide bf16 latent rows
     mla_q, idx, o, lse = 32 * 128 * 576 * 2, 32 * 2048 * 4, 32 * 128 * 512 * 2, 32 * 128 * 4
     assert w["mla"] == (rows + mla_q + idx + o + lse, 2 * 32 * 128 * 2048 * (576 + 512))
