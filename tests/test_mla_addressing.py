@@ -180,3 +180,27 @@ def test_grid_addresses_in_bounds(B, Sq, H, k):
                 else:
                     ob = ((np.int64(QR - 1) * splits + splits - 1) * H + head[ok]) * VDIM + g_of[ok] * 4 + vt * 16
                     assert (ob + 4 <= QR * splits * H * VDIM).all()
+
+
+@pytest.mark.parametrize("B,Sq,H,k", GRIDS)
+def test_output_rows_written_inside_o_or_the_partials(B, Sq, H, k):
+    """Wave ws of head block hb writes the rows of its heads below H, head0 .. head0 +
+    min(16, H - head0), of its query row (and split): inside o [QR, H, 512] or the partials
+    [QR, splits, H, 512]."""
+    nw = 4 if H >= 64 else (2 if H > 16 else 1)
+    QR = B * Sq
+    splits = split_plan(B, Sq, H, k)
+    nhb = -(-H // (16 * nw))
+    for hb in range(nhb):
+        for ws in range(nw):
+            head0 = hb * 16 * nw + ws * 16
+            rows_ok = min(16, H - head0)
+            if rows_ok <= 0:
+                continue
+            for qr, split in ((0, 0), (QR - 1, splits - 1)):
+                if splits == 1:
+                    end = (qr * H + head0 + rows_ok) * VDIM
+                    assert end <= QR * H * VDIM
+                else:
+                    end = ((qr * splits + split) * H + head0 + rows_ok) * VDIM
+                    assert end <= QR * splits * H * VDIM
