@@ -537,16 +537,33 @@ static int device_cus() {
 // waves per work-group: 16 heads each, up to one per SIMD
 static int mla_waves(int H) { return H >= 64 ? 4 : (H > 16 ? 2 : 1); }
 
+// Splits per (query row, head block): one work-group fits a CU (its LDS ring), so a launch of
+// W work-groups runs in ceil(W / CUs) rounds and takes about rounds x (F + tiles per split)
+// tile-times, F being the per-work-group start-up and finish in tile-times (≈ 8: 18.8 µs for
+// a one-tile work-group against 1.74 µs per further tile).  The plan takes the split count
+// with the least such estimate (ties: fewer splits, fewer partials), from the fewest that
+// keep a split within kMaxSplit rows up to four times the count that covers the CUs.  With
+// 264 work-groups at 2 splits, a 66-row batch ran a second round of 8; 3 splits make two full
+// rounds of shorter work-groups.
+constexpr int kSplitStartTiles = 8;
 static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_split) {
   const int wg_heads = 16 * mla_waves(H);
   const int64_t wgs = (int64_t)B * Sq * ((H + wg_heads - 1) / wg_heads);
   const int tiles = (k + kTT - 1) / kTT;
-  // one work-group per CU
-  int s = (int)((device_cus() + wgs - 1) / wgs);
-  if (s < 1) s = 1;
-  if (s > tiles) s = tiles;
+  const int64_t cus = device_cus();
   const int min_s = (tiles + kMaxSplit / kTT - 1) / (kMaxSplit / kTT);
-  if (s < min_s) s = min_s;
+  const int cover = (int)std::min<int64_t>(tiles, (cus + wgs - 1) / wgs);
+  const int max_s = std::max(min_s, std::min(tiles, 4 * std::max(cover, 1)));
+  int s = min_s;
+  int64_t best = -1;
+  for (int c = min_s; c <= max_s; ++c) {
+    const int64_t rounds = (wgs * c + cus - 1) / cus;
+    const int64_t cost = rounds * (kSplitStartTiles + (tiles + c - 1) / c);
+    if (best < 0 || cost < best) {
+      best = cost;
+      s = c;
+    }
+  }
   const int tps = (tiles + s - 1) / s;
   per_split = tps * kTT;
   splits = (k + per_split - 1) / per_split;
