@@ -424,6 +424,309 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   }
 }
 
+// ---- role-split form: 64 heads per work-group, eight waves in two roles
+// Score waves 0-3: wave w keeps q^T of heads 16w..16w+15 in VGPRs and computes
+//   S^T[32 tokens x 16 heads] = K_tile . q^T exactly as the two-stream form does, then the
+//   online softmax of its heads; it writes P^T (bf16, already in the B-operand lane layout of
+//   the value product) and, when its running max moved, the heads' rescale factors to LDS.
+// Value waves 4-7: wave 4+d keeps O^T for value dims 128d..128d+127 of all 64 heads (32
+//   accumulator tiles of 16 dims x 16 heads) and adds V^T . P^T for the tile the score waves
+//   finished one iteration earlier.  Each V^T operand read serves the four head groups, so a
+//   tile's V^T bytes are read from LDS once per 64 heads instead of once per 16.  The value
+//   waves also issue the row loads (token group d of every tile).
+// Iteration i: score waves take tile i, value waves tile i-1, one barrier.  Ring slot i % 4
+// holds tile i from its load (issued in iteration i-2) until the value waves are done with it
+// (iteration i+1), so two tiles are always in flight.
+constexpr int kRolesRing = 4;
+constexpr int kScoreRK = 2;     // K-operand read buffers of a score wave
+
+__global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
+  constexpr int NT = 512;
+  constexpr int CPT = kTileSlots / 256;     // LDS-direct loads per value-wave thread per tile
+  static_assert(CPT == 9, "a tile is 36 blocks, nine per value wave");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRolesRing][kTileBytes];
+  __shared__ int32_t rowix[kMaxSplit];      // row index of each selected row of the split, -1 = none
+  __shared__ uint32_t tmask[kMaxSplit / kTT];          // valid-row bits per tile
+  __shared__ uint32_t mmask[4][kMaxSplit / kTT];       // union form: the entries each head group's query selected
+  __shared__ bf16x8 pbuf[2][4][64];         // P^T of a tile per head group, lane (n, g) as the B operand
+  __shared__ float abuf[2][4][16];          // rescale factor per (head group, head), valid when aflag is set
+  __shared__ __attribute__((aligned(16))) uint32_t aflag[2][4];
+  __shared__ float xinv[4][16];             // 1 / sum of the bf16 weights per head, for the output
+  static_assert(kRolesRing * kTileBytes + kMaxSplit * 4 + (kMaxSplit / kTT) * 4 * 5 + 2 * 4 * 64 * 16 +
+                        2 * 4 * 16 * 4 + 2 * 4 * 4 + 4 * 16 * 4 <= 160 * 1024,
+                "LDS budget");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nhb = (a.H + 63) / 64;
+  int unit, hb;
+  mla_block_unit(nhb, unit, hb);
+  const int qr = unit / a.splits;
+  const int split = unit - qr * a.splits;
+  const int b = qr / a.Sq;
+
+  const int kq = a.counts ? max(0, min(a.k, a.counts[qr])) : a.k;
+  const int per = a.counts ? min(a.per_split, (((kq + a.splits - 1) / a.splits) + kTT - 1) / kTT * kTT) : a.per_split;
+  const int e_begin = split * per;
+  const int e_end = min(e_begin + per, kq);
+  const int ntiles = e_end > e_begin ? (e_end - e_begin + kTT - 1) / kTT : 0;
+  const int32_t* idx = a.idx + (int64_t)qr * a.k;
+
+  // ---- resolve every selected row of this split once: index -> page table -> row
+  for (int e = tid; e < ntiles * kTT; e += NT) {
+    int32_t r = -1;
+    if (e_begin + e < e_end) {
+      const int32_t p = idx[e_begin + e];
+      const int64_t row = a.rows.row(b, p);
+      if (row < 0 && p >= 0) count_error(a.err);
+      if (row >= 0) r = (int32_t)row;       // num_rows < 2^31 (checked on the host)
+    }
+    rowix[e] = r;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(r >= 0);
+    if (lane == 0) {            // e is a multiple of 64 here: lanes 0-31 and 32-63 are two tiles
+      tmask[e >> 5] = (uint32_t)m;
+      if ((e >> 5) + 1 < ntiles) tmask[(e >> 5) + 1] = (uint32_t)(m >> 32);
+    }
+  }
+
+  if (wave < 4) {
+    // ================================================================ score wave
+    const int w = wave;
+    const int head = hb * 64 + w * 16 + n;
+    const bool head_ok = head < a.H;
+    bf16x8 qb[18];              // q^T: lane (n, g) holds dims 32j + 8g .. +8 of head n
+    {
+      const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + g * 8;
+#pragma unroll
+      for (int j = 0; j < 18; ++j) {
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + j * 32);
+        if (!head_ok) v = bf16x8{};
+        qb[j] = v;
+      }
+    }
+    int koff[2][2];             // K operand of M tile mt, k-step j: koff[j % 2][mt] + 4 blocks (j / 2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) koff[j][mt] = chunk_byte(n + 16 * mt, 4 * j + g);
+    if (a.member && lane < ntiles) {
+      // the query of this wave's 16 heads (fold_h is a multiple of 16, so they share one)
+      const int t = (hb * 64 + w * 16) / a.fold_h;
+      mmask[w][lane] = (t < a.fold_sq) ? a.member[((int64_t)qr * a.fold_sq + t) * a.mwords + e_begin / kTT + lane] : 0u;
+    }
+    __syncthreads();            // rowix / tmask / mmask ready
+
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
+    float m_used = -INFINITY;   // log2-domain running max used for p
+    float l_part = 0.0f;        // this lane's share of sum p (fp32 p: for lse)
+    float lr_part = 0.0f;       // this lane's share of sum bf16(p) (the PV weights: for o)
+    for (int i = 0; i <= ntiles; ++i) {
+      __syncthreads();          // tile i is in its slot; the value waves are done with P of tile i-2
+      if (i >= ntiles) continue;
+      const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((i % kRolesRing) * kTileBytes));
+
+      // ---- S^T over the 576 latent dims: two independent 16-token chains, operand reads
+      // kScoreRK - 1 steps ahead
+      f32x4 s0 = f32x4{}, s1 = f32x4{};
+      {
+        auto kop = [&](int j, int mt) {
+          return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + koff[j & 1][mt] +
+                                                                                   (j >> 1) * 4 * kBlockBytes);
+        };
+        bf16x8 r0[kScoreRK], r1[kScoreRK];
+#pragma unroll
+        for (int c = 0; c < kScoreRK - 1; ++c) {
+          r0[c] = kop(c, 0);
+          r1[c] = kop(c, 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 18; ++j) {
+          if (j + kScoreRK - 1 < 18) {
+            r0[(j + kScoreRK - 1) % kScoreRK] = kop(j + kScoreRK - 1, 0);
+            r1[(j + kScoreRK - 1) % kScoreRK] = kop(j + kScoreRK - 1, 1);
+          }
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0[j % kScoreRK], qb[j], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1[j % kScoreRK], qb[j], s1, 0, 0, 0);
+        }
+      }
+      float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};   // tokens 4g+i, 16+4g+i
+
+      // ---- online softmax for head n
+      uint32_t vmask = __builtin_amdgcn_readfirstlane(tmask[i]);
+      if (a.member) vmask &= __builtin_amdgcn_readfirstlane(mmask[w][i]);
+      if (vmask != 0xffffffffu) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int tok = (c >> 2) * 16 + g * 4 + (c & 3);
+          if (!((vmask >> tok) & 1u)) s[c] = -INFINITY;
+        }
+      }
+      float tmax = s[0];
+#pragma unroll
+      for (int c = 1; c < 8; ++c) tmax = fmaxf(tmax, s[c]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;   // scale > 0 keeps the order
+      const bool grow = tmax > m_used + kLazy || (m_used == -INFINITY && tmax > -INFINITY);
+      uint32_t rescaled = 0;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? tmax : m_used;
+        const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+        l_part *= alpha;
+        lr_part *= alpha;
+        m_used = m_new;
+        if (g == 0) abuf[i & 1][w][n] = alpha;
+        rescaled = 1;
+      }
+      const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
+      uint32_t pb[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c], a.scale_log2, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c + 1], a.scale_log2, -msub));
+        const uint32_t wd = pack_bf16x2(p0, p1);
+        pb[c] = wd;
+        l_part += p0 + p1;
+        lr_part += __uint_as_float(wd << 16) + __uint_as_float(wd & 0xffff0000u);
+      }
+      pbuf[i & 1][w][lane] = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
+      if (lane == 0) aflag[i & 1][w] = rescaled;
+    }
+
+    // ---- finish: l over the head's four lanes; the value waves normalise and write o
+    float l_tot = l_part + __shfl_xor(l_part, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    float lr_tot = lr_part + __shfl_xor(lr_part, 16);
+    lr_tot += __shfl_xor(lr_tot, 32);
+    if (g == 0) xinv[w][n] = (lr_tot > 0.0f) ? 1.0f / lr_tot : 0.0f;
+    const float lse = (l_tot > 0.0f) ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (g == 0 && head_ok) {
+      if (a.splits == 1)
+        a.lse[(int64_t)qr * a.H + head] = lse;
+      else
+        a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
+    }
+    __syncthreads();            // xinv ready
+    return;
+  }
+
+  // ================================================================== value wave
+  const int d = wave - 4;       // value dims 128d .. 128d + 127 = value tiles 8d .. 8d + 7
+  // LDS-direct load r of this lane: token group d, chunk group r; the lane fetches chunk
+  // (lane % 8) ^ 2(m/2) of token m = 8d + lane / 8
+  const int dlane = ((lane & 7) ^ (((lane >> 4) & 3) << 1)) * 16;
+  int voff[4];                  // V^T operand of value tile vt: voff[vt % 4] + 4 blocks (vt / 4)
+  {
+    const int jj = n >> 2, qq = n & 3;          // source lane n = 4 jj + qq of this 16-lane group
+    const int tok = 4 * g + jj;
+#pragma unroll
+    for (int vm = 0; vm < 4; ++vm) voff[vm] = chunk_byte(tok, 2 * vm + (qq >> 1)) + (qq & 1) * 8;
+  }
+  // rows that are padding or unresolvable are loaded from this query row instead (finite
+  // values; their probabilities are exactly zero)
+  const char* stand_in = reinterpret_cast<const char*>(a.q + (int64_t)qr * a.H * kRowEl);
+  __syncthreads();              // rowix / tmask / mmask ready
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
+  const char* nsrc[1];          // row of the next tile this lane loads
+  auto prepare = [&](int T) {
+    const int32_t r = rowix[T * kTT + d * 8 + (lane >> 3)];
+    nsrc[0] = (r >= 0 ? a.rows.base + (int64_t)r * kRowBytes : stand_in) + dlane;
+  };
+  auto issue = [&](int T) {
+    const uint32_t dst = ring_lds + (uint32_t)((T % kRolesRing) * kTileBytes + d * kBlockBytes);
+    dma_tile<0, CPT, 1, 4>(nsrc, dst);
+  };
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    if (T < ntiles) {
+      prepare(T);
+      issue(T);
+    }
+  }
+  if (2 < ntiles) prepare(2);
+
+  f32x4 oacc[4][8];             // [head group][value tile 8d + v]
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) oacc[h][v] = f32x4{};
+
+  for (int i = 0; i <= ntiles; ++i) {
+    if (i + 1 < ntiles)
+      wait_vmcnt<CPT>();        // this wave's loads of tile i are done (tile i+1's may be in flight)
+    else
+      wait_vmcnt<0>();
+    __syncthreads();            // tile i complete; P of tile i-1 written; the slot of tile i-2 is free
+    if (i + 2 < ntiles) {
+      issue(i + 2);
+      if (i + 3 < ntiles) prepare(i + 3);
+    }
+    if (i == 0) continue;
+    const int T = i - 1;
+    const int pslot = T & 1;
+    const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((T % kRolesRing) * kTileBytes));
+    bf16x8 pt[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pt[h] = pbuf[pslot][h][lane];
+    const u32x4 fl = *reinterpret_cast<const u32x4*>(&aflag[pslot][0]);
+    if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (__builtin_amdgcn_readfirstlane(fl[h])) {
+          const float alpha = abuf[pslot][h][n];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) oacc[h][v] *= alpha;
+        }
+      }
+    }
+
+    // ---- O^T += V^T . P^T over this wave's 8 value tiles, each read once for the 4 head groups
+    auto vop = [&](int v) {     // tokens 4g.. (first 8 bytes) and 16+4g.. (last 8 bytes)
+      const int vt = 8 * d + v;
+      const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4 * kBlockBytes;
+      const u32x2 lo = lds_read_tr16(p);
+      const u32x2 hi = lds_read_tr16(p + 2 * kBlockBytes);   // tokens + 16: two token groups on
+      return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    };
+    constexpr int RV = 3;       // operand reads in flight
+    bf16x8 rv[RV];
+#pragma unroll
+    for (int c = 0; c < RV - 1; ++c) rv[c] = vop(c);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      if (v + RV - 1 < 8) rv[(v + RV - 1) % RV] = vop(v + RV - 1);
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        oacc[h][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[v % RV], pt[h], oacc[h][v], 0, 0, 0);
+    }
+  }
+
+  __syncthreads();              // xinv ready
+  const bool direct = a.splits == 1;
+  void* dst = direct ? a.o : a.part_o;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int head = hb * 64 + h * 16 + n;
+    if (head >= a.H) continue;
+    const float inv = xinv[h][n];
+    const int64_t obase =
+        (direct ? ((int64_t)qr * a.H + head) : ((((int64_t)qr * a.splits + split) * a.H + head))) * kVDim +
+        d * 128 + g * 4;
+    if (a.o_f32) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + obase + v * 16) = oacc[h][v] * inv;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + obase + v * 16) =
+            u32x2{pack_bf16x2(oacc[h][v].x * inv, oacc[h][v].y * inv),
+                  pack_bf16x2(oacc[h][v].z * inv, oacc[h][v].w * inv)};
+    }
+  }
+}
+
 // merge of split partials: 64 threads per (query row, head), 8 value dims per thread.  With
 // SMAX > 0 (splits <= SMAX) every lse and partial load is issued before any is used, so a
 // thread waits for memory once; SMAX == 0 handles any split count.  F32: o and the partials
@@ -639,6 +942,7 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   DSA_CHECK_ARG(scale > 0.0f && scale < INFINITY, "dsa_sparse_mla_decode: scale must be positive and finite");
   DSA_CHECK_SUPPORTED(H % 16 == 0 && k <= 65536, "dsa_sparse_mla_decode: needs H %% 16 == 0 and k <= 65536");
   if (rows->page_table) DSA_CHECK_ARG(rows->page_size > 0, "dsa_sparse_mla_decode: bad page_size");
+  DSA_CHECK_SUPPORTED(rows->num_rows < ((int64_t)1 << 31), "dsa_sparse_mla_decode: num_rows must be below 2^31");
   DSA_CHECK_SUPPORTED((int64_t)B * Sq * ((H + 15) / 16) <= (1 << 24),
                       "dsa_sparse_mla_decode: more than 2^24 (query row, 16-head group) pairs");
   int splits, per;
@@ -682,7 +986,7 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   const int nhb = (H + 16 * nw - 1) / (16 * nw);
   const dim3 grid(splits * QR * nhb);
   if (nw == 4)
-    DSA_LAUNCH((mla_decode_kernel<4, 2>), grid, dim3(512), 0, stream, a);
+    DSA_LAUNCH(mla_roles_kernel, grid, dim3(512), 0, stream, a);
   else if (nw == 2)
     DSA_LAUNCH((mla_decode_kernel<2, 2>), grid, dim3(256), 0, stream, a);
   else

@@ -1,10 +1,10 @@
-"""Host simulation of every LDS and global address the sparse-MLA decode kernel computes.
+"""Host simulation of every LDS and global address the sparse-MLA decode kernels compute.
 
-The kernel (csrc/mla.hip, mla_decode_kernel<NW, 2>) stages 32-token tiles of 576-wide bf16
-rows in an LDS ring through LDS-direct loads and reads its MFMA operands back with plain
-and transposing LDS reads.  This file restates that index arithmetic lane by lane, in numpy,
-and checks on the CPU, for every work-group shape the library launches and the grids the
-GPU tests run:
+The kernels (csrc/mla.hip: mla_decode_kernel<NW, 2> for 16-48 heads, mla_roles_kernel for 64
+heads per work-group) stage 32-token tiles of 576-wide bf16 rows in an LDS ring through
+LDS-direct loads and read their MFMA operands back with plain and transposing LDS reads.
+This file restates that index arithmetic lane by lane, in numpy, and checks on the CPU, for
+every work-group shape the library launches and the grids the GPU tests run:
 
   * every LDS-direct destination, K-operand read, V^T transpose read and stream-merge staging
     access lies inside the ring; every global row read lies inside its 1152-byte row; every
@@ -15,7 +15,12 @@ GPU tests run:
     group g value dims 16 vt + i at tokens 4g..4g+3 and 16+4g..16+4g+3 (the operand layouts
     the MFMAs are issued with), using the ds_read_b64_tr_b16 lane mapping measured on the
     device: within each 16-lane group, lane i receives element i % 4 of the 8-byte rows
-    addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+    addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4;
+  * the role-split kernel's schedule: the value waves' row loads, the score waves' K reads and
+    P^T writes and the value waves' V^T and P^T reads never touch a ring slot or P buffer
+    that another role uses in the same barrier interval, every tile is read only after the
+    loads that fill it were waited for, and P^T of a tile is read one interval after it was
+    written, before it is overwritten.
 """
 import numpy as np
 import pytest
@@ -29,6 +34,7 @@ BLOCK = 1024
 NS = 2                                   # token streams per work-group
 RING_OF = {1: NS * 2, 2: NS * 2, 4: NS * 2}   # RING = NS * (PD + 1), PD = 1 for two streams
 KMAXSPLIT = 1024
+ROLES_RING = 4                           # mla_roles_kernel: tile T in slot T % 4
 
 lanes = np.arange(64)
 n_of, g_of = lanes & 15, lanes >> 4
@@ -137,7 +143,7 @@ GRIDS = [(32, 1, 128, 2048), (8, 4, 128, 2048), (66, 1, 128, 2048), (1, 1, 16, 2
 @pytest.mark.parametrize("B,Sq,H,k", GRIDS)
 def test_grid_addresses_in_bounds(B, Sq, H, k):
     nw = 4 if H >= 64 else (2 if H > 16 else 1)
-    RING = RING_OF[nw]
+    RING = ROLES_RING if nw == 4 else RING_OF[nw]
     QR = B * Sq
     splits = split_plan(B, Sq, H, k)
     tiles = -(-k // TT)
@@ -164,11 +170,18 @@ def test_grid_addresses_in_bounds(B, Sq, H, k):
     # ring slots used by tile T of stream s: (T % RING) * TILE_BYTES + block offsets checked above
     for T in range(int(ntiles.max())):
         assert (T % RING) * TILE_BYTES + TILE_BYTES <= RING * TILE_BYTES
-    # stream merge through the idle ring: f32x4 at (ws * 32 + vt) * 64 + lane, then 3 floats per lane
-    xo_end = (nw * 32 * 64) * 16
-    xs_end = xo_end + (nw * 3 * 64) * 4
-    assert xs_end <= RING * TILE_BYTES
+    if nw < 4:
+        # stream merge through the idle ring: f32x4 at (ws * 32 + vt) * 64 + lane, then 3 floats per lane
+        xo_end = (nw * 32 * 64) * 16
+        xs_end = xo_end + (nw * 3 * 64) * 4
+        assert xs_end <= RING * TILE_BYTES
+    else:
+        # role split: value wave d loads row rowix[T * 32 + 8 d + lane / 8] of tile T < ntiles
+        for d in range(4):
+            e = (ntiles.max() - 1) * TT + 8 * d + (lanes >> 3)
+            assert (e < KMAXSPLIT).all()
     # output writes: direct o [QR, H, 512] or partials [QR, splits, H, 512], 4 values at g * 4 + vt * 16
+    # (the role-split kernel's value wave d writes value tiles 8d .. 8d + 7 of every head group)
     for h_blk in range(nhb):
         for ws_ in range(nw):
             head = h_blk * 16 * nw + ws_ * 16 + n_of
@@ -204,3 +217,107 @@ def test_output_rows_written_inside_o_or_the_partials(B, Sq, H, k):
                 else:
                     end = ((qr * splits + split) * H + head0 + rows_ok) * VDIM
                     assert end <= QR * splits * H * VDIM
+
+
+def roles_value_wave_loads_fill_the_tile(rows):
+    """The role-split kernel's row loads: value wave d (d = 0..3) issues nine LDS-direct loads
+    per tile, load r taking chunk group r of token 8d + lane / 8 into block 4r + d: the same
+    placement as the two-stream form's four-wave stream."""
+    return dma_tile(4, rows)
+
+
+def test_roles_wave_assignment_covers_every_head_group_and_value_tile_once():
+    """Eight waves: wave w < 4 scores head group w; wave w >= 4 is value wave d = w - 4, which
+    loads token group d of every tile and accumulates value tiles 8d .. 8d + 7.  Waves w and
+    w + 4 share a SIMD, so every SIMD holds one wave of each role."""
+    assert sorted(w for w in range(8) if w < 4) == [0, 1, 2, 3]
+    assert sorted(w - 4 for w in range(8) if w >= 4) == [0, 1, 2, 3]
+    # the resolution loop strides by 512 threads: lane 0 of a wave always holds an entry index
+    # that is a multiple of 64 (its ballot covers two whole tiles)
+    for w in range(8):
+        for it in range(4):
+            assert (64 * w + 512 * it) % 64 == 0
+
+
+def test_roles_row_loads_and_operand_layout():
+    rng = np.random.default_rng(77)
+    rows = rng.integers(0, 2 ** 16, size=(TT, ROW_EL), dtype=np.uint16)
+    tile, hits = roles_value_wave_loads_fill_the_tile(rows)
+    assert (hits == 1).all()
+    # the value wave d reads value tiles 8d .. 8d + 7 with the transpose reads; together the
+    # four waves cover the 32 value tiles (512 dims) once
+    jj, qq = n_of >> 2, n_of & 3
+    tok = 4 * g_of + jj
+    voff = [chunk_byte(tok, 2 * vm + (qq >> 1)) + (qq & 1) * 8 for vm in range(4)]
+    covered = np.zeros(VDIM, dtype=np.int64)
+    for d in range(4):
+        for v in range(8):
+            vt = 8 * d + v
+            lo_addr = voff[vt & 3] + (vt >> 2) * 4 * BLOCK
+            lo, hi = tr16_read(tile, lo_addr), tr16_read(tile, lo_addr + 2 * BLOCK)
+            for L in range(64):
+                i, g = L & 15, L >> 4
+                assert np.array_equal(lo[L], rows[4 * g:4 * g + 4, 16 * vt + i])
+                assert np.array_equal(hi[L], rows[16 + 4 * g:16 + 4 * g + 4, 16 * vt + i])
+            covered[16 * vt:16 * vt + 16] += 1
+    assert (covered == 1).all()
+    # P^T crosses from score wave w, lane L, to every value wave's lane L unchanged: score lane
+    # (n, g) holds head n at tokens 4g..4g+3, 16+4g..16+4g+3 (its S^T accumulators), which are
+    # the k slots 8g..8g+7 of the B operand, and the V^T operand of the same lane group holds
+    # the same tokens in the same order (checked above), so the contraction pairs equal tokens
+    s_tokens = np.array([[(c >> 2) * 16 + g * 4 + (c & 3) for c in range(8)] for g in g_of])
+    v_tokens = np.array([[4 * g + c for c in range(4)] + [16 + 4 * g + c for c in range(4)] for g in g_of])
+    assert np.array_equal(s_tokens, v_tokens)
+
+
+@pytest.mark.parametrize("ntiles", list(range(0, 33)))
+def test_roles_schedule_has_no_slot_or_buffer_race(ntiles):
+    """Replays the role-split kernel's loop, interval by interval (an interval = the code
+    between two barriers), and checks what each role touches."""
+    slot_tile = {}          # ring slot -> tile whose loads last targeted it
+    in_flight = []          # tiles with loads outstanding, in issue order
+    landed = set()
+    pbuf_tile = {}          # P buffer -> tile whose P^T it holds
+    last_read = {}          # tile -> last interval in which a role reads its slot
+
+    def issue(T, interval):
+        s = T % ROLES_RING
+        prev = slot_tile.get(s)
+        if prev is not None:
+            # the previous tile of this slot was last read (V^T, interval prev + 1) before
+            # this interval began
+            assert last_read.get(prev, -1) < interval, (T, prev)
+            assert prev + 1 < interval
+        slot_tile[s] = T
+        in_flight.append(T)
+
+    # interval -1: before the first loop barrier (after the barrier that publishes rowix)
+    for T in range(min(2, ntiles)):
+        issue(T, -1)
+    for i in range(ntiles + 1):
+        # value waves: wait until at most one tile's loads are outstanding (CPT loads), or none
+        allowed = 1 if i + 1 < ntiles else 0
+        while len(in_flight) > allowed:
+            landed.add(in_flight.pop(0))
+        # ---- barrier i; interval i
+        touched_slots = []
+        if i + 2 < ntiles:
+            issue(i + 2, i)
+            touched_slots.append(("dma", (i + 2) % ROLES_RING))
+        if i < ntiles:                          # score waves: tile i
+            assert i in landed and slot_tile[i % ROLES_RING] == i
+            touched_slots.append(("k", i % ROLES_RING))
+            last_read[i] = i
+            pbuf_tile[i & 1] = i
+        if i >= 1:                              # value waves: tile i - 1
+            T = i - 1
+            assert T in landed and slot_tile[T % ROLES_RING] == T
+            assert pbuf_tile[T & 1] == T        # written in interval T, not yet overwritten
+            touched_slots.append(("v", T % ROLES_RING))
+            last_read[T] = i
+            if i < ntiles:
+                assert (i & 1) != (T & 1)       # score waves write the other P buffer meanwhile
+        slots = [s for _, s in touched_slots]
+        assert len(slots) == len(set(slots)), (i, touched_slots)
+    assert not in_flight
+    assert sorted(last_read) == list(range(ntiles))
