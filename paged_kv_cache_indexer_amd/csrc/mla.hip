@@ -5,24 +5,28 @@
 // normalised partial o (in o's dtype) and its lse, and an LSE-rescaling merge combines
 // them (TokenSpeed audit, two-stage split-KV decode).
 //
-// Work-group = two token streams of NW waves (one per SIMD per stream) for 16*NW heads of
-// one query row and one split of its selected rows; stream s takes tiles T with
-// T % 2 == s, and the streams' softmax states are merged through LDS at the end.  Each
-// wave owns 16 heads over the whole latent row:
-//   S^T[32 tokens x 16 heads] = K_tile . q^T       (bf16 MFMA 16x16x32: two 16-token
-//     M tiles x 18 steps of 32 latent dims, q^T resident in VGPRs)
-//   O^T[512 dims x 16 heads] += V^T . P^T           (bf16 MFMA 16x16x32: 32 M tiles of 16
-//     value dims, K = the tile's 32 tokens)
-// No partial sums cross waves, so a tile needs one barrier (the ring's).  Heads sit on the
-// N axis: the four lanes of a head (lane % 16) hold its running max / sums, and P^T is the
-// S^T accumulator itself rounded to bf16; lane group g = lane / 16 holds tokens 4g..4g+3
-// and 16+4g..16+4g+3, which are also its eight K slots of the PV product.  The V^T operand
-// is read straight from the token-major K tile with LDS transpose reads
-// (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of the
+// Two work-group forms share the tile layout, the row loads and the online softmax:
+//  * mla_roles_kernel (64 heads per work-group, used whenever H >= 64): eight waves in two
+//    roles.  Four score waves each keep q^T of 16 heads in VGPRs and compute
+//      S^T[32 tokens x 16 heads] = K_tile . q^T  (bf16 MFMA 16x16x32: two 16-token M tiles x 18
+//      steps of 32 latent dims)
+//    and the softmax; they hand P^T to four value waves through LDS.  Value wave d keeps O^T
+//    for value dims 128d..128d+127 of all 64 heads and computes
+//      O^T[128 dims x 64 heads] += V^T . P^T  (bf16 MFMA 16x16x32, K = the tile's 32 tokens),
+//    so each V^T operand read serves 64 heads.  Details at the kernel.
+//  * mla_decode_kernel<NW, 2> (16 to 48 heads): two token streams of NW waves (one per SIMD
+//    per stream) for 16*NW heads; stream s takes tiles T with T % 2 == s, and the streams'
+//    softmax states are merged through LDS at the end.  Each wave owns 16 heads over the
+//    whole latent row and computes both products itself.
+// In both, heads sit on the N axis of S^T: the four lanes of a head (lane % 16) hold its
+// running max / sums, and P^T is the S^T accumulator rounded to bf16; lane group g = lane / 16
+// holds tokens 4g..4g+3 and 16+4g..16+4g+3, which are also its eight K slots of the PV
+// product.  The V^T operand is read straight from the token-major K tile with LDS transpose
+// reads (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4 of the
 // 8-byte rows addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so no transposed copy is made.
-// Selected rows stream into a ring of four LDS tiles (each stream loads one tile ahead of
-// the one it computes) with LDS-direct loads (global_load_lds_dwordx4: lane i of a wave
-// instruction lands at M0 + 16 i); no VGPRs hold rows in flight.  A tile is stored as 1 KB
+// Selected rows stream into a ring of four LDS tiles with LDS-direct loads
+// (global_load_lds_dwordx4: lane i of a wave instruction lands at M0 + 16 i); no VGPRs hold
+// rows in flight.  A tile is stored as 1 KB
 // blocks of 8 tokens x 128 bytes (block = chunk group cg * 4 + token group), so one wave
 // instruction fetches eight whole 128-byte lines; the placement inside a block
 // (chunk_byte) keeps both operand reads free of LDS bank conflicts.
@@ -119,18 +123,40 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_u8* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// grid position -> (unit = query row x split, head block).  The head blocks of one unit
-// read the same rows; they are placed on one XCD (work-groups go round-robin over the 8
-// XCDs) so that the second reader finds the rows in that XCD's L2.
-__device__ __forceinline__ void mla_block_unit(int nhb, int& unit, int& hb) {
+// grid position -> (unit = query row x split, head block).  Work-groups go round robin over
+// the 8 XCDs, each with its own L2.  When the query rows split evenly over the XCDs (QR % 8 ==
+// 0), every work-group of one query row runs on XCD qr % 8: its head blocks read the same
+// selected rows and its splits the same q from that L2, and the merge of its split partials
+// (mla_merge_unit) runs there too.  Otherwise the head blocks of one unit share an XCD.
+__device__ __forceinline__ void mla_block_unit(int nhb, int splits, int& unit, int& hb) {
   const int x = blockIdx.x, G = gridDim.x;
-  if (G % (8 * nhb) == 0) {
+  const int per_qr = splits * nhb;
+  if (G % (8 * per_qr) == 0) {
+    const int xcd = x & 7, kk = x >> 3;
+    const int local = kk % per_qr;
+    hb = local % nhb;
+    unit = ((kk / per_qr) * 8 + xcd) * splits + local / nhb;
+  } else if (G % (8 * nhb) == 0) {
     const int xcd = x & 7, kk = x >> 3;
     hb = kk % nhb;
     unit = (kk / nhb) * 8 + xcd;
   } else {
     hb = x % nhb;
     unit = x / nhb;
+  }
+}
+
+// merge grid position -> (query row, head block of kMergeHeads): with QR % 8 == 0 the merge
+// of query row qr runs on XCD qr % 8, where the decode work-groups wrote its partials
+__device__ __forceinline__ void mla_merge_unit(int hblocks, int& qr, int& hblk) {
+  const int x = blockIdx.x, G = gridDim.x;
+  if (G % (8 * hblocks) == 0) {
+    const int xcd = x & 7, kk = x >> 3;
+    hblk = kk % hblocks;
+    qr = (kk / hblocks) * 8 + xcd;
+  } else {
+    qr = x / hblocks;
+    hblk = x - qr * hblocks;
   }
 }
 
@@ -161,7 +187,7 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   const int n = lane & 15, g = lane >> 4;
   const int nhb = (a.H + 16 * NW - 1) / (16 * NW);
   int unit, hb;
-  mla_block_unit(nhb, unit, hb);
+  mla_block_unit(nhb, a.splits, unit, hb);
   const int qr = unit / a.splits;
   const int split = unit - qr * a.splits;
   const int b = qr / a.Sq;
@@ -437,8 +463,18 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
 // Iteration i: score waves take tile i, value waves tile i-1, one barrier.  Ring slot i % 4
 // holds tile i from its load (issued in iteration i-2) until the value waves are done with it
 // (iteration i+1), so two tiles are always in flight.
+// Waves w and w + 4 of a work-group share a SIMD (measured placement), so each SIMD runs one
+// score and one value wave: 36 + 32 MFMAs 16x16x32 per tile.  Per tile and CU the LDS serves
+// 144 KB of K-operand reads (ds_read_b128, measured 250 B/clk per CU), 32 KB of V^T transpose
+// reads (ds_read_b64_tr_b16, measured 62.5 B/clk per CU) and 36 KB of row loads: about 1,400
+// LDS cycles against 1,088 MFMA cycles per SIMD.  The operand reads are kept ahead of their
+// MFMAs with scheduling barriers; left alone, the scheduler sinks each read next to its use.
+// Tried and slower: two 32-head score waves alone on their SIMDs (six waves; K read once per
+// 32 heads, but 72 score MFMAs and the softmax of 32 heads on one SIMD per tile), and a second
+// barrier that keeps the value MFMAs off the matrix cores until the score MFMAs are issued.
 constexpr int kRolesRing = 4;
-constexpr int kScoreRK = 2;     // K-operand read buffers of a score wave
+constexpr int kScoreRK = 4;     // K-operand read buffers of a score wave (reads 3 k-steps ahead)
+constexpr int kValueRV = 3;     // V^T operand buffers of a value wave (reads 2 value tiles ahead)
 
 __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   constexpr int NT = 512;
@@ -461,7 +497,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int nhb = (a.H + 63) / 64;
   int unit, hb;
-  mla_block_unit(nhb, unit, hb);
+  mla_block_unit(nhb, a.splits, unit, hb);
   const int qr = unit / a.splits;
   const int split = unit - qr * a.splits;
   const int b = qr / a.Sq;
@@ -548,6 +584,9 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
           }
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0[j % kScoreRK], qb[j], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1[j % kScoreRK], qb[j], s1, 0, 0, 0);
+          // keep the reads kScoreRK - 1 steps ahead: the scheduler would otherwise sink each
+          // read next to its MFMA and every MFMA would wait out a full LDS latency
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};   // tokens 4g+i, 16+4g+i
@@ -666,10 +705,22 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
     const int T = i - 1;
     const int pslot = T & 1;
     const lds_u8* tile = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((T % kRolesRing) * kTileBytes));
+    // ---- O^T += V^T . P^T over this wave's 8 value tiles, each read once for the 4 head groups
+    auto vop = [&](int v) {     // tokens 4g.. (first 8 bytes) and 16+4g.. (last 8 bytes)
+      const int vt = 8 * d + v;
+      const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4 * kBlockBytes;
+      const u32x2 lo = lds_read_tr16(p);
+      const u32x2 hi = lds_read_tr16(p + 2 * kBlockBytes);   // tokens + 16: two token groups on
+      return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    };
+    bf16x8 rv[kValueRV];
+#pragma unroll
+    for (int c = 0; c < kValueRV - 1; ++c) rv[c] = vop(c);
     bf16x8 pt[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) pt[h] = pbuf[pslot][h][lane];
     const u32x4 fl = *reinterpret_cast<const u32x4*>(&aflag[pslot][0]);
+    __builtin_amdgcn_sched_barrier(0);      // the first operand reads are in flight before any wait
     if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -680,25 +731,13 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
         }
       }
     }
-
-    // ---- O^T += V^T . P^T over this wave's 8 value tiles, each read once for the 4 head groups
-    auto vop = [&](int v) {     // tokens 4g.. (first 8 bytes) and 16+4g.. (last 8 bytes)
-      const int vt = 8 * d + v;
-      const lds_u8* p = tile + voff[vt & 3] + (vt >> 2) * 4 * kBlockBytes;
-      const u32x2 lo = lds_read_tr16(p);
-      const u32x2 hi = lds_read_tr16(p + 2 * kBlockBytes);   // tokens + 16: two token groups on
-      return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-    };
-    constexpr int RV = 3;       // operand reads in flight
-    bf16x8 rv[RV];
-#pragma unroll
-    for (int c = 0; c < RV - 1; ++c) rv[c] = vop(c);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      if (v + RV - 1 < 8) rv[(v + RV - 1) % RV] = vop(v + RV - 1);
+      if (v + kValueRV - 1 < 8) rv[(v + kValueRV - 1) % kValueRV] = vop(v + kValueRV - 1);
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        oacc[h][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[v % RV], pt[h], oacc[h][v], 0, 0, 0);
+        oacc[h][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rv[v % kValueRV], pt[h], oacc[h][v], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);    // reads stay kValueRV - 1 value tiles ahead
     }
   }
 
@@ -761,8 +800,9 @@ __device__ __forceinline__ void merge_add(float w, const u32x4& v0, const u32x4&
 template <int SMAX, bool F32>
 __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) {
   const int hblocks = (a.H + kMergeHeads - 1) / kMergeHeads;   // 1-D grid: query row x head block
-  const int qr = blockIdx.x / hblocks;
-  const int head = (blockIdx.x - qr * hblocks) * kMergeHeads + (threadIdx.x >> 6);
+  int qr, hblk;
+  mla_merge_unit(hblocks, qr, hblk);
+  const int head = hblk * kMergeHeads + (threadIdx.x >> 6);
   if (head >= a.H) return;
   const int S = a.splits;
   const int d = (threadIdx.x & 63) * 8;

@@ -153,12 +153,30 @@ def test_grid_addresses_in_bounds(B, Sq, H, k):
     G = splits * QR * nhb
     x = np.arange(G)
     # grid position -> (unit, head block)
-    if G % (8 * nhb) == 0:
+    per_qr = splits * nhb
+    if G % (8 * per_qr) == 0:
+        xcd, kk = x & 7, x >> 3
+        local = kk % per_qr
+        hb, unit = local % nhb, ((kk // per_qr) * 8 + xcd) * splits + local // nhb
+        assert ((unit // splits) % 8 == xcd).all()         # every work-group of query row qr on XCD qr % 8
+    elif G % (8 * nhb) == 0:
         xcd, kk = x & 7, x >> 3
         hb, unit = kk % nhb, (kk // nhb) * 8 + xcd
     else:
         hb, unit = x % nhb, x // nhb
     assert sorted(zip(unit.tolist(), hb.tolist())) == [(u, h) for u in range(splits * QR) for h in range(nhb)]
+    if splits > 1:
+        # the merge grid: query row x head block of 4 heads, query row qr on XCD qr % 8 when QR % 8 == 0
+        hblocks = -(-H // 4)
+        MG = hblocks * QR
+        mx = np.arange(MG)
+        if MG % (8 * hblocks) == 0:
+            mxcd, mkk = mx & 7, mx >> 3
+            mh, mq = mkk % hblocks, (mkk // hblocks) * 8 + mxcd
+            assert (mq % 8 == mxcd).all()
+        else:
+            mq, mh = mx // hblocks, mx % hblocks
+        assert sorted(zip(mq.tolist(), mh.tolist())) == [(q, h) for q in range(QR) for h in range(hblocks)]
     qr, split = unit // splits, unit % splits
     assert (qr < QR).all()
     e_begin = split * per
