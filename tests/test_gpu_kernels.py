@@ -341,6 +341,28 @@ def test_mla_against_oracle(H, k, L):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("H,o_dtype", [(80, torch.bfloat16), (192, torch.float32)])
+def test_mla_partial_head_blocks_and_query_rows_on_one_xcd(H, o_dtype):
+    """64-head work-groups with a partly used last head block (80 heads: its score waves 1-3
+    hold no real head) or three head blocks (192), at 8 query rows (every work-group of a
+    row and its merge on one XCD), 16 splits of 128 rows each, padded selections."""
+    B, k, L = 8, 2048, 3000
+    wl = synth.make_workload(synth.spec(2).scaled(B=B, L=L, mla_heads=H, topk=k))
+    rng = np.random.default_rng(H)
+    idx = np.full((B, 1, k), -1, dtype=np.int32)
+    for b in range(B):
+        n = k - 37 * b
+        idx[b, 0, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx), o_dtype=o_dtype)
+    o_ref = np.empty((B, 1, H, 512))
+    l_ref = np.empty((B, 1, H))
+    for b in range(B):
+        o_ref[b, 0], l_ref[b, 0] = o_mla.sparse_mla(wl.mla_q[b, 0], selected_rows(wl, b, idx[b, 0]), wl.scale)
+    check_attention(o, lse, o_ref, l_ref)
+    assert int(dw.err) == 0
+
+
 def test_mla_f32_output_and_empty_selection():
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=500, topk=64))
     idx = np.full((2, 1, 64), -1, dtype=np.int32)
