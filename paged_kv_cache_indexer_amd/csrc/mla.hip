@@ -531,15 +531,14 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
     const int w = wave;
     const int head = hb * 64 + w * 16 + n;
     const bool head_ok = head < a.H;
-    bf16x8 qb[18];              // q^T: lane (n, g) holds dims 32j + 8g .. +8 of head n
+    // q^T: lane (n, g) holds dims 32j + 8g .. +8 of head n.  A head past H reads head 0 instead
+    // (finite values; nothing of it is stored), so no select waits for these loads before the
+    // first barrier, which the value waves' first row loads wait behind.
+    bf16x8 qb[18];
     {
       const uint16_t* qp = a.q + ((int64_t)qr * a.H + (head_ok ? head : 0)) * kRowEl + g * 8;
 #pragma unroll
-      for (int j = 0; j < 18; ++j) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + j * 32);
-        if (!head_ok) v = bf16x8{};
-        qb[j] = v;
-      }
+      for (int j = 0; j < 18; ++j) qb[j] = *reinterpret_cast<const bf16x8*>(qp + j * 32);
     }
     int koff[2][2];             // K operand of M tile mt, k-step j: koff[j % 2][mt] + 4 blocks (j / 2)
 #pragma unroll
