@@ -363,6 +363,29 @@ def test_mla_partial_head_blocks_and_query_rows_on_one_xcd(H, o_dtype):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("B,k,L", [(2, 32, 500), (129, 100, 300)])
+def test_mla_single_split_writes_o_directly(B, k, L):
+    """Shapes whose split plan is one split (one tile per row; or 258 work-groups of 64 heads,
+    where a second split would add a round): the 64-head kernel writes o and lse itself,
+    with no partials and no merge."""
+    H = 128
+    assert dsa.dsa_sparse_mla_workspace_size(B, 1, H, k) == 0
+    wl = synth.make_workload(synth.spec(2).scaled(B=B, L=L, mla_heads=H, topk=k))
+    rng = np.random.default_rng(B + k)
+    idx = np.full((B, 1, k), -1, dtype=np.int32)
+    for b in range(B):
+        n = k - (b % 5)
+        idx[b, 0, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx))
+    o_ref = np.empty((B, 1, H, 512))
+    l_ref = np.empty((B, 1, H))
+    for b in range(B):
+        o_ref[b, 0], l_ref[b, 0] = o_mla.sparse_mla(wl.mla_q[b, 0], selected_rows(wl, b, idx[b, 0]), wl.scale)
+    check_attention(o, lse, o_ref, l_ref)
+    assert int(dw.err) == 0
+
+
 def test_mla_f32_output_and_empty_selection():
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=500, topk=64))
     idx = np.full((2, 1, 64), -1, dtype=np.int32)

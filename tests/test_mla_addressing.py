@@ -137,7 +137,8 @@ def split_plan(B, Sq, H, k):
 # (B, Sq, H, k): the workloads and the shapes the GPU parity tests launch
 GRIDS = [(32, 1, 128, 2048), (8, 4, 128, 2048), (66, 1, 128, 2048), (1, 1, 16, 256), (16, 1, 128, 2048),
          (4, 1, 16, 100), (3, 1, 32, 300), (2, 1, 48, 1000), (2, 1, 64, 2048), (2, 1, 128, 65536),
-         (4, 1, 128, 4096), (3, 4, 64, 2048), (8, 1, 80, 2048), (8, 1, 192, 2048)]
+         (4, 1, 128, 4096), (3, 4, 64, 2048), (8, 1, 80, 2048), (8, 1, 192, 2048),
+         (2, 1, 128, 32), (129, 1, 128, 100)]
 
 
 @pytest.mark.parametrize("B,Sq,H,k", GRIDS)
