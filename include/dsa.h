@@ -305,9 +305,11 @@ dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int
  *   ws     workspace of dsa_sparse_mla_workspace_size(B, Sq, H, k) bytes (16-byte aligned);
  *          NULL allowed when that size is 0.  Holds the split partials: lse as float32,
  *          o normalised in o_dtype.  Its contents are scratch between calls.
- * Supported: H a multiple of 16 (H > 32 runs 64-head work-groups), k <= 65536, at most
- * 2^24 (query row, 16-head group) pairs, and a split grid that fits one launch (fewer than
- * 2^32 work-items); beyond those limits the call returns DSA_ERR_UNSUPPORTED.
+ * Supported: H a multiple of 16 (H >= 64 runs 64-head work-groups of score and value waves;
+ * 32 and 48 heads run 32-head, 16 heads 16-head work-groups), k <= 65536, rows->num_rows
+ * < 2^31, at most 2^24 (query row, 16-head group) pairs, and a split grid that fits one
+ * launch (fewer than 2^32 work-items); beyond those limits the call returns
+ * DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_sparse_mla_workspace_size(int B, int Sq, int H, int k);
 dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx, const dsa_rows_t* rows,

@@ -107,6 +107,12 @@ def test_size_products_checked_in_64_bits():
     assert L.dsa_sparse_mla_decode(p, p, ctypes.byref(rows), 1 << 20, 64, 128, 2048, ctypes.c_float(0.1), p,
                                    _lib.DSA_BF16, p, None, 0, None, None) == _lib.DSA_ERR_UNSUPPORTED
     assert b"pairs" in L.dsa_last_error()
+    # the 64-head kernel keeps row indices as 32-bit in LDS: a row store of 2^31 rows is refused
+    big = _lib.dsa_rows_t()
+    big.base, big.row_bytes, big.num_rows = 16, 1152, 1 << 31
+    assert L.dsa_sparse_mla_decode(p, p, ctypes.byref(big), 1, 1, 128, 2048, ctypes.c_float(0.1), p,
+                                   _lib.DSA_BF16, p, None, 0, None, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert b"num_rows" in L.dsa_last_error()
     keys = _lib.dsa_rows_t()
     keys.base, keys.row_bytes, keys.num_rows = 16, 128, 64
     # Sq * H = 2^32 wraps to 0 in 32 bits
