@@ -74,6 +74,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// max over lanes l, l^16, l^32, l^48 (the four lanes of a head) with the row-swap permutes
+// (VALU; a shuffle through LDS would wait behind the tile's operand reads).  Each swap
+// pairs lane l with l^16 (v_permlane16_swap) or l^32 (v_permlane32_swap) across its two
+// results; lane check on the device: a probe of both swaps against l ^ 16 and l ^ 32.
+__device__ __forceinline__ float head_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 // Byte offset of 16-byte chunk c of token n inside a tile.  Token group tg = n / 8 and
 // chunk group cg = c / 8 select block cg * 4 + tg (1 KB, unpadded); inside it, chunk
 // cc = c % 8 of token m = n % 8 sits at 16-byte slot m * 8 + (cc ^ 2(m/2)).  One LDS-direct
@@ -603,8 +614,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
       float tmax = s[0];
 #pragma unroll
       for (int c = 1; c < 8; ++c) tmax = fmaxf(tmax, s[c]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;   // scale > 0 keeps the order
+      tmax = head_max4(tmax) * a.scale_log2;   // scale > 0 keeps the order
       const bool grow = tmax > m_used + kLazy || (m_used == -INFINITY && tmax > -INFINITY);
       uint32_t rescaled = 0;
       if (__builtin_amdgcn_ballot_w64(grow)) {
