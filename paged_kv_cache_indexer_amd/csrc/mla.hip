@@ -46,7 +46,7 @@ constexpr int kTileBytes = 36 * 1024;       // 36 blocks of 8 tokens x 128 bytes
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;
-constexpr int kMaxSplit = 1024;             // selected rows per split (row offsets kept in LDS)
+constexpr int kMaxSplit = 1152;             // selected rows of one work-group piece (row table in LDS)
 
 struct MlaArgs {
   const uint16_t* q;       // [QR, H, 576] bf16
@@ -55,11 +55,11 @@ struct MlaArgs {
   int Sq, H, k;
   int splits, per_split;   // per_split: entries per split (multiple of 32)
   float scale_log2;
-  void* o;                 // [QR, H, 512] (o_f32 ? float : bf16)   -- splits == 1
+  void* o;                 // [QR, H, 512] (o_f32 ? float : bf16)   -- written directly when splits == 1
   int o_f32;
-  float* lse;              // [QR, H]                                 -- splits == 1
-  void* part_o;            // [QR, splits, H, 512] in o's dtype, normalised   -- splits > 1
-  float* part_lse;         // [QR, splits, H]
+  float* lse;              // [QR, H]
+  void* part_o;            // split partials, 512 values per row in o's dtype, normalised:
+  float* part_lse;         //   [QR, splits, H] rows (split form) or the row-stream slots
   int32_t* err;
   // union form (query tokens folded into the head axis): entries of row qr past counts[qr]
   // are skipped; wave heads of query t = head / fold_h only see entries whose bit is set in
@@ -67,6 +67,10 @@ struct MlaArgs {
   const int32_t* counts;   // [QR] or null
   const uint32_t* member;  // or null
   int fold_h, fold_sq, mwords;
+  // row-stream form of the 64-head kernel (sk_groups > 0, split form otherwise): the
+  // sk_groups work-groups of each head block share its QR x sk_tpu tiles evenly; partials
+  // in nhb x (sk_groups + QR) slots of 64 rows (see mla_pieces)
+  int QR, sk_groups, sk_tpu;
 };
 
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -461,6 +465,67 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
   }
 }
 
+// A piece of a 64-head work-group's work: entries e_begin..e_end of query row qr's selection
+// for head block hb.  Its normalised o and lse go to rows orow0 + (head - 64 hb) of the
+// caller's o and lse (direct) or of the partial arrays.
+struct MlaPiece {
+  int qr, hb, e_begin, e_end;
+  int64_t orow0;
+  bool direct;
+};
+
+// The pieces of this work-group.  Split form: one piece, the (query row, split) of the grid
+// position.  Row-stream form (sk_groups = G > 0): the G work-groups of head block hb share
+// its QR x Tu tiles of 32 entries (row by row) evenly, work-group w taking tiles
+// [w T / G, (w + 1) T / G) of T = QR Tu.  The host picks this form only when a share is at
+// most one row's Tu tiles, so a work-group meets at most two rows: piece 0 writes partial
+// slot w, a second piece (which starts row r) slot G + r, among head block hb's G + QR slots
+// of 64 rows.  Work-group w of every head block runs on XCD w % 8 (round-robin placement),
+// so the head blocks read the same rows from one L2.
+__device__ __forceinline__ int mla_pieces(const MlaArgs& a, int nhb, MlaPiece (&pc)[2]) {
+  if (a.sk_groups == 0) {
+    int unit, hb;
+    mla_block_unit(nhb, a.splits, unit, hb);
+    const int qr = unit / a.splits;
+    const int split = unit - qr * a.splits;
+    const int kq = a.counts ? max(0, min(a.k, a.counts[qr])) : a.k;
+    // with a per-row count the row's entries are spread evenly over its splits (never more
+    // per split than the host sized for)
+    const int per =
+        a.counts ? min(a.per_split, (((kq + a.splits - 1) / a.splits) + kTT - 1) / kTT * kTT) : a.per_split;
+    pc[0].qr = qr;
+    pc[0].hb = hb;
+    pc[0].e_begin = split * per;
+    pc[0].e_end = min(pc[0].e_begin + per, kq);
+    pc[0].direct = a.splits == 1;
+    pc[0].orow0 = (pc[0].direct ? (int64_t)qr * a.H : ((int64_t)qr * a.splits + split) * a.H) + hb * 64;
+    return 1;
+  }
+  const int G = a.sk_groups, Tu = a.sk_tpu;
+  const int x = blockIdx.x, xcd = x & 7, kk = x >> 3;
+  const int hb = kk % nhb;
+  const int w = (kk / nhb) * 8 + xcd;
+  const int64_t T = (int64_t)a.QR * Tu;
+  const int64_t start = (int64_t)w * T / G, end = (int64_t)(w + 1) * T / G;
+  const int r0 = (int)(start / Tu);
+  const int64_t slots = (int64_t)hb * (G + a.QR);
+  pc[0].qr = r0;
+  pc[0].hb = hb;
+  pc[0].e_begin = (int)(start - (int64_t)r0 * Tu) * kTT;
+  pc[0].e_end = min((int)min(end - (int64_t)r0 * Tu, (int64_t)Tu) * kTT, a.k);
+  pc[0].direct = false;
+  pc[0].orow0 = (slots + w) * 64;
+  if (end <= (int64_t)(r0 + 1) * Tu) return 1;
+  const int r1 = r0 + 1;
+  pc[1].qr = r1;
+  pc[1].hb = hb;
+  pc[1].e_begin = 0;
+  pc[1].e_end = min((int)(end - (int64_t)r1 * Tu) * kTT, a.k);
+  pc[1].direct = false;
+  pc[1].orow0 = (slots + G + r1) * 64;
+  return 2;
+}
+
 // ---- role-split form: 64 heads per work-group, eight waves in two roles
 // Score waves 0-3: wave w keeps q^T of heads 16w..16w+15 in VGPRs and computes
 //   S^T[32 tokens x 16 heads] = K_tile . q^T exactly as the two-stream form does, then the
@@ -507,16 +572,13 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int nhb = (a.H + 63) / 64;
-  int unit, hb;
-  mla_block_unit(nhb, a.splits, unit, hb);
-  const int qr = unit / a.splits;
-  const int split = unit - qr * a.splits;
-  const int b = qr / a.Sq;
+  MlaPiece pcs[2];
+  const int npc = mla_pieces(a, nhb, pcs);
 
-  const int kq = a.counts ? max(0, min(a.k, a.counts[qr])) : a.k;
-  const int per = a.counts ? min(a.per_split, (((kq + a.splits - 1) / a.splits) + kTT - 1) / kTT * kTT) : a.per_split;
-  const int e_begin = split * per;
-  const int e_end = min(e_begin + per, kq);
+  for (int pi = 0; pi < npc; ++pi) {
+  const MlaPiece pc = pi == 0 ? pcs[0] : pcs[1];
+  const int qr = pc.qr, hb = pc.hb, e_begin = pc.e_begin, e_end = pc.e_end;
+  const int b = qr / a.Sq;
   const int ntiles = e_end > e_begin ? (e_end - e_begin + kTT - 1) / kTT : 0;
   const int32_t* idx = a.idx + (int64_t)qr * a.k;
 
@@ -648,14 +710,9 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
     lr_tot += __shfl_xor(lr_tot, 32);
     if (g == 0) xinv[w][n] = (lr_tot > 0.0f) ? 1.0f / lr_tot : 0.0f;
     const float lse = (l_tot > 0.0f) ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
-    if (g == 0 && head_ok) {
-      if (a.splits == 1)
-        a.lse[(int64_t)qr * a.H + head] = lse;
-      else
-        a.part_lse[((int64_t)qr * a.splits + split) * a.H + head] = lse;
-    }
+    if (g == 0 && head_ok) (pc.direct ? a.lse : a.part_lse)[pc.orow0 + w * 16 + n] = lse;
     __syncthreads();            // xinv ready
-    return;
+    continue;
   }
 
   // ================================================================== value wave
@@ -751,16 +808,13 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   }
 
   __syncthreads();              // xinv ready
-  const bool direct = a.splits == 1;
-  void* dst = direct ? a.o : a.part_o;
+  void* dst = pc.direct ? a.o : a.part_o;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const int head = hb * 64 + h * 16 + n;
     if (head >= a.H) continue;
     const float inv = xinv[h][n];
-    const int64_t obase =
-        (direct ? ((int64_t)qr * a.H + head) : ((((int64_t)qr * a.splits + split) * a.H + head))) * kVDim +
-        d * 128 + g * 4;
+    const int64_t obase = (pc.orow0 + h * 16 + n) * kVDim + d * 128 + g * 4;
     if (a.o_f32) {
 #pragma unroll
       for (int v = 0; v < 8; ++v)
@@ -773,6 +827,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
                   pack_bf16x2(oacc[h][v].z * inv, oacc[h][v].w * inv)};
     }
   }
+  }                             // pieces
 }
 
 // merge of split partials: 64 threads per (query row, head), 8 value dims per thread.  With
@@ -813,11 +868,32 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
   mla_merge_unit(hblocks, qr, hblk);
   const int head = hblk * kMergeHeads + (threadIdx.x >> 6);
   if (head >= a.H) return;
-  const int S = a.splits;
   const int d = (threadIdx.x & 63) * 8;
-  const float* pl = a.part_lse + (int64_t)qr * S * a.H + head;
-  const int64_t pbase = ((int64_t)qr * S * a.H + head) * kVDim + d;   // split s adds s * H * 512
-  const int64_t pstep = (int64_t)a.H * kVDim;
+  // partial row of this head's s-th partial: split form, split s of row qr; row-stream
+  // form, the pieces of the work-groups w0.. whose tile ranges meet row qr (mla_pieces)
+  int S;
+  int64_t srow0 = 0, sstep = 0;       // split form: row srow0 + s * sstep
+  int sk_w0 = 0;
+  int64_t sk_base = 0, sk_T = 0, sk_x0 = 0;
+  if (a.sk_groups == 0) {
+    S = a.splits;
+    srow0 = (int64_t)qr * S * a.H + head;
+    sstep = a.H;
+  } else {
+    const int G = a.sk_groups, Tu = a.sk_tpu;
+    sk_T = (int64_t)a.QR * Tu;
+    sk_x0 = (int64_t)qr * Tu;
+    const int64_t x1 = sk_x0 + Tu - 1;
+    sk_w0 = (int)(((sk_x0 + 1) * G - 1) / sk_T);        // the work-group holding tile x0
+    S = (int)(((x1 + 1) * G - 1) / sk_T) - sk_w0 + 1;
+    sk_base = (int64_t)(head >> 6) * (G + a.QR);
+  }
+  auto prow = [&](int s) -> int64_t {
+    if (a.sk_groups == 0) return srow0 + s * sstep;
+    const int G = a.sk_groups, w = sk_w0 + s;
+    const int64_t slot = ((int64_t)w * sk_T / G < sk_x0) ? (int64_t)G + qr : (int64_t)w;
+    return (sk_base + slot) * 64 + (head & 63);
+  };
   float mx = -INFINITY, wsum = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (SMAX > 0) {
@@ -829,8 +905,9 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
       v0[s] = u32x4{};
       v1[s] = u32x4{};
       if (s < S) {
-        lv[s] = pl[(int64_t)s * a.H];
-        merge_load<F32>(a.part_o, pbase + s * pstep, v0[s], v1[s]);
+        const int64_t r = prow(s);
+        lv[s] = a.part_lse[r];
+        merge_load<F32>(a.part_o, r * kVDim + d, v0[s], v1[s]);
       }
     }
 #pragma unroll
@@ -844,14 +921,15 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
       }
     }
   } else {
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * a.H]);
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[prow(s)]);
     if (mx > -INFINITY) {
       for (int s = 0; s < S; ++s) {
-        const float l = pl[(int64_t)s * a.H];
+        const int64_t r = prow(s);
+        const float l = a.part_lse[r];
         const float w = (l == -INFINITY) ? 0.0f : __expf(l - mx);
         wsum += w;
         u32x4 v0 = u32x4{}, v1 = u32x4{};
-        merge_load<F32>(a.part_o, pbase + s * pstep, v0, v1);
+        merge_load<F32>(a.part_o, r * kVDim + d, v0, v1);
         merge_add<F32>(w, v0, v1, acc);
       }
     }
@@ -894,16 +972,32 @@ static int mla_waves(int H) { return H >= 64 ? 4 : (H > 16 ? 2 : 1); }
 // tile-times, F being the per-work-group start-up and finish in tile-times (≈ 8: 18.8 µs for
 // a one-tile work-group against 1.74 µs per further tile).  The plan takes the split count
 // with the least such estimate (ties: fewer splits, fewer partials), from the fewest that
-// keep a split within kMaxSplit rows up to four times the count that covers the CUs.  With
-// 264 work-groups at 2 splits, a 66-row batch ran a second round of 8; 3 splits make two full
-// rounds of shorter work-groups.
+// keep a split within kMaxSplitRows rows up to four times the count that covers the CUs.
+// With 264 work-groups at 2 splits, a 66-row batch ran a second round of 8; 3 splits make
+// two full rounds of shorter work-groups.
+// The 64-head kernel can instead share each head block's tiles evenly over a fixed set of
+// work-groups (the row-stream form, mla_pieces): one round of F + tiles per work-group, plus
+// a second start-up (≈ kPieceStartTiles) where a share crosses into a second row.  It is
+// taken when its estimate is lower, a share is at most one row and fits the LDS row table,
+// and the rows carry no per-row counts (the union form keeps splits).
 constexpr int kSplitStartTiles = 8;
-static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_split) {
-  const int wg_heads = 16 * mla_waves(H);
-  const int64_t wgs = (int64_t)B * Sq * ((H + wg_heads - 1) / wg_heads);
+constexpr int kPieceStartTiles = 4;
+constexpr int kMaxSplitRows = 1024;         // rows per split of the split form
+
+struct MlaPlan {
+  int splits = 1, per_split = 0;
+  int sk_groups = 0, sk_tpu = 0;            // row-stream form when sk_groups > 0
+  int sk_max_parts = 0;                     // most partials one (row, head) gets in that form
+};
+
+static MlaPlan mla_plan(int B, int Sq, int H, int k, bool row_stream) {
+  MlaPlan p;
+  const int nhb = (H + 16 * mla_waves(H) - 1) / (16 * mla_waves(H));
+  const int64_t QR = (int64_t)B * Sq;
+  const int64_t wgs = QR * nhb;
   const int tiles = (k + kTT - 1) / kTT;
   const int64_t cus = device_cus();
-  const int min_s = (tiles + kMaxSplit / kTT - 1) / (kMaxSplit / kTT);
+  const int min_s = (tiles + kMaxSplitRows / kTT - 1) / (kMaxSplitRows / kTT);
   const int cover = (int)std::min<int64_t>(tiles, (cus + wgs - 1) / wgs);
   const int max_s = std::max(min_s, std::min(tiles, 4 * std::max(cover, 1)));
   int s = min_s;
@@ -917,19 +1011,45 @@ static void mla_split_plan(int B, int Sq, int H, int k, int& splits, int& per_sp
     }
   }
   const int tps = (tiles + s - 1) / s;
-  per_split = tps * kTT;
-  splits = (k + per_split - 1) / per_split;
-  if (splits < 1) splits = 1;
+  p.per_split = tps * kTT;
+  p.splits = std::max(1, (k + p.per_split - 1) / p.per_split);
+  if (row_stream && mla_waves(H) == 4) {
+    const int64_t G = (cus / nhb) / 8 * 8;  // work-groups per head block, whole XCD rounds
+    const int64_t T = QR * tiles;
+    if (G >= 8 && T >= G && QR < ((int64_t)1 << 24)) {
+      const int64_t tpw = (T + G - 1) / G;
+      if (tpw <= tiles && tpw * kTT <= kMaxSplit) {
+        const int64_t cost = kSplitStartTiles + tpw + (tpw < tiles ? kPieceStartTiles : 0);
+        if (cost < best) {
+          p.sk_groups = (int)G;
+          p.sk_tpu = tiles;
+          const int64_t tmin = T / G;       // every share holds at least this many tiles
+          p.sk_max_parts = (int)((tiles + tmin - 1) / tmin + 1);
+        }
+      }
+    }
+  }
+  return p;
+}
+
+// bytes of split partials the plan writes: float32 lse, then o in float32 (the larger dtype)
+static size_t mla_workspace_bytes(int B, int Sq, int H, int k, bool row_stream) {
+  if (B <= 0 || Sq <= 0 || H <= 0 || k <= 0) return 0;
+  const MlaPlan p = mla_plan(B, Sq, H, k, row_stream);
+  size_t rows;
+  if (p.sk_groups > 0)
+    rows = (size_t)((H + 63) / 64) * (p.sk_groups + (size_t)B * Sq) * 64;
+  else if (p.splits > 1)
+    rows = (size_t)B * Sq * p.splits * H;
+  else
+    return 0;
+  return rows * (kVDim + 1) * sizeof(float);
 }
 
 }  // namespace dsa
 
 extern "C" size_t dsa_sparse_mla_workspace_size(int B, int Sq, int H, int k) {
-  if (B <= 0 || Sq <= 0 || H <= 0 || k <= 0) return 0;
-  int splits, per;
-  dsa::mla_split_plan(B, Sq, H, k, splits, per);
-  if (splits <= 1) return 0;
-  return (size_t)B * Sq * splits * H * (dsa::kVDim + 1) * sizeof(float);
+  return dsa::mla_workspace_bytes(B, Sq, H, k, true);
 }
 
 namespace dsa {
@@ -952,7 +1072,7 @@ extern "C" dsa_status_t dsa_sparse_mla_decode(const void* q, const int32_t* idx,
 
 extern "C" size_t dsa_sparse_mla_union_workspace_size(int B, int Sq, int H, int U) {
   if (B <= 0 || Sq <= 0 || H <= 0 || U <= 0 || (int64_t)Sq * H > (1 << 20)) return 0;
-  return dsa_sparse_mla_workspace_size(B, 1, Sq * H, U);
+  return dsa::mla_workspace_bytes(B, 1, Sq * H, U, false);
 }
 
 extern "C" dsa_status_t dsa_sparse_mla_decode_union(const void* q, const int32_t* uni, const int32_t* count,
@@ -994,16 +1114,17 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   DSA_CHECK_SUPPORTED(rows->num_rows < ((int64_t)1 << 31), "dsa_sparse_mla_decode: num_rows must be below 2^31");
   DSA_CHECK_SUPPORTED((int64_t)B * Sq * ((H + 15) / 16) <= (1 << 24),
                       "dsa_sparse_mla_decode: more than 2^24 (query row, 16-head group) pairs");
-  int splits, per;
-  mla_split_plan(B, Sq, H, k, splits, per);
-  {
-    // the launch's work-items (blocks x threads) must fit the 32-bit grid size
-    const int nw_ = mla_waves(H);
-    const int64_t blocks = (int64_t)splits * B * Sq * ((H + 16 * nw_ - 1) / (16 * nw_));
-    DSA_CHECK_SUPPORTED(blocks * 128 * nw_ < ((int64_t)1 << 32),
-                        "dsa_sparse_mla_decode: %lld work-groups exceed one launch", (long long)blocks);
-  }
-  const size_t need = dsa_sparse_mla_workspace_size(B, Sq, H, k);
+  const bool row_stream = un.counts == nullptr;
+  const MlaPlan plan = mla_plan(B, Sq, H, k, row_stream);
+  const int splits = plan.splits;
+  const int QR = B * Sq;
+  const int nw = mla_waves(H);
+  const int nhb = (H + 16 * nw - 1) / (16 * nw);
+  const int64_t blocks = plan.sk_groups > 0 ? (int64_t)nhb * plan.sk_groups : (int64_t)splits * QR * nhb;
+  // the launch's work-items (blocks x threads) must fit the 32-bit grid size
+  DSA_CHECK_SUPPORTED(blocks * 128 * nw < ((int64_t)1 << 32),
+                      "dsa_sparse_mla_decode: %lld work-groups exceed one launch", (long long)blocks);
+  const size_t need = mla_workspace_bytes(B, Sq, H, k, row_stream);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) {
     set_last_error("dsa_sparse_mla_decode: workspace %zu < %zu bytes", ws_bytes, need);
     return DSA_ERR_WORKSPACE;
@@ -1016,7 +1137,7 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   a.H = H;
   a.k = k;
   a.splits = splits;
-  a.per_split = per;
+  a.per_split = plan.per_split;
   a.scale_log2 = scale * kLog2e;
   a.o = o;
   a.o_f32 = (o_dtype == DSA_F32);
@@ -1026,14 +1147,17 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   a.fold_h = un.fold_h;
   a.fold_sq = un.fold_sq;
   a.mwords = un.mwords;
-  if (splits > 1) {
+  a.QR = QR;
+  a.sk_groups = plan.sk_groups;
+  a.sk_tpu = plan.sk_tpu;
+  const bool merged = plan.sk_groups > 0 || splits > 1;
+  if (merged) {
+    const size_t part_rows = plan.sk_groups > 0 ? (size_t)nhb * (plan.sk_groups + (size_t)QR) * 64
+                                                : (size_t)QR * splits * H;
     a.part_lse = static_cast<float*>(ws);
-    a.part_o = a.part_lse + (size_t)B * Sq * splits * H;
+    a.part_o = a.part_lse + part_rows;
   }
-  const int QR = B * Sq;
-  const int nw = mla_waves(H);
-  const int nhb = (H + 16 * nw - 1) / (16 * nw);
-  const dim3 grid(splits * QR * nhb);
+  const dim3 grid((unsigned)blocks);
   if (nw == 4)
     DSA_LAUNCH(mla_roles_kernel, grid, dim3(512), 0, stream, a);
   else if (nw == 2)
@@ -1041,13 +1165,14 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   else
     DSA_LAUNCH((mla_decode_kernel<1, 2>), grid, dim3(128), 0, stream, a);
   dsa_status_t st = launch_status("dsa_sparse_mla_decode");
-  if (st != DSA_OK || splits == 1) return st;
+  if (st != DSA_OK || !merged) return st;
   const dim3 mgrid((unsigned)(((H + kMergeHeads - 1) / kMergeHeads) * QR));
   const dim3 mblock(64 * kMergeHeads);
+  const int parts = plan.sk_groups > 0 ? plan.sk_max_parts : splits;
   // (the unrolled fp32 variant needs four times the registers, so fp32 keeps the loop)
   if (a.o_f32)
     DSA_LAUNCH((mla_merge_kernel<0, true>), mgrid, mblock, 0, stream, a);
-  else if (splits <= kMergeUnrolled)
+  else if (parts <= kMergeUnrolled)
     DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false>), mgrid, mblock, 0, stream, a);
   else
     DSA_LAUNCH((mla_merge_kernel<0, false>), mgrid, mblock, 0, stream, a);

@@ -386,6 +386,37 @@ def test_mla_single_split_writes_o_directly(B, k, L):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("cfg,B,H,k,L,o_dtype", [(2, 66, 128, 2048, 2600, torch.bfloat16),
+                                                  (2, 50, 128, 2048, 2300, torch.float32),
+                                                  (2, 100, 128, 1000, 1500, torch.bfloat16),
+                                                  (3, 13, 128, 2048, 2200, torch.bfloat16),
+                                                  (2, 70, 80, 1500, 1700, torch.bfloat16),
+                                                  (2, 66, 64, 2048, 2100, torch.bfloat16)])
+def test_mla_row_stream_form_against_oracle(cfg, B, H, k, L, o_dtype):
+    """Batches whose split plan would leave a second, partly empty round take the row-stream
+    form: each head block's tiles shared evenly by a fixed set of work-groups, a share meeting
+    up to two rows.  Every (row, head) against the oracle, padded selections included."""
+    from tests.test_mla_addressing import mla_plan
+    wl = synth.make_workload(synth.spec(cfg).scaled(B=B, L=L, mla_heads=H, topk=k))
+    Sq = wl.Sq
+    assert mla_plan(B, Sq, H, k)[2] > 0                   # the row-stream form is the one launched
+    rng = np.random.default_rng(B + H + k)
+    idx = np.full((B, Sq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(Sq):
+            n = k - ((b * 3 + t) % 7) * 5
+            idx[b, t, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx), o_dtype=o_dtype)
+    o_ref = np.empty((B, Sq, H, 512))
+    l_ref = np.empty((B, Sq, H))
+    for b in range(B):
+        for t in range(Sq):
+            o_ref[b, t], l_ref[b, t] = o_mla.sparse_mla(wl.mla_q[b, t], selected_rows(wl, b, idx[b, t]), wl.scale)
+    check_attention(o, lse, o_ref, l_ref)
+    assert int(dw.err) == 0
+
+
 def test_mla_f32_output_and_empty_selection():
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=500, topk=64))
     idx = np.full((2, 1, 64), -1, dtype=np.int32)

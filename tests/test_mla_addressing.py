@@ -33,7 +33,8 @@ TILE_BYTES = 36 * 1024
 BLOCK = 1024
 NS = 2                                   # token streams per work-group
 RING_OF = {1: NS * 2, 2: NS * 2, 4: NS * 2}   # RING = NS * (PD + 1), PD = 1 for two streams
-KMAXSPLIT = 1024
+KMAXSPLIT = 1152                         # rows of one piece the LDS row table holds
+KMAXSPLIT_ROWS = 1024                    # rows per split of the split form
 ROLES_RING = 4                           # mla_roles_kernel: tile T in slot T % 4
 
 lanes = np.arange(64)
@@ -124,14 +125,11 @@ def test_operand_reads_stay_in_the_tile_and_return_the_intended_elements(NW):
 
 
 def split_plan(B, Sq, H, k):
-    """Splits the library picks, read back from its workspace size (the kernel launches the
-    same plan)."""
-    ws = _lib.load().dsa_sparse_mla_workspace_size(B, Sq, H, k)
-    if ws == 0:
-        return 1
-    s = ws // (B * Sq * H * (VDIM + 1) * 4)
-    assert s * B * Sq * H * (VDIM + 1) * 4 == ws
-    return int(s)
+    """Splits of the split form the library launches (checked against its workspace size by
+    test_row_stream_plan_matches_the_library_and_covers_every_entry_once), or None when it
+    launches the row-stream form (covered by the row-stream tests below)."""
+    splits, _, G, _ = mla_plan(B, Sq, H, k)
+    return None if G else splits
 
 
 # (B, Sq, H, k): the workloads and the shapes the GPU parity tests launch
@@ -147,9 +145,11 @@ def test_grid_addresses_in_bounds(B, Sq, H, k):
     RING = ROLES_RING if nw == 4 else RING_OF[nw]
     QR = B * Sq
     splits = split_plan(B, Sq, H, k)
+    if splits is None:
+        return
     tiles = -(-k // TT)
     per = -(-tiles // splits) * TT
-    assert -(-k // per) == splits and per <= KMAXSPLIT
+    assert -(-k // per) == splits and per <= KMAXSPLIT_ROWS
     nhb = -(-H // (16 * nw))
     G = splits * QR * nhb
     x = np.arange(G)
@@ -222,6 +222,8 @@ def test_output_rows_written_inside_o_or_the_partials(B, Sq, H, k):
     nw = 4 if H >= 64 else (2 if H > 16 else 1)
     QR = B * Sq
     splits = split_plan(B, Sq, H, k)
+    if splits is None:
+        return
     nhb = -(-H // (16 * nw))
     for hb in range(nhb):
         for ws in range(nw):
@@ -340,3 +342,121 @@ def test_roles_schedule_has_no_slot_or_buffer_race(ntiles):
         assert len(slots) == len(set(slots)), (i, touched_slots)
     assert not in_flight
     assert sorted(last_read) == list(range(ntiles))
+
+
+# ------------------------------------------------------------------ row-stream form
+CUS = 256
+SPLIT_START, PIECE_START = 8, 4
+
+
+def mla_plan(B, Sq, H, k, row_stream=True, cus=CUS):
+    """The host plan restated: (splits, per_split, sk_groups, sk_max_parts)."""
+    nw = 4 if H >= 64 else (2 if H > 16 else 1)
+    nhb = -(-H // (16 * nw))
+    QR = B * Sq
+    wgs = QR * nhb
+    tiles = -(-k // TT)
+    min_s = -(-tiles // (KMAXSPLIT_ROWS // TT))
+    cover = min(tiles, -(-cus // wgs))
+    max_s = max(min_s, min(tiles, 4 * max(cover, 1)))
+    best, s = None, min_s
+    for c in range(min_s, max_s + 1):
+        cost = -(-(wgs * c) // cus) * (SPLIT_START + -(-tiles // c))
+        if best is None or cost < best:
+            best, s = cost, c
+    per = -(-tiles // s) * TT
+    splits = max(1, -(-k // per))
+    sk = parts = 0
+    if row_stream and nw == 4:
+        G = (cus // nhb) // 8 * 8
+        T = QR * tiles
+        if G >= 8 and T >= G:
+            tpw = -(-T // G)
+            if tpw <= tiles and tpw * TT <= KMAXSPLIT:
+                cost = SPLIT_START + tpw + (PIECE_START if tpw < tiles else 0)
+                if cost < best:
+                    sk = G
+                    tmin = T // G
+                    parts = -(-tiles // tmin) + 1
+    return splits, per, sk, parts
+
+
+def sk_pieces(QR, H, k, G):
+    """mla_pieces of every work-group of the row-stream launch: list of (x, qr, hb, e0, e1, slot)."""
+    nhb = -(-H // 64)
+    Tu = -(-k // TT)
+    T = QR * Tu
+    out = []
+    for x in range(nhb * G):
+        xcd, kk = x & 7, x >> 3
+        hb, w = kk % nhb, (kk // nhb) * 8 + xcd
+        start, end = w * T // G, (w + 1) * T // G
+        r0 = start // Tu
+        slots = hb * (G + QR)
+        out.append((x, r0, hb, (start - r0 * Tu) * TT, min(min(end - r0 * Tu, Tu) * TT, k), slots + w))
+        if end > (r0 + 1) * Tu:
+            r1 = r0 + 1
+            out.append((x, r1, hb, 0, min((end - r1 * Tu) * TT, k), slots + G + r1))
+            assert end <= (r1 + 1) * Tu            # never a third row
+    return out
+
+
+def sk_merge_rows(QR, H, k, G, qr, head):
+    """Partial rows the merge reads for (qr, head) in the row-stream form."""
+    Tu = -(-k // TT)
+    T = QR * Tu
+    x0, x1 = qr * Tu, qr * Tu + Tu - 1
+    w0 = ((x0 + 1) * G - 1) // T
+    S = ((x1 + 1) * G - 1) // T - w0 + 1
+    base = (head >> 6) * (G + QR)
+    rows = []
+    for s in range(S):
+        w = w0 + s
+        slot = G + qr if w * T // G < x0 else w
+        rows.append((base + slot) * 64 + (head & 63))
+    return rows
+
+
+@pytest.mark.parametrize("B,Sq,H,k", [(66, 1, 128, 2048), (50, 1, 128, 2048), (100, 1, 128, 1000),
+                                       (13, 4, 128, 2048), (70, 1, 80, 1500), (66, 1, 64, 2048),
+                                       (40, 1, 128, 2048), (60, 1, 192, 2048)])
+def test_row_stream_plan_matches_the_library_and_covers_every_entry_once(B, Sq, H, k):
+    splits, per, G, parts = mla_plan(B, Sq, H, k)
+    # the library's workspace size follows the same plan (256 CUs when no device is present)
+    nhb = -(-H // 64)
+    QR = B * Sq
+    want_ws = (nhb * (G + QR) * 64 if G else (QR * splits * H if splits > 1 else 0)) * (VDIM + 1) * 4
+    assert _lib.load().dsa_sparse_mla_workspace_size(B, Sq, H, k) == want_ws
+    if not G:
+        return
+    pcs = sk_pieces(QR, H, k, G)
+    per_wg = {}
+    for x, qr, hb, e0, e1, slot in pcs:
+        per_wg.setdefault(x, []).append((qr, hb, e0, e1, slot))
+        assert 0 <= e0 < e1 <= k and e1 - e0 <= KMAXSPLIT
+        assert 0 <= qr < QR and 0 <= slot < nhb * (G + QR)
+    assert len(per_wg) == nhb * G and all(len(v) <= 2 for v in per_wg.values())
+    slots = [p[5] for p in pcs]
+    assert len(slots) == len(set(slots))       # every piece has its own partial slot
+    for hb in range(nhb):
+        for qr in range(QR):
+            segs = sorted((e0, e1) for _, r, h, e0, e1, _ in pcs if r == qr and h == hb)
+            pos = 0
+            for e0, e1 in segs:                 # the row's entries, each exactly once
+                assert e0 == pos
+                pos = e1
+            assert pos == k
+            mine = sorted(slot * 64 + h16 for _, r, h, _, _, slot in pcs if r == qr and h == hb
+                          for h16 in (0,))
+            for head in (hb * 64, min(H, hb * 64 + 64) - 1):
+                rows = sk_merge_rows(QR, H, k, G, qr, head)
+                assert len(rows) <= parts
+                assert sorted(r - (head & 63) for r in rows) == mine
+
+
+def test_row_stream_taken_for_the_66_row_share_and_not_for_the_decode_batch():
+    assert mla_plan(66, 1, 128, 2048)[2] == 128       # rank-0 share: one round of 128 + 128
+    assert mla_plan(32, 1, 128, 2048)[2] == 0         # B=32: 4 splits already fill one round
+    assert mla_plan(8, 4, 128, 2048)[2] == 0          # MTP verify: the same
+    assert mla_plan(66, 1, 128, 2048, row_stream=False)[2] == 0
+    assert mla_plan(66, 1, 48, 2048)[2] == 0          # 32-head work-groups keep splits
