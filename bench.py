@@ -185,7 +185,7 @@ ENTRY_KERNELS = {
                             ["indexer.hip", "topk_wave.h"]),
     "topk": (["dsa::topk_wave_kernel", "dsa::topk_select_kernel"], ["topk.hip", "topk_wave.h"]),
     "topk_select": (["dsa::topk_select_kernel"], ["topk.hip", "topk_wave.h"]),
-    "mla": (["dsa::mla_roles_kernel", "void dsa::mla_merge_kernel<"], ["mla.hip"]),
+    "mla": (["void dsa::mla_roles_kernel<", "void dsa::mla_merge_kernel<"], ["mla.hip"]),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0   # counter KiB -> bytes/1024, from a 256 MiB device copy
 

@@ -482,8 +482,9 @@ struct MlaPiece {
 // slot w, a second piece (which starts row r) slot G + r, among head block hb's G + QR slots
 // of 64 rows.  Work-group w of every head block runs on XCD w % 8 (round-robin placement),
 // so the head blocks read the same rows from one L2.
+template <bool SK>
 __device__ __forceinline__ int mla_pieces(const MlaArgs& a, int nhb, MlaPiece (&pc)[2]) {
-  if (a.sk_groups == 0) {
+  if constexpr (!SK) {
     int unit, hb;
     mla_block_unit(nhb, a.splits, unit, hb);
     const int qr = unit / a.splits;
@@ -500,7 +501,7 @@ __device__ __forceinline__ int mla_pieces(const MlaArgs& a, int nhb, MlaPiece (&
     pc[0].direct = a.splits == 1;
     pc[0].orow0 = (pc[0].direct ? (int64_t)qr * a.H : ((int64_t)qr * a.splits + split) * a.H) + hb * 64;
     return 1;
-  }
+  } else {
   const int G = a.sk_groups, Tu = a.sk_tpu;
   const int x = blockIdx.x, xcd = x & 7, kk = x >> 3;
   const int hb = kk % nhb;
@@ -524,6 +525,7 @@ __device__ __forceinline__ int mla_pieces(const MlaArgs& a, int nhb, MlaPiece (&
   pc[1].direct = false;
   pc[1].orow0 = (slots + G + r1) * 64;
   return 2;
+  }
 }
 
 // ---- role-split form: 64 heads per work-group, eight waves in two roles
@@ -552,6 +554,7 @@ constexpr int kRolesRing = 4;
 constexpr int kScoreRK = 4;     // K-operand read buffers of a score wave (reads 3 k-steps ahead)
 constexpr int kValueRV = 3;     // V^T operand buffers of a value wave (reads 2 value tiles ahead)
 
+template <bool SK>   // row-stream form (a.sk_groups > 0), else the split form
 __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   constexpr int NT = 512;
   constexpr int CPT = kTileSlots / 256;     // LDS-direct loads per value-wave thread per tile
@@ -573,7 +576,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int nhb = (a.H + 63) / 64;
   MlaPiece pcs[2];
-  const int npc = mla_pieces(a, nhb, pcs);
+  const int npc = mla_pieces<SK>(a, nhb, pcs);
 
   for (int pi = 0; pi < npc; ++pi) {
   const MlaPiece pc = pi == 0 ? pcs[0] : pcs[1];
@@ -861,7 +864,7 @@ __device__ __forceinline__ void merge_add(float w, const u32x4& v0, const u32x4&
   }
 }
 
-template <int SMAX, bool F32>
+template <int SMAX, bool F32, bool SK>
 __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) {
   const int hblocks = (a.H + kMergeHeads - 1) / kMergeHeads;   // 1-D grid: query row x head block
   int qr, hblk;
@@ -875,7 +878,7 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
   int64_t srow0 = 0, sstep = 0;       // split form: row srow0 + s * sstep
   int sk_w0 = 0;
   int64_t sk_base = 0, sk_T = 0, sk_x0 = 0;
-  if (a.sk_groups == 0) {
+  if constexpr (!SK) {
     S = a.splits;
     srow0 = (int64_t)qr * S * a.H + head;
     sstep = a.H;
@@ -889,10 +892,13 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
     sk_base = (int64_t)(head >> 6) * (G + a.QR);
   }
   auto prow = [&](int s) -> int64_t {
-    if (a.sk_groups == 0) return srow0 + s * sstep;
-    const int G = a.sk_groups, w = sk_w0 + s;
-    const int64_t slot = ((int64_t)w * sk_T / G < sk_x0) ? (int64_t)G + qr : (int64_t)w;
-    return (sk_base + slot) * 64 + (head & 63);
+    if constexpr (!SK) {
+      return srow0 + s * sstep;
+    } else {
+      const int G = a.sk_groups, w = sk_w0 + s;
+      const int64_t slot = ((int64_t)w * sk_T / G < sk_x0) ? (int64_t)G + qr : (int64_t)w;
+      return (sk_base + slot) * 64 + (head & 63);
+    }
   };
   float mx = -INFINITY, wsum = 0.0f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -1158,8 +1164,10 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
     a.part_o = a.part_lse + part_rows;
   }
   const dim3 grid((unsigned)blocks);
-  if (nw == 4)
-    DSA_LAUNCH(mla_roles_kernel, grid, dim3(512), 0, stream, a);
+  if (nw == 4 && plan.sk_groups > 0)
+    DSA_LAUNCH(mla_roles_kernel<true>, grid, dim3(512), 0, stream, a);
+  else if (nw == 4)
+    DSA_LAUNCH(mla_roles_kernel<false>, grid, dim3(512), 0, stream, a);
   else if (nw == 2)
     DSA_LAUNCH((mla_decode_kernel<2, 2>), grid, dim3(256), 0, stream, a);
   else
@@ -1168,14 +1176,22 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   if (st != DSA_OK || !merged) return st;
   const dim3 mgrid((unsigned)(((H + kMergeHeads - 1) / kMergeHeads) * QR));
   const dim3 mblock(64 * kMergeHeads);
-  const int parts = plan.sk_groups > 0 ? plan.sk_max_parts : splits;
   // (the unrolled fp32 variant needs four times the registers, so fp32 keeps the loop)
-  if (a.o_f32)
-    DSA_LAUNCH((mla_merge_kernel<0, true>), mgrid, mblock, 0, stream, a);
-  else if (parts <= kMergeUnrolled)
-    DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false>), mgrid, mblock, 0, stream, a);
-  else
-    DSA_LAUNCH((mla_merge_kernel<0, false>), mgrid, mblock, 0, stream, a);
+  if (plan.sk_groups > 0) {
+    if (a.o_f32)
+      DSA_LAUNCH((mla_merge_kernel<0, true, true>), mgrid, mblock, 0, stream, a);
+    else if (plan.sk_max_parts <= kMergeUnrolled)
+      DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false, true>), mgrid, mblock, 0, stream, a);
+    else
+      DSA_LAUNCH((mla_merge_kernel<0, false, true>), mgrid, mblock, 0, stream, a);
+  } else {
+    if (a.o_f32)
+      DSA_LAUNCH((mla_merge_kernel<0, true, false>), mgrid, mblock, 0, stream, a);
+    else if (splits <= kMergeUnrolled)
+      DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false, false>), mgrid, mblock, 0, stream, a);
+    else
+      DSA_LAUNCH((mla_merge_kernel<0, false, false>), mgrid, mblock, 0, stream, a);
+  }
   return launch_status("dsa_sparse_mla_decode(merge)");
 }
 
