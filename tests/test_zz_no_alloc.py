@@ -1,7 +1,8 @@
 """dsa_sparse_mla_decode_noalloc, called through the C ABI, gives exactly the output of
-dsa_sparse_mla_decode with a caller workspace: two calls in a row, the second smaller (the
-scratch array keeps the first call's contents), and a call too large for the array is
-rejected before anything is enqueued."""
+dsa_sparse_mla_decode with a caller workspace: three calls in a row (the row-stream form,
+then two split-form calls, each smaller than the one before, while the scratch array keeps
+the earlier call's contents), and a call too large for the array is rejected before anything
+is enqueued."""
 import ctypes
 
 import numpy as np
@@ -31,7 +32,8 @@ def _call_noalloc(dw, idx, o, lse):
 def test_noalloc_matches_the_workspace_entry_point():
     L = _lib.load()
     assert L.dsa_sparse_mla_noalloc_max_workspace() == 64 << 20
-    cases = [(synth.spec(2).scaled(B=16, L=30000), torch.bfloat16),   # 4 splits, bf16 partials
+    cases = [(synth.spec(2).scaled(B=66, L=2600), torch.bfloat16),    # row-stream form, 388 partial slots
+             (synth.spec(2).scaled(B=16, L=30000), torch.bfloat16),   # 4 splits, bf16 partials
              (synth.spec(3).scaled(B=3, L=9000, mla_heads=64), torch.float32)]   # smaller, fp32 partials
     for cfg, odt in cases:
         wl = synth.make_workload(cfg)
