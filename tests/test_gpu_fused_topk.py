@@ -58,6 +58,30 @@ def test_fused_scan_topk_matches_separate_calls(case):
     _fused_vs_separate(dw)
 
 
+def test_fused_scan_topk_rows_the_candidates_cannot_settle():
+    """Rows whose answer the chunk candidates cannot prove, so the select goes back to the
+    scores the scan wrote: request 0 has a 700-position window of keys that outscore every
+    other key (distinct scales, so distinct scores), all inside one 1024-position chunk that
+    keeps at most 2 * 32 + 16 candidates; request 1 has an all-zero key cache, so every score
+    is +0 and the answer is its first 2048 positions.  Fused and separate calls and the
+    oracle's select must agree."""
+    wl = synth.make_workload(synth.spec(2).scaled(B=4, L=40000), with_kv=False)
+    ps = wl.page_size
+    lo, width = 2100, 700
+    for j in range(width):
+        pos = lo + j
+        pg, slot = wl.page_table[0, pos // ps], pos % ps
+        wl.idx_k[pg, slot, :] = 0x7E               # e4m3 448 in every dim
+        wl.idx_k_scale[pg, slot] = np.float32(1.0 + j / 4096.0)
+    wl.idx_k[wl.page_table[1, : -(-int(wl.seq_lens[1]) // ps)]] = 0
+    dw = DevWorkload(wl, with_kv=False)
+    got = _fused_vs_separate(dw)
+    sel0 = got[0, 0]
+    # the window's chunk holds far more of the answer than its candidate slots
+    assert np.count_nonzero((sel0 >= 2048) & (sel0 < 3072)) >= width > 2 * 32 + 16
+    assert np.array_equal(got[1, 0], np.arange(2048, dtype=np.int32))
+
+
 def test_fused_scan_topk_through_the_decode_step():
     """DecodeStep takes the fused entry points for one query token; its indices equal the
     unfused step's, eager and replayed from a graph."""
