@@ -297,7 +297,10 @@ dsa_status_t dsa_gather_kv(const int32_t* topk, const uint8_t* is_hit, const int
  * partial (o, lse) are merged by LSE rescaling ([TSA] two-stage split-KV decode).
  *
  *   q      [B, Sq, H, 576] bf16
- *   idx    [B, Sq, k] int32 positions into `rows` (-1 = skip)
+ *   idx    [B, Sq, k] int32 positions into `rows` (-1 = skip).  A position >= 0 that resolves
+ *          to no row (past the request's page-table row or dense stride, on a page whose id
+ *          is negative, or at a row >= num_rows) is skipped like -1 and adds one to
+ *          err_count.
  *   rows   row store of latent rows, row_bytes = 1152
  *   o      [B, Sq, H, 512], o_dtype BF16 (round-to-nearest-even) or F32
  *   lse    [B, Sq, H] float32

@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(64 * NW * NS, 1) mla_decode_kernel(MlaArgs a) 
     if (e_begin + e < e_end) {
       const int32_t p = idx[e_begin + e];
       const int64_t row = a.rows.row(b, p);
-      if (row < 0 && p >= 0) count_error(a.err);
+      if (row < 0 && p >= 0 && hb == 0) count_error(a.err);   // once per entry, not per head block
       if (row >= 0) off = row * kRowBytes;
     }
     rowoff[e] = off;
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
     if (e_begin + e < e_end) {
       const int32_t p = idx[e_begin + e];
       const int64_t row = a.rows.row(b, p);
-      if (row < 0 && p >= 0) count_error(a.err);
+      if (row < 0 && p >= 0 && hb == 0) count_error(a.err);   // once per entry, not per head block
       if (row >= 0) r = (int32_t)row;       // num_rows < 2^31 (checked on the host)
     }
     rowix[e] = r;
@@ -1148,6 +1148,7 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   a.o = o;
   a.o_f32 = (o_dtype == DSA_F32);
   a.lse = lse;
+  a.err = err_count;
   a.counts = un.counts;
   a.member = un.member;
   a.fold_h = un.fold_h;

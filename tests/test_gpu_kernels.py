@@ -417,6 +417,53 @@ def test_mla_row_stream_form_against_oracle(cfg, B, H, k, L, o_dtype):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("ps", [16, 128])
+def test_mla_page_sizes_dense_rows_and_unresolvable_entries(ps):
+    """Pages of 16 and 128 tokens; the same rows laid out densely (no page table, one block of
+    L rows per request), which must give bit-identical o and lse; and selections holding
+    entries that resolve to no row (positions on a page whose table entry is -1, a position
+    past the request's page-table row): each is counted once in err_count and left out of
+    the softmax, so o and lse match the oracle over the remaining entries."""
+    B, H, k, L = 4, 128, 1024, 3000
+    wl = synth.make_workload(synth.spec(2).scaled(B=B, L=L, mla_heads=H, topk=k, page_size=ps))
+    rng = np.random.default_rng(ps)
+    idx = np.full((B, 1, k), -1, dtype=np.int32)
+    for b in range(B):
+        n = k - 9 * b
+        idx[b, 0, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    dw = DevWorkload(wl)
+    o, lse = dw.mla(t_i32(idx))
+    o_ref = np.empty((B, 1, H, 512))
+    l_ref = np.empty((B, 1, H))
+    for b in range(B):
+        o_ref[b, 0], l_ref[b, 0] = o_mla.sparse_mla(wl.mla_q[b, 0], selected_rows(wl, b, idx[b, 0]), wl.scale)
+    check_attention(o, lse, o_ref, l_ref)
+    assert int(dw.err) == 0
+
+    dense = np.stack([selected_rows(wl, b, np.arange(L)) for b in range(B)]).reshape(B * L, 576)
+    dense_t = t_u16_as_bf16(dense)
+    o2, lse2 = dw.mla(t_i32(idx), rows=dsa.Rows(dense_t, 1152, None, 0, req_stride=L))
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(lse2, lse)
+    assert int(dw.err) == 0
+
+    pt = wl.page_table.copy()
+    dead_page = int(idx[0, 0, 40]) // ps                  # request 0: one page marked absent
+    pt[0, dead_page] = -1
+    bad = idx.copy()
+    past = pt.shape[1] * ps + 5                           # request 2: past its page-table row
+    bad[2, 0, k - 9 * 2] = past                           # in place of its first padding entry
+    pt_t = t_i32(pt)
+    o3, lse3 = dw.mla(t_i32(bad), rows=dsa.Rows(dw.kv, 1152, pt_t, ps))
+    torch.cuda.synchronize()
+    on_dead = (idx[0, 0] >= 0) & (idx[0, 0] // ps == dead_page)
+    assert int(dw.err) == int(on_dead.sum()) + 1
+    keep = [np.where(on_dead, -1, idx[0, 0])] + [idx[b, 0] for b in range(1, B)]
+    for b in range(B):
+        o_ref[b, 0], l_ref[b, 0] = o_mla.sparse_mla(wl.mla_q[b, 0], selected_rows(wl, b, keep[b]), wl.scale)
+    check_attention(o3, lse3, o_ref, l_ref)
+
+
 def test_mla_f32_output_and_empty_selection():
     wl = synth.make_workload(synth.spec(2).scaled(B=2, L=500, topk=64))
     idx = np.full((2, 1, 64), -1, dtype=np.int32)
