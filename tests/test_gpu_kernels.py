@@ -540,6 +540,98 @@ def test_plan_pool_group_trajectory_bit_exact():
     _run_plan_steps([traj[s][:, None, :] for s in range(cfg.steps)], cfg.n_sets, cfg.ways, cfg.id_range)
 
 
+def test_plan_invalid_ids_and_stored_slots_are_skipped_and_counted():
+    """Positions >= id_range and ids whose stored slot lies outside the pool are invalid
+    entries: is_hit 0, slot -1, not misses, the metadata untouched for them, one count each
+    in err_count.  Everything else equals the oracle's plan of the rows without them."""
+    rng = np.random.default_rng(41)
+    B, k, n_sets, W, id_range = 2, 40, 8, 4, 300
+    first = np.stack([np.sort(rng.choice(id_range, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    pool = torch.full((B, n_sets * W), -1, dtype=torch.int32, device=DEV)
+    its = torch.full((B, id_range), -1, dtype=torch.int32, device=DEV)
+    ptr = torch.zeros((B, n_sets), dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    outs = [torch.empty((B, 1, k), dtype=torch.uint8, device=DEV), torch.empty((B, 1, k), dtype=torch.int32, device=DEV),
+            torch.empty((B, k), dtype=torch.int32, device=DEV), torch.empty((B, k), dtype=torch.int32, device=DEV),
+            torch.empty(B, dtype=torch.int32, device=DEV)]
+    dsa.dsa_plan(t_i32(first[:, None, :]), pool, its, ptr, n_sets, W, *outs, commit=True, err=err)
+    torch.cuda.synchronize()
+    assert int(err) == 0
+    state = [o_plan.plan_step(first[b][None], *o_plan.empty_state(n_sets, W, id_range), n_sets, W)[1]
+             for b in range(B)]
+    # second step: k - 3 valid ids, then three ids past id_range; one valid id of each row
+    # (not pooled) gets a stored slot far outside the pool
+    second = np.empty((B, k), dtype=np.int32)
+    clean = np.empty((B, k), dtype=np.int32)
+    its_np = its.cpu().numpy()
+    bad_ids = []
+    for b in range(B):
+        ids = np.sort(rng.choice(id_range, k - 3, replace=False))
+        second[b] = np.concatenate([ids, [id_range, id_range + 7, 5000]])
+        u = int(next(x for x in ids if its_np[b, x] == -1))
+        bad_ids.append(u)
+        its_np[b, u] = 1 << 20
+        clean[b] = np.where((second[b] >= id_range) | (second[b] == u), -1, second[b])
+    its.copy_(torch.from_numpy(its_np))
+    dsa.dsa_plan(t_i32(second[:, None, :]), pool, its, ptr, n_sets, W, *outs, commit=True, err=err)
+    torch.cuda.synchronize()
+    assert int(err) == B * 4
+    is_hit, slot, mpos, mslot, mcnt = (x.cpu().numpy() for x in outs)
+    for b in range(B):
+        its_b = state[b][1].copy()
+        its_b[bad_ids[b]] = 1 << 20
+        out, (p_new, i_new, r_new) = o_plan.plan_step(clean[b][None], state[b][0], its_b, state[b][2], n_sets, W)
+        m = out["miss_count"]
+        assert int(mcnt[b]) == m
+        assert np.array_equal(is_hit[b], out["is_hit"]) and np.array_equal(slot[b], out["slot"])
+        assert np.array_equal(mpos[b, :m], out["miss_pos"]) and np.array_equal(mslot[b, :m], out["miss_slot"])
+        assert np.array_equal(pool[b].cpu().numpy(), p_new)
+        assert np.array_equal(its[b].cpu().numpy(), i_new)
+        assert np.array_equal(ptr[b].cpu().numpy(), r_new)
+
+
+def test_gather_unresolvable_positions_and_slots_are_counted():
+    """SERVE: a position with no source row gets the zero row, -1 in sel_idx and one count;
+    INSTALL: a surviving miss whose slot lies past the pool is skipped and counted, and no
+    pool row changes for it."""
+    rng = np.random.default_rng(43)
+    B, L, k, pool_rows = 2, 500, 16, 8
+    full = rng.integers(0, 1 << 16, (B * L, 576), dtype=np.uint16)
+    src = dsa.Rows(t_u16_as_bf16(full), 1152, req_stride=L)
+    tk = np.stack([np.sort(rng.choice(L, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    tk[0, -2:] = [L + 3, L + 90]                          # past request 0's stride
+    tk[1, -1] = -1                                        # padding: zero row, not counted
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sel = torch.full((B, 1, k, 576), 3.0, dtype=torch.bfloat16, device=DEV)
+    sel_idx = torch.full((B, 1, k), -9, dtype=torch.int32, device=DEV)
+    dsa.dsa_gather_kv(t_i32(tk[:, None, :]), None, None, src, None, sel, dsa.DSA_GATHER_SERVE, err=err,
+                      sel_idx=sel_idx)
+    torch.cuda.synchronize()
+    assert int(err) == 2
+    got = sel.view(torch.int16).cpu().numpy().view(np.uint16)
+    si = sel_idx.cpu().numpy()
+    for b in range(B):
+        for j in range(k):
+            p = int(tk[b, j])
+            if 0 <= p < L:
+                assert np.array_equal(got[b, 0, j], full[b * L + p]) and si[b, 0, j] == j
+            else:
+                assert not got[b, 0, j].any() and si[b, 0, j] == -1
+    pool = torch.zeros((B, pool_rows, 576), dtype=torch.bfloat16, device=DEV)
+    is_hit = torch.zeros((B, 1, k), dtype=torch.uint8, device=DEV)
+    slot_np = np.full((B, 1, k), -1, dtype=np.int32)
+    slot_np[0, 0, :3] = [0, pool_rows, 5]                 # the second is past the pool
+    slot_np[1, 0, 0] = 2
+    dsa.dsa_gather_kv(t_i32(tk[:, None, :]), is_hit, t_i32(slot_np), None, pool, sel, dsa.DSA_GATHER_INSTALL,
+                      err=err)
+    torch.cuda.synchronize()
+    assert int(err) == 3
+    pool_np = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = np.zeros((B, pool_rows, 576), dtype=np.uint16)
+    want[0, 0], want[0, 5], want[1, 2] = full[tk[0, 0]], full[tk[0, 2]], full[L + tk[1, 0]]
+    assert np.array_equal(pool_np, want)
+
+
 # ------------------------------------------------------------------ gather
 def test_gather_serve_and_install_bit_exact():
     rng = np.random.default_rng(9)
