@@ -417,14 +417,15 @@ def test_mla_row_stream_form_against_oracle(cfg, B, H, k, L, o_dtype):
     assert int(dw.err) == 0
 
 
-@pytest.mark.parametrize("ps", [16, 128])
-def test_mla_page_sizes_dense_rows_and_unresolvable_entries(ps):
-    """Pages of 16 and 128 tokens; the same rows laid out densely (no page table, one block of
-    L rows per request), which must give bit-identical o and lse; and selections holding
-    entries that resolve to no row (positions on a page whose table entry is -1, a position
-    past the request's page-table row): each is counted once in err_count and left out of
-    the softmax, so o and lse match the oracle over the remaining entries."""
-    B, H, k, L = 4, 128, 1024, 3000
+@pytest.mark.parametrize("ps,H", [(16, 128), (128, 128), (64, 32)])
+def test_mla_page_sizes_dense_rows_and_unresolvable_entries(ps, H):
+    """Pages of 16, 128 and 64 tokens (the last with 32 heads, the two-stream work-group);
+    the same rows laid out densely (no page table, one block of L rows per request), which
+    must give bit-identical o and lse; and selections holding entries that resolve to no row
+    (positions on a page whose table entry is -1, a position past the request's page-table
+    row): each is counted once in err_count and left out of the softmax, so o and lse match
+    the oracle over the remaining entries."""
+    B, k, L = 4, 1024, 3000
     wl = synth.make_workload(synth.spec(2).scaled(B=B, L=L, mla_heads=H, topk=k, page_size=ps))
     rng = np.random.default_rng(ps)
     idx = np.full((B, 1, k), -1, dtype=np.int32)
