@@ -118,6 +118,41 @@ def test_indexer_max_batch_ragged_within_bound(cid, B, Sq):
     assert int(dw.err) == 0
 
 
+@pytest.mark.parametrize("path", ["mfma", "fused", "f32"])
+def test_indexer_leaves_positions_past_the_length_untouched_and_reads_a_null_scale_as_one(path):
+    """Requests of different lengths in one score array: every entry at or past a request's
+    length keeps its sentinel bits (the scan writes only [0, seq_len)), and with k_scale
+    NULL the e4m3 keys are scored with sigma = 1 (the oracle with unit scales)."""
+    import dataclasses
+    if path == "f32":
+        wl = synth.make_workload(synth.spec(1).scaled(B=3, L=3000), with_kv=False)
+    else:
+        wl = synth.make_workload(synth.spec(2).scaled(B=4, L=5000), with_kv=False)
+    lens = np.array([5000, 3100, 4097, 2049][:wl.B], dtype=np.int32) if path != "f32" else \
+        np.array([3000, 1777, 65], dtype=np.int32)
+    wl = dataclasses.replace(wl, seq_lens=lens)
+    if path != "f32":
+        wl = dataclasses.replace(wl, idx_k_scale=np.ones_like(wl.idx_k_scale))
+    dw = DevWorkload(wl, with_kv=False)
+    stride = int(lens.max()) + 37
+    sentinel = 0x7FC0DEAD
+    sc = torch.full((wl.B, wl.Sq, stride), sentinel, dtype=torch.int32, device=DEV).view(torch.float32)
+    k_scale = None if path != "f32" else dw.k_scale
+    if path == "fused":
+        ws = torch.empty((dsa.dsa_topk_workspace_size(wl.B, 1, wl.topk, stride),), dtype=torch.uint8, device=DEV)
+        dsa.dsa_indexer_topk_chunks(dw.idx_q, dw.idx_w, dw.keys, k_scale, dw.seq_lens, sc, wl.topk, ws,
+                                    k_dtype=dw.k_dtype, err=dw.err, q_dtype=dw.q_dtype)
+    else:
+        dsa.dsa_indexer_scores(dw.idx_q, dw.idx_w, dw.keys, k_scale, dw.seq_lens, sc, k_dtype=dw.k_dtype,
+                               err=dw.err, q_dtype=dw.q_dtype)
+    torch.cuda.synchronize()
+    assert int(dw.err) == 0
+    bits = sc.view(torch.int32).cpu().numpy()
+    for b in range(wl.B):
+        assert (bits[b, :, int(lens[b]):] == sentinel).all(), b
+    check_scores(wl, sc, exact=(path == "f32"))
+
+
 def test_indexer_length_past_the_score_row_is_clamped():
     """seq_lens[0] = 900 over a 700-wide score row: request 0 scores as a 700-token request,
     counts one error, and nothing is written past the rows (a sentinel row follows them)."""
