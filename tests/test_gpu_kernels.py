@@ -272,6 +272,26 @@ def test_topk_standalone_bit_exact(case):
     assert np.array_equal(idx.cpu().numpy()[0, 0], o_topk.select(s, k))
 
 
+def test_topk_minus_inf_scores_and_lengths_past_the_stride():
+    """-inf is an ordinary (lowest) score: a row mostly of -inf takes its finite positions and
+    then the lowest -inf positions; a row of -inf only takes its first k positions.  A length
+    above the score stride is read as the stride.  Both the wave-chunk rows (stride 9000)
+    and the work-group-chunk rows (stride 300000) are checked against the oracle's select."""
+    rng = np.random.default_rng(17)
+    for stride, k in ((9000, 2048), (300000, 2048)):
+        B = 4
+        s = rng.standard_normal((B, 1, stride)).astype(np.float32)
+        s[0, 0, rng.random(stride) < 0.85] = -np.inf
+        s[1, 0, :] = -np.inf
+        lens = np.array([stride, stride - 11, stride + 100, stride // 3], dtype=np.int32)
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+        dsa.dsa_topk(torch.from_numpy(s).to(DEV), t_i32(lens), idx)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            n = min(int(lens[b]), stride)
+            assert np.array_equal(got[b, 0], o_topk.select(s[b, 0, :n], k)), (stride, b)
+
+
 def _long_chunk_rows(stride):
     """Rows of a batch whose 8192-position chunks would take more than 512 work-groups, so
     the chunk stage runs with 16384 positions per chunk."""
