@@ -839,6 +839,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
 // are float32, else bf16.
 constexpr int kMergeHeads = 4;   // heads per 256-thread work-group
 constexpr int kMergeUnrolled = 8;
+constexpr int kMergeUnrolledF32 = 4;
 
 template <bool F32>
 __device__ __forceinline__ void merge_load(const void* part_o, int64_t pb, u32x4& v0, u32x4& v1) {
@@ -1177,16 +1178,20 @@ static dsa_status_t dsa::mla_decode_impl(const void* q, const int32_t* idx, cons
   if (st != DSA_OK || !merged) return st;
   const dim3 mgrid((unsigned)(((H + kMergeHeads - 1) / kMergeHeads) * QR));
   const dim3 mblock(64 * kMergeHeads);
-  // (the unrolled fp32 variant needs four times the registers, so fp32 keeps the loop)
+  // float32 partials take twice the registers per part: up to kMergeUnrolledF32 parts unrolled
   if (plan.sk_groups > 0) {
-    if (a.o_f32)
+    if (a.o_f32 && plan.sk_max_parts <= kMergeUnrolledF32)
+      DSA_LAUNCH((mla_merge_kernel<kMergeUnrolledF32, true, true>), mgrid, mblock, 0, stream, a);
+    else if (a.o_f32)
       DSA_LAUNCH((mla_merge_kernel<0, true, true>), mgrid, mblock, 0, stream, a);
     else if (plan.sk_max_parts <= kMergeUnrolled)
       DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false, true>), mgrid, mblock, 0, stream, a);
     else
       DSA_LAUNCH((mla_merge_kernel<0, false, true>), mgrid, mblock, 0, stream, a);
   } else {
-    if (a.o_f32)
+    if (a.o_f32 && splits <= kMergeUnrolledF32)
+      DSA_LAUNCH((mla_merge_kernel<kMergeUnrolledF32, true, false>), mgrid, mblock, 0, stream, a);
+    else if (a.o_f32)
       DSA_LAUNCH((mla_merge_kernel<0, true, false>), mgrid, mblock, 0, stream, a);
     else if (splits <= kMergeUnrolled)
       DSA_LAUNCH((mla_merge_kernel<kMergeUnrolled, false, false>), mgrid, mblock, 0, stream, a);
