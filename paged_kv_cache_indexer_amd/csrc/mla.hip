@@ -835,7 +835,7 @@ __global__ void __launch_bounds__(512, 1) mla_roles_kernel(MlaArgs a) {
 
 // merge of split partials: 64 threads per (query row, head), 8 value dims per thread.  With
 // SMAX > 0 (splits <= SMAX) every lse and partial load is issued before any is used, so a
-// thread waits for memory once; SMAX == 0 handles any split count.  F32: o and the partials
+// thread waits for memory once; SMAX == 0 handles any split count in batches of that kind.  F32: o and the partials
 // are float32, else bf16.
 constexpr int kMergeHeads = 4;   // heads per 256-thread work-group
 constexpr int kMergeUnrolled = 8;
@@ -928,16 +928,37 @@ __global__ void __launch_bounds__(64 * kMergeHeads) mla_merge_kernel(MlaArgs a) 
       }
     }
   } else {
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[prow(s)]);
+    // any part count, in batches whose loads are all issued before any is used (a plain loop
+    // waited out one memory latency per part)
+    constexpr int NB = F32 ? kMergeUnrolledF32 : kMergeUnrolled;
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      float lv[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) lv[j] = (s0 + j < S) ? a.part_lse[prow(s0 + j)] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) mx = fmaxf(mx, lv[j]);
+    }
     if (mx > -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const int64_t r = prow(s);
-        const float l = a.part_lse[r];
-        const float w = (l == -INFINITY) ? 0.0f : __expf(l - mx);
-        wsum += w;
-        u32x4 v0 = u32x4{}, v1 = u32x4{};
-        merge_load<F32>(a.part_o, r * kVDim + d, v0, v1);
-        merge_add<F32>(w, v0, v1, acc);
+      for (int s0 = 0; s0 < S; s0 += NB) {
+        float lv[NB];
+        u32x4 v0[NB], v1[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          lv[j] = -INFINITY;
+          v0[j] = u32x4{};
+          v1[j] = u32x4{};
+          if (s0 + j < S) {
+            const int64_t r = prow(s0 + j);
+            lv[j] = a.part_lse[r];
+            merge_load<F32>(a.part_o, r * kVDim + d, v0[j], v1[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float w = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - mx);
+          wsum += w;
+          merge_add<F32>(w, v0[j], v1[j], acc);
+        }
       }
     }
   }

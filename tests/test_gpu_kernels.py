@@ -446,11 +446,15 @@ def test_mla_single_split_writes_o_directly(B, k, L):
                                                   (2, 100, 128, 1000, 1500, torch.bfloat16),
                                                   (3, 13, 128, 2048, 2200, torch.bfloat16),
                                                   (2, 70, 80, 1500, 1700, torch.bfloat16),
-                                                  (2, 66, 64, 2048, 2100, torch.bfloat16)])
+                                                  (2, 66, 64, 2048, 2100, torch.bfloat16),
+                                                  (2, 17, 128, 8192, 9000, torch.bfloat16),
+                                                  (2, 17, 256, 2048, 2600, torch.float32)])
 def test_mla_row_stream_form_against_oracle(cfg, B, H, k, L, o_dtype):
     """Batches whose split plan would leave a second, partly empty round take the row-stream
     form: each head block's tiles shared evenly by a fixed set of work-groups, a share meeting
-    up to two rows.  Every (row, head) against the oracle, padded selections included."""
+    up to two rows.  Every (row, head) against the oracle, padded selections included.  The
+    17-row shapes give up to 9 (bf16) and 5 (float32) parts per row, more than the merge
+    unrolls: its batched form."""
     from tests.test_mla_addressing import mla_plan
     wl = synth.make_workload(synth.spec(cfg).scaled(B=B, L=L, mla_heads=H, topk=k))
     Sq = wl.Sq
